@@ -1,0 +1,180 @@
+"""Seeded synthetic inputs for the Gated DeltaNet layer.
+
+This module is shared by the HIP path's tests/benchmark and by the fp64
+oracle's tests; it therefore holds none of the layer's arithmetic -- only
+random draws, bf16 rounding of the drawn values and the workload shapes.
+
+Workloads (the layer shape is the 35B-A3B one described on the llmxabe
+README, model section: 16 key heads, 32 value heads, 128-wide heads, a
+fixed-size state of 32x128x128 fp32 per sequence and layer):
+
+* ``tiny``     1 sequence of 64 tokens, 2 key / 4 value heads, dk = dv = 32,
+               chunk 16, fp32 everywhere, zero initial state;
+* ``prefill``  1 sequence of 4096 tokens, 16 / 32 heads, dk = dv = 128,
+               chunk 64, bf16 activations, zero initial state;
+* ``decode``   B sequences x one bf16 token, 30 stacked layers, carried fp32
+               state and conv state;
+* ``long``     1 sequence of 131072 tokens resuming from a random state;
+* ``varlen``   8 packed sequences, lengths log-uniform in [512, 32768],
+               per-sequence random initial states.
+
+Distributions: q, k, v, z ~ N(0, 1); gate logits a, b ~ N(0, 1); conv
+weights ~ N(0, 1/4); A_log ~ U(log 1, log 16); dt_bias ~ N(0, 0.1);
+initial states ~ N(0, 0.02).  The second argument of N(., .) is read as the
+variance.  Values are drawn in fp32 and rounded to nearest-even bf16 where
+the workload is bf16, so the GPU and the oracle see identical bits.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returned as fp32
+    arrays whose values are exactly representable in bf16."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+
+
+@dataclass
+class LayerShape:
+    Hk: int = 16
+    Hv: int = 32
+    dk: int = 128
+    dv: int = 128
+    K: int = 4
+    chunk: int = 64
+    act_dtype: str = "bf16"      # "bf16" or "fp32" for q/k/v/z/a/b, conv state
+    eps_l2: float = 1e-6
+    eps_rms: float = 1e-6
+
+    @property
+    def Cc(self) -> int:
+        return 2 * self.Hk * self.dk + self.Hv * self.dv
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dk)
+
+
+TINY = LayerShape(Hk=2, Hv=4, dk=32, dv=32, K=4, chunk=16, act_dtype="fp32")
+FULL = LayerShape()
+
+
+def _act(x: np.ndarray, shape: LayerShape) -> np.ndarray:
+    x = x.astype(np.float32, copy=False)
+    return bf16_round(x) if shape.act_dtype == "bf16" else x
+
+
+def _normal(rng, size, std=1.0):
+    return (rng.standard_normal(size, dtype=np.float32) * np.float32(std))
+
+
+def layer_params(shape: LayerShape, seed: int, norm_w_jitter: bool = False,
+                 A_log_range=(0.0, math.log(16.0))):
+    """conv_w [Cc, K], A_log [Hv], dt_bias [Hv], norm_w [dv]; all fp32."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    conv_w = _normal(rng, (shape.Cc, shape.K), 0.5)
+    A_log = rng.uniform(A_log_range[0], A_log_range[1], shape.Hv).astype(np.float32)
+    dt_bias = _normal(rng, (shape.Hv,), math.sqrt(0.1))
+    if norm_w_jitter:
+        norm_w = (1.0 + 0.1 * rng.standard_normal(shape.dv)).astype(np.float32)
+    else:
+        norm_w = np.ones(shape.dv, dtype=np.float32)
+    return {"conv_w": conv_w, "A_log": A_log, "dt_bias": dt_bias,
+            "norm_w": norm_w}
+
+
+def token_inputs(shape: LayerShape, T: int, seed: int):
+    """q, k [T, Hk, dk]; v, z [T, Hv, dv]; a, b [T, Hv] in the activation
+    dtype's values (held as fp32 arrays)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2])))
+    out = {}
+    out["q"] = _act(_normal(rng, (T, shape.Hk, shape.dk)), shape)
+    out["k"] = _act(_normal(rng, (T, shape.Hk, shape.dk)), shape)
+    out["v"] = _act(_normal(rng, (T, shape.Hv, shape.dv)), shape)
+    out["z"] = _act(_normal(rng, (T, shape.Hv, shape.dv)), shape)
+    out["a"] = _act(_normal(rng, (T, shape.Hv)), shape)
+    out["b"] = _act(_normal(rng, (T, shape.Hv)), shape)
+    return out
+
+
+def initial_states(shape: LayerShape, N: int, seed: int, var: float = 0.02):
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    return _normal(rng, (N, shape.Hv, shape.dk, shape.dv), math.sqrt(var))
+
+
+def conv_states(shape: LayerShape, N: int, seed: int):
+    """Random carried conv states [N, K-1, Cc] (raw inputs ~ N(0,1))."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 4])))
+    return _act(_normal(rng, (N, shape.K - 1, shape.Cc)), shape)
+
+
+def varlen_lengths(N: int, seed: int, lo: int = 512, hi: int = 32768):
+    """Lengths floor(exp(U(ln lo, ln hi))), one per sequence."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5])))
+    return np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), N))).astype(np.int64)
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@dataclass
+class PrefillCase:
+    shape: LayerShape
+    cu_seqlens: np.ndarray
+    inputs: dict
+    params: dict
+    initial_state: np.ndarray | None = None
+    conv_state: np.ndarray | None = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def N(self) -> int:
+        return int(self.cu_seqlens.size - 1)
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def prefill_case(shape: LayerShape, lengths, seed: int, with_state=False,
+                 with_conv_state=False, norm_w_jitter=False,
+                 A_log_range=(0.0, math.log(16.0))) -> PrefillCase:
+    cu = cu_from_lengths(lengths)
+    T = int(cu[-1])
+    N = len(lengths)
+    return PrefillCase(
+        shape=shape, cu_seqlens=cu,
+        inputs=token_inputs(shape, T, seed),
+        params=layer_params(shape, seed, norm_w_jitter, A_log_range),
+        initial_state=initial_states(shape, N, seed) if with_state else None,
+        conv_state=conv_states(shape, N, seed) if with_conv_state else None,
+        meta={"seed": seed})
+
+
+def tiny_case(seed: int = 0) -> PrefillCase:
+    """1 x 64 tokens, fp32, zero initial state."""
+    return prefill_case(TINY, [64], seed)
+
+
+def prefill_4k_case(seed: int = 1) -> PrefillCase:
+    """1 x 4096 tokens at the 35B-A3B layer shape, zero initial state."""
+    return prefill_case(FULL, [4096], seed)
+
+
+def long_case(seed: int = 3, T: int = 131072) -> PrefillCase:
+    """1 x 131072 tokens resuming from a N(0, 0.02) state, zero conv state."""
+    return prefill_case(FULL, [T], seed, with_state=True)
+
+
+def varlen_case(seed: int = 4, N: int = 8) -> PrefillCase:
+    """8 packed sequences, log-uniform lengths, random initial states."""
+    return prefill_case(FULL, varlen_lengths(N, seed), seed, with_state=True)
