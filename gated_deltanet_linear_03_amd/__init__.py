@@ -1,0 +1,264 @@
+"""MI355X (gfx950) Gated DeltaNet layer: thin Python binding of ``libgdn.so``.
+
+Every step of the layer runs in the HIP kernels behind the C ABI declared in
+``include/gdn.h``; this module only marshals torch tensors (device memory)
+and the current HIP stream into that ABI.  There is no fallback: if the
+library is missing the import of the binding raises.
+
+    import torch, gated_deltanet_linear_03_amd as gdn
+    layer = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                      conv_w=..., A_log=..., dt_bias=..., norm_w=...)
+    res = gdn.prefill(layer, q, k, v, z, a, b, cu_seqlens,
+                      initial_state=None, conv_state_in=None)
+    dec = gdn.decode(layer, q1, k1, v1, z1, a1, b1, state, conv_state)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARGUMENT = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_WORKSPACE = 3
+GDN_ERR_HIP = 4
+GDN_DTYPE_FP32 = 0
+GDN_DTYPE_BF16 = 1
+
+EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
+           "gdn_decode", "gdn_status_string", "gdn_last_error",
+           "gdn_selftest_mfma")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"gdn status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class CLayer(ctypes.Structure):
+    _fields_ = [("Hk", ctypes.c_int32), ("Hv", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("conv_K", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("eps_l2", ctypes.c_float),
+                ("eps_rms", ctypes.c_float),
+                ("conv_w", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+
+
+_TOKEN_FIELDS = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                 ("v", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                 ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                 ("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+                 ("v_stride", ctypes.c_int64), ("z_stride", ctypes.c_int64),
+                 ("a_stride", ctypes.c_int64), ("b_stride", ctypes.c_int64)]
+
+
+class CPrefillIO(ctypes.Structure):
+    _fields_ = ([("N", ctypes.c_int32), ("T_total", ctypes.c_int64),
+                 ("cu_seqlens", ctypes.c_void_p)] + _TOKEN_FIELDS +
+                [("initial_state", ctypes.c_void_p),
+                 ("final_state", ctypes.c_void_p),
+                 ("conv_state_in", ctypes.c_void_p),
+                 ("conv_state_out", ctypes.c_void_p),
+                 ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p)])
+
+
+class CDecodeIO(ctypes.Structure):
+    _fields_ = ([("B", ctypes.c_int32)] + _TOKEN_FIELDS +
+                [("state_in", ctypes.c_void_p), ("state_out", ctypes.c_void_p),
+                 ("conv_state_in", ctypes.c_void_p),
+                 ("conv_state_out", ctypes.c_void_p),
+                 ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p)])
+
+
+_lib = None
+
+
+def lib():
+    """Load ``libgdn.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_deltanet_linear_03_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_abi_version.argtypes = []
+        L.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(CLayer),
+                                                  ctypes.c_int32, ctypes.c_int64]
+        L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_decode.restype = ctypes.c_int
+        L.gdn_decode.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CDecodeIO),
+                                 ctypes.c_void_p]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_selftest_mfma.restype = ctypes.c_int
+        L.gdn_selftest_mfma.argtypes = [ctypes.c_void_p] * 4
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Layer:
+    """Shape and parameters of one layer.  Parameters are fp32 device
+    tensors: conv_w [Cc, 4], A_log [Hv], dt_bias [Hv], norm_w [dv]."""
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    chunk: int
+    conv_w: object
+    A_log: object
+    dt_bias: object
+    norm_w: object
+    act_dtype: int = GDN_DTYPE_BF16
+    out_dtype: int = GDN_DTYPE_FP32
+    scale: float | None = None
+    eps_l2: float = 1e-6
+    eps_rms: float = 1e-6
+    conv_K: int = 4
+
+    @property
+    def Cc(self) -> int:
+        return 2 * self.Hk * self.dk + self.Hv * self.dv
+
+    def c(self) -> CLayer:
+        scale = self.scale if self.scale is not None else self.dk ** -0.5
+        return CLayer(self.Hk, self.Hv, self.dk, self.dv, self.conv_K, self.chunk,
+                      self.act_dtype, self.out_dtype, scale, self.eps_l2,
+                      self.eps_rms, _ptr(self.conv_w), _ptr(self.A_log),
+                      _ptr(self.dt_bias), _ptr(self.norm_w))
+
+
+def _tok_stride(t):
+    return 0 if t is None else int(t.stride(0))
+
+
+def prefill_workspace_bytes(layer: Layer, N: int, T_total: int) -> int:
+    cl = layer.c()
+    n = lib().gdn_prefill_workspace_bytes(ctypes.byref(cl), int(N), int(T_total))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return int(n)
+
+
+def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
+                out, core_out=None, initial_state=None, final_state=None,
+                conv_state_in=None, conv_state_out=None, workspace=None,
+                workspace_bytes=None, stream=None):
+    """Call ``gdn_prefill`` on caller-provided buffers (no allocation)."""
+    cl = layer.c()
+    io = CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
+                    _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
+                    _tok_stride(q), _tok_stride(k), _tok_stride(v),
+                    _tok_stride(z), _tok_stride(a), _tok_stride(b),
+                    _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
+                    _ptr(conv_state_out), _ptr(out), _ptr(core_out))
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill(ctypes.byref(cl), ctypes.byref(io), _ptr(workspace),
+                             int(workspace_bytes), _stream(stream)))
+
+
+def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,
+            conv_state_in=None, want_core=False, in_place=False, workspace=None,
+            stream=None):
+    """Allocate outputs with torch and run ``gdn_prefill``.
+
+    q, k [T, Hk, dk]; v, z [T, Hv, dv]; a, b [T, Hv] (act dtype, may be
+    token-strided views); cu_seqlens int32 [N+1] on the device.  Returns a
+    dict with out, final_state, conv_state_out and (if asked) core_out.
+    With in_place=True the states are updated in the given tensors."""
+    import torch
+    dev = q.device
+    T = int(q.shape[0])
+    N = int(cu_seqlens.numel() - 1)
+    odt = torch.bfloat16 if layer.out_dtype == GDN_DTYPE_BF16 else torch.float32
+    adt = torch.bfloat16 if layer.act_dtype == GDN_DTYPE_BF16 else torch.float32
+    out = torch.empty((T, layer.Hv, layer.dv), dtype=odt, device=dev)
+    core = torch.empty((T, layer.Hv, layer.dv), dtype=torch.float32, device=dev) if want_core else None
+    if in_place and initial_state is not None:
+        fs = initial_state
+    else:
+        fs = torch.empty((N, layer.Hv, layer.dk, layer.dv), dtype=torch.float32, device=dev)
+    if in_place and conv_state_in is not None:
+        cs = conv_state_in
+    else:
+        cs = torch.empty((N, layer.conv_K - 1, layer.Cc), dtype=adt, device=dev)
+    if workspace is None:
+        nb = prefill_workspace_bytes(layer, N, T)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
+    prefill_raw(layer, N=N, T_total=T, cu_seqlens=cu_seqlens, q=q, k=k, v=v, z=z,
+                a=a, b=b, out=out, core_out=core, initial_state=initial_state,
+                final_state=fs, conv_state_in=conv_state_in, conv_state_out=cs,
+                workspace=workspace, stream=stream)
+    res = {"out": out, "final_state": fs, "conv_state_out": cs}
+    if want_core:
+        res["core_out"] = core
+    return res
+
+
+def decode_raw(layer: Layer, *, B, q, k, v, z, a, b, out, state_in, state_out,
+               conv_state_in, conv_state_out, core_out=None, stream=None):
+    """Call ``gdn_decode`` on caller-provided buffers (no allocation)."""
+    cl = layer.c()
+    io = CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
+                   _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
+                   _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
+                   _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
+                   _ptr(core_out))
+    _check(lib().gdn_decode(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
+
+
+def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
+           want_core=False, stream=None):
+    """One token per sequence: q, k [B, Hk, dk]; v, z [B, Hv, dv]; a, b
+    [B, Hv]; state [B, Hv, dk, dv] fp32; conv_state [B, 3, Cc].  Updates
+    the states in place by default.  Returns a dict like ``prefill``."""
+    import torch
+    B = int(q.shape[0])
+    odt = torch.bfloat16 if layer.out_dtype == GDN_DTYPE_BF16 else torch.float32
+    out = torch.empty((B, layer.Hv, layer.dv), dtype=odt, device=q.device)
+    core = torch.empty((B, layer.Hv, layer.dv), dtype=torch.float32, device=q.device) if want_core else None
+    so = state if in_place else torch.empty_like(state)
+    co = conv_state if in_place else torch.empty_like(conv_state)
+    decode_raw(layer, B=B, q=q, k=k, v=v, z=z, a=a, b=b, out=out, state_in=state,
+               state_out=so, conv_state_in=conv_state, conv_state_out=co,
+               core_out=core, stream=stream)
+    res = {"out": out, "final_state": so, "conv_state_out": co}
+    if want_core:
+        res["core_out"] = core
+    return res
+
+
+def selftest_mfma(A, B, C, stream=None):
+    _check(lib().gdn_selftest_mfma(_ptr(A), _ptr(B), _ptr(C), _stream(stream)))

@@ -1,0 +1,264 @@
+// gdn_abi.hip -- C-ABI front end: argument validation, workspace carving and
+// dispatch to the compiled kernel instantiations.  No allocation, no host
+// synchronisation (except the self-test), no exceptions across the ABI.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t act_size(int32_t dt) { return dt == GDN_DTYPE_BF16 ? 2 : 4; }
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// [lo, hi) byte ranges overlap partially (identical ranges are allowed).
+bool bad_alias(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    if (a0 == b0 && na == nb) return false;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+gdn_status check_layer(const gdn_layer* L, bool prefill) {
+    if (!L) return fail(GDN_ERR_INVALID_ARGUMENT, "layer is NULL");
+    if (L->Hk <= 0 || L->Hv <= 0 || L->dk <= 0 || L->dv <= 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "head counts and dims must be positive (Hk=%d Hv=%d dk=%d dv=%d)",
+                    L->Hk, L->Hv, L->dk, L->dv);
+    if (L->Hv % L->Hk != 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "Hv (%d) must be a multiple of Hk (%d)", L->Hv, L->Hk);
+    if (L->conv_K != 4) return fail(GDN_ERR_UNSUPPORTED, "conv_K=%d not compiled (only 4)", L->conv_K);
+    if (L->act_dtype != GDN_DTYPE_FP32 && L->act_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "act_dtype %d unknown", L->act_dtype);
+    if (L->out_dtype != GDN_DTYPE_FP32 && L->out_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "out_dtype %d unknown", L->out_dtype);
+    if (!(L->eps_l2 >= 0.f) || !(L->eps_rms >= 0.f))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "epsilons must be >= 0");
+    if (!L->conv_w || !L->A_log || !L->dt_bias || !L->norm_w)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "layer parameter pointer is NULL");
+    if (prefill) {
+        if (L->chunk <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "chunk must be positive");
+        if (!gdn::prefill_shape_supported(L->dk, L->dv, L->chunk))
+            return fail(GDN_ERR_UNSUPPORTED, "prefill shape dk=%d dv=%d chunk=%d not compiled",
+                        L->dk, L->dv, L->chunk);
+    } else if (!gdn::decode_shape_supported(L->dk, L->dv)) {
+        return fail(GDN_ERR_UNSUPPORTED, "decode shape dk=%d dv=%d not compiled", L->dk, L->dv);
+    }
+    return GDN_OK;
+}
+
+struct WsLayout {
+    int64_t max_chunks = 0;
+    int64_t off_chunk = 0, off_decay = 0, off_core = 0, off_vch = 0, total = 0;
+};
+
+WsLayout ws_layout(const gdn_layer* L, int32_t N, int64_t T, bool need_core) {
+    WsLayout w;
+    w.max_chunks = (L->chunk > 0 ? T / L->chunk : 0) + N;
+    int64_t o = 0;
+    w.off_chunk = o;
+    o = round_up(o + 4 * (static_cast<int64_t>(N) + 1), 256);
+    w.off_decay = o;
+    o = round_up(o + 4 * w.max_chunks * L->Hv, 256);
+    w.off_core = o;
+    if (need_core) o = round_up(o + 4 * T * L->Hv * L->dv, 256);
+    w.off_vch = o;
+    o += w.max_chunks * L->Hv * gdn::vch_bytes(L->dk, L->dv, L->chunk);
+    w.total = round_up(o, 256);
+    return w;
+}
+
+int64_t stride_or(int64_t s, int64_t dense) { return s == 0 ? dense : s; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status st) {
+    switch (st) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+size_t gdn_prefill_workspace_bytes(const gdn_layer* L, int32_t N, int64_t T) {
+    g_err[0] = 0;
+    if (check_layer(L, true) != GDN_OK) return 0;
+    if (N < 0 || T < 0) {
+        fail(GDN_ERR_INVALID_ARGUMENT, "N and T_total must be >= 0");
+        return 0;
+    }
+    // sized for the case without a caller core_out (the larger one)
+    return static_cast<size_t>(ws_layout(L, N, T, true).total);
+}
+
+gdn_status gdn_prefill(const gdn_layer* L, const gdn_prefill_io* io, void* ws, size_t ws_bytes,
+                       void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_layer(L, true);
+    if (st != GDN_OK) return st;
+    if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
+    const int32_t N = io->N;
+    const int64_t T = io->T_total;
+    if (N < 0 || T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "N (%d) and T_total (%lld) must be >= 0",
+                                    N, static_cast<long long>(T));
+    if (T > 0 && N == 0) return fail(GDN_ERR_INVALID_ARGUMENT, "T_total > 0 with N == 0");
+    if (T >= (int64_t(1) << 31)) return fail(GDN_ERR_INVALID_ARGUMENT, "T_total must be < 2^31");
+    if (N > 0 && !io->cu_seqlens) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+    const size_t es = act_size(L->act_dtype);
+    const int Hk = L->Hk, Hv = L->Hv, dk = L->dk, dv = L->dv;
+    if (T > 0) {
+        if (!io->q || !io->k || !io->v || !io->z || !io->a || !io->b)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "a token input pointer is NULL");
+        if (!io->out) return fail(GDN_ERR_INVALID_ARGUMENT, "out is NULL");
+        if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->z, 16) ||
+            !aligned(io->out, 16) || (io->core_out && !aligned(io->core_out, 16)))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "q/k/v/z/out/core_out must be 16-byte aligned");
+        if (!aligned(io->a, es) || !aligned(io->b, es))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "a/b must be element aligned");
+    }
+    const int64_t qs = stride_or(io->q_stride, int64_t(Hk) * dk), ks = stride_or(io->k_stride, int64_t(Hk) * dk);
+    const int64_t vs = stride_or(io->v_stride, int64_t(Hv) * dv), zs = stride_or(io->z_stride, int64_t(Hv) * dv);
+    const int64_t as = stride_or(io->a_stride, Hv), bs = stride_or(io->b_stride, Hv);
+    if (qs < int64_t(Hk) * dk || ks < int64_t(Hk) * dk || vs < int64_t(Hv) * dv || zs < int64_t(Hv) * dv ||
+        as < Hv || bs < Hv)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "a token stride is smaller than one token's row");
+    if (qs % 8 || ks % 8 || vs % 8 || zs % 8)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q/k/v/z strides must be multiples of 8 elements");
+    const size_t state_bytes = size_t(N) * Hv * dk * dv * 4;
+    const int64_t Cc = 2ll * Hk * dk + int64_t(Hv) * dv;
+    const size_t conv_bytes = size_t(N) * 3 * Cc * es;
+    if ((io->initial_state && !aligned(io->initial_state, 16)) || (io->final_state && !aligned(io->final_state, 16)))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "states must be 16-byte aligned");
+    if ((io->conv_state_in && !aligned(io->conv_state_in, 16)) ||
+        (io->conv_state_out && !aligned(io->conv_state_out, 16)))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "conv states must be 16-byte aligned");
+    if (bad_alias(io->initial_state, state_bytes, io->final_state, state_bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "final_state partially overlaps initial_state");
+    if (bad_alias(io->conv_state_in, conv_bytes, io->conv_state_out, conv_bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "conv_state_out partially overlaps conv_state_in");
+    const size_t out_bytes = size_t(T) * Hv * dv * (L->out_dtype == GDN_DTYPE_BF16 ? 2 : 4);
+    if (io->core_out && bad_alias(io->out, out_bytes, io->core_out, size_t(T) * Hv * dv * 4) &&
+        static_cast<const void*>(io->out) != static_cast<const void*>(io->core_out))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "out overlaps core_out");
+    if (io->core_out && static_cast<const void*>(io->out) == static_cast<const void*>(io->core_out) && T > 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "out and core_out must be different buffers");
+
+    const WsLayout w = ws_layout(L, N, T, io->core_out == nullptr);
+    if (!ws) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (need %lld bytes)", static_cast<long long>(w.total));
+    if (!aligned(ws, 256)) return fail(GDN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < static_cast<size_t>(w.total))
+        return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, need %lld", ws_bytes,
+                    static_cast<long long>(w.total));
+    if (w.max_chunks > (int64_t(1) << 30)) return fail(GDN_ERR_INVALID_ARGUMENT, "too many chunks");
+
+    gdn::PrefillParams p{};
+    p.N = N; p.Hk = Hk; p.Hv = Hv; p.G = Hv / Hk; p.T = T;
+    p.max_chunks = static_cast<int>(w.max_chunks);
+    p.scale = L->scale; p.eps_l2 = L->eps_l2; p.eps_rms = L->eps_rms;
+    p.cu = io->cu_seqlens;
+    p.conv_w = L->conv_w; p.A_log = L->A_log; p.dt_bias = L->dt_bias; p.norm_w = L->norm_w;
+    p.q = io->q; p.k = io->k; p.v = io->v; p.z = io->z; p.a = io->a; p.b = io->b;
+    p.qs = qs; p.ks = ks; p.vs = vs; p.zs = zs; p.as = as; p.bs = bs;
+    p.state_in = io->initial_state; p.state_out = io->final_state;
+    p.conv_in = io->conv_state_in; p.conv_out = io->conv_state_out;
+    p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    p.core = io->core_out ? io->core_out : reinterpret_cast<float*>(base + w.off_core);
+    p.chunk_off = reinterpret_cast<int32_t*>(base + w.off_chunk);
+    p.decay = reinterpret_cast<float*>(base + w.off_decay);
+    p.vch = base + w.off_vch;
+
+    bool supported = false;
+    hipError_t e = gdn::launch_prefill(dk, dv, L->chunk, L->act_dtype == GDN_DTYPE_BF16, p,
+                                       static_cast<hipStream_t>(stream), &supported);
+    if (!supported) return fail(GDN_ERR_UNSUPPORTED, "prefill shape not compiled");
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_layer(L, false);
+    if (st != GDN_OK) return st;
+    if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
+    const int32_t B = io->B;
+    if (B < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "B (%d) must be >= 0", B);
+    if (B == 0) return GDN_OK;
+    const int Hk = L->Hk, Hv = L->Hv, dk = L->dk, dv = L->dv;
+    const size_t es = act_size(L->act_dtype);
+    if (!io->q || !io->k || !io->v || !io->z || !io->a || !io->b)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "a token input pointer is NULL");
+    if (!io->out || !io->state_out || !io->conv_state_out)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "out, state_out and conv_state_out are required");
+    if (!aligned(io->out, 16) || !aligned(io->state_out, 16) || !aligned(io->conv_state_out, 16) ||
+        (io->state_in && !aligned(io->state_in, 16)) || (io->conv_state_in && !aligned(io->conv_state_in, 16)) ||
+        (io->core_out && !aligned(io->core_out, 16)))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "out/core_out/states must be 16-byte aligned");
+    if (!aligned(io->q, es) || !aligned(io->k, es) || !aligned(io->v, es) || !aligned(io->z, es) ||
+        !aligned(io->a, es) || !aligned(io->b, es))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "token inputs must be element aligned");
+    const int64_t qs = stride_or(io->q_stride, int64_t(Hk) * dk), ks = stride_or(io->k_stride, int64_t(Hk) * dk);
+    const int64_t vs = stride_or(io->v_stride, int64_t(Hv) * dv), zs = stride_or(io->z_stride, int64_t(Hv) * dv);
+    const int64_t as = stride_or(io->a_stride, Hv), bs = stride_or(io->b_stride, Hv);
+    if (qs < int64_t(Hk) * dk || ks < int64_t(Hk) * dk || vs < int64_t(Hv) * dv || zs < int64_t(Hv) * dv ||
+        as < Hv || bs < Hv)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "a token stride is smaller than one token's row");
+    const size_t state_bytes = size_t(B) * Hv * dk * dv * 4;
+    const int64_t Cc = 2ll * Hk * dk + int64_t(Hv) * dv;
+    const size_t conv_bytes = size_t(B) * 3 * Cc * es;
+    if (bad_alias(io->state_in, state_bytes, io->state_out, state_bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "state_out partially overlaps state_in");
+    if (bad_alias(io->conv_state_in, conv_bytes, io->conv_state_out, conv_bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "conv_state_out partially overlaps conv_state_in");
+    if (static_cast<int64_t>(B) * Hk >= (int64_t(1) << 31))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "B * Hk too large");
+
+    gdn::DecodeParams p{};
+    p.B = B; p.Hk = Hk; p.Hv = Hv; p.G = Hv / Hk;
+    p.scale = L->scale; p.eps_l2 = L->eps_l2; p.eps_rms = L->eps_rms;
+    p.conv_w = L->conv_w; p.A_log = L->A_log; p.dt_bias = L->dt_bias; p.norm_w = L->norm_w;
+    p.q = io->q; p.k = io->k; p.v = io->v; p.z = io->z; p.a = io->a; p.b = io->b;
+    p.qs = qs; p.ks = ks; p.vs = vs; p.zs = zs; p.as = as; p.bs = bs;
+    p.state_in = io->state_in; p.state_out = io->state_out;
+    p.conv_in = io->conv_state_in; p.conv_out = io->conv_state_out;
+    p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16; p.core_out = io->core_out;
+    bool supported = false;
+    hipError_t e = gdn::launch_decode(dk, dv, L->act_dtype == GDN_DTYPE_BF16, p,
+                                      static_cast<hipStream_t>(stream), &supported);
+    if (!supported) return fail(GDN_ERR_UNSUPPORTED, "decode shape not compiled");
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_selftest_mfma(const float* A, const float* B, float* C, void* stream) {
+    g_err[0] = 0;
+    if (!A || !B || !C) return fail(GDN_ERR_INVALID_ARGUMENT, "NULL pointer");
+    hipError_t e = gdn::launch_selftest_mfma(A, B, C, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "self-test failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+}  // extern "C"

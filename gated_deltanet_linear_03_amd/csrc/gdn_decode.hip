@@ -1,0 +1,233 @@
+// gdn_decode.hip -- one-token Gated DeltaNet step against carried state.
+//
+// One work-group per (sequence b, key head hk) handles the key head's conv,
+// its L2 norms, and every value head h = hk*G + g of its group.  Grouping by
+// key head lets each conv channel be owned by exactly one thread of the grid,
+// so the conv state may be updated in place; each state element is likewise
+// read and rewritten by one thread, so the recurrent state may be updated in
+// place too.
+//
+// The state of one value head is H = S^T [dk][dv] fp32 (dv fastest).  With
+// u = beta (v - e^g S k) and S_t = e^g S + u k^T (the gated delta rule of
+// Yang, Kautz, Hatamizadeh, "Gated Delta Networks", ICLR 2025, rewritten by
+// distributivity), one token needs
+//     r_k = H^T k^,  r_q = H^T q^          (one streaming read of H)
+//     u   = beta (v~ - e^g r_k),  o = e^g r_q + (k^.q^) u
+//     H' = e^g H + k^ u^T                  (one streaming write)
+// so the step is a pure HBM stream of 2 x dk x dv x 4 bytes per head; the
+// fixed state size per sequence is the one the llmxabe README's model
+// section gives (~60 MiB over 30 layers, i.e. 2 MiB per layer).
+//
+// Thread layout over H: DV/4 column groups (one float4 each) x RG row groups;
+// thread (rg, cg) holds rows rg + RG*m.  Loads of one instruction cover whole
+// 512-byte rows, so the stream is fully coalesced.  Column sums over the row
+// groups are combined through LDS in a fixed order, so the result does not
+// depend on the batch: a sequence is bit-identical batched or alone (llmxabe
+// README, "Status").
+#include "gdn_device.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+    using A = Act<BF16>;
+    using T = typename A::T;
+    constexpr int NT = 256;
+    constexpr int CG = DV / 4;          // float4 column groups
+    constexpr int RG = NT / CG;         // row groups
+    constexpr int RPT = DK / RG;        // rows per thread
+    static_assert(CG <= 64 && NT % CG == 0 && DK % RG == 0 && RPT >= 1, "shape");
+    static_assert(2 * DK <= NT, "one thread per q/k channel");
+
+    __shared__ float sq[DK], sk[DK], sv[DV], sz[DV];
+    __shared__ f32x4 red_k[RG][CG], red_q[RG][CG];
+    __shared__ float s_r[2], s_kq, s_eg, s_beta;
+
+    const int b = blockIdx.x / p.Hk;
+    const int hk = blockIdx.x % p.Hk;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int Cc = 2 * p.Hk * DK + p.Hv * DV;
+    const T* cin = static_cast<const T*>(p.conv_in);
+    T* cout = static_cast<T*>(p.conv_out);
+    const size_t crow = static_cast<size_t>(b) * 3 * Cc;
+
+    // conv1d(K=4) + SiLU of the q and k channels; shift their conv state.
+    if (tid < 2 * DK) {
+        const int isk = tid >= DK;
+        const int i = tid - isk * DK;
+        const int c = isk * p.Hk * DK + hk * DK + i;
+        const T* src = isk ? static_cast<const T*>(p.k) + b * p.ks + hk * DK + i
+                           : static_cast<const T*>(p.q) + b * p.qs + hk * DK + i;
+        T x = *src;
+        T t0 = cin ? cin[crow + c] : T(0);
+        T t1 = cin ? cin[crow + Cc + c] : T(0);
+        T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
+        const float* w = p.conv_w + static_cast<size_t>(c) * 4;
+        float acc = w[0] * A::load(&t0);
+        acc = fmaf(w[1], A::load(&t1), acc);
+        acc = fmaf(w[2], A::load(&t2), acc);
+        acc = fmaf(w[3], A::load(&x), acc);
+        (isk ? sk : sq)[i] = silu(acc);
+        cout[crow + c] = t1;
+        cout[crow + Cc + c] = t2;
+        cout[crow + 2 * Cc + c] = x;
+    }
+    __syncthreads();
+    if (wave < 2) {
+        const float* src = wave == 0 ? sq : sk;
+        float ss = 0.f;
+        for (int i = lane; i < DK; i += kWave) ss = fmaf(src[i], src[i], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) s_r[wave] = (wave == 0 ? p.scale : 1.0f) / sqrtf(ss + p.eps_l2);
+    }
+    __syncthreads();
+    if (tid < 2 * DK) {
+        if (tid < DK) sq[tid] *= s_r[0];
+        else sk[tid - DK] *= s_r[1];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float d = 0.f;
+        for (int i = lane; i < DK; i += kWave) d = fmaf(sk[i], sq[i], d);
+        d = wave_sum(d);
+        if (lane == 0) s_kq = d;
+    }
+
+    const int cg = tid % CG, rg = tid / CG;
+    for (int g = 0; g < p.G; ++g) {
+        const int h = hk * p.G + g;
+        // conv + SiLU of this head's v channels, gate inputs.
+        for (int j = tid; j < DV; j += NT) {
+            const int c = 2 * p.Hk * DK + h * DV + j;
+            T x = static_cast<const T*>(p.v)[b * p.vs + h * DV + j];
+            T t0 = cin ? cin[crow + c] : T(0);
+            T t1 = cin ? cin[crow + Cc + c] : T(0);
+            T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
+            const float* w = p.conv_w + static_cast<size_t>(c) * 4;
+            float acc = w[0] * A::load(&t0);
+            acc = fmaf(w[1], A::load(&t1), acc);
+            acc = fmaf(w[2], A::load(&t2), acc);
+            acc = fmaf(w[3], A::load(&x), acc);
+            sv[j] = silu(acc);
+            sz[j] = A::load(static_cast<const T*>(p.z) + b * p.zs + h * DV + j);
+            cout[crow + c] = t1;
+            cout[crow + Cc + c] = t2;
+            cout[crow + 2 * Cc + c] = x;
+        }
+        if (tid == 0) {
+            const float av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
+            const float bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
+            const float gg = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
+            s_eg = expf(gg);
+            s_beta = sigmoid(bv);
+        }
+        __syncthreads();
+
+        const size_t hbase = (static_cast<size_t>(b) * p.Hv + h) * DK * DV;
+        f32x4 H[RPT];
+        f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            if (p.state_in) {
+                H[m] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(p.state_in + hbase + static_cast<size_t>(i) * DV) + cg);
+            } else {
+                H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float kk = sk[i], qq = sq[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                rk[e] = fmaf(H[m][e], kk, rk[e]);
+                rq[e] = fmaf(H[m][e], qq, rq[e]);
+            }
+        }
+        red_k[rg][cg] = rk;
+        red_q[rg][cg] = rq;
+        __syncthreads();
+        f32x4 RK = red_k[0][cg], RQ = red_q[0][cg];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            f32x4 a = red_k[r][cg], c = red_q[r][cg];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { RK[e] += a[e]; RQ[e] += c[e]; }
+        }
+        const float eg = s_eg, beta = s_beta, kq = s_kq;
+        f32x4 u, o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[e] = beta * (sv[4 * cg + e] - eg * RK[e]);
+            o[e] = fmaf(eg, RQ[e], kq * u[e]);
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float kk = sk[i];
+            f32x4 hn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hn[e] = fmaf(eg, H[m][e], kk * u[e]);
+            __builtin_nontemporal_store(
+                hn, reinterpret_cast<f32x4*>(p.state_out + hbase + static_cast<size_t>(i) * DV) + cg);
+        }
+        // z-gated RMSNorm over dv: row group 0 (lanes 0..CG-1 of wave 0).
+        if (wave == 0) {
+            float ps = 0.f;
+            if (lane < CG) ps = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+            ps = wave_sum(ps);
+            if (lane < CG) {
+                const float r = 1.0f / sqrtf(ps / DV + p.eps_rms);
+                const size_t obase = (static_cast<size_t>(b) * p.Hv + h) * DV + 4 * cg;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = p.norm_w[4 * cg + e] * (o[e] * r) * silu(sz[4 * cg + e]);
+                if (p.out_bf16) {
+                    uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
+                } else {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) =
+                        f32x4{y[0], y[1], y[2], y[3]};
+                }
+                if (p.core_out)
+                    *reinterpret_cast<f32x4*>(p.core_out + obase) = o;
+            }
+        }
+        __syncthreads();   // LDS (sv, sz, red_*) reused by the next value head
+    }
+}
+
+template <int DK, int DV, bool BF16>
+static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.Hk));
+    hipLaunchKernelGGL((decode_kernel<DK, DV, BF16>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+bool decode_shape_supported(int DK, int DV) {
+    return (DK == 128 && DV == 128) || (DK == 32 && DV == 32) || (DK == 32 && DV == 64) ||
+           (DK == 64 && DV == 64);
+}
+
+hipError_t launch_decode(int DK, int DV, bool bf16, const DecodeParams& p, hipStream_t s,
+                         bool* supported) {
+    *supported = true;
+#define GDN_DEC(dk, dv)                                                              \
+    if (DK == dk && DV == dv)                                                        \
+        return bf16 ? launch_decode_t<dk, dv, true>(p, s) : launch_decode_t<dk, dv, false>(p, s);
+    GDN_DEC(128, 128)
+    GDN_DEC(32, 32)
+    GDN_DEC(32, 64)
+    GDN_DEC(64, 64)
+#undef GDN_DEC
+    *supported = false;
+    return hipSuccess;
+}
+
+}  // namespace gdn

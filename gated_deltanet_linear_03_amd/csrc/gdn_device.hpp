@@ -1,0 +1,106 @@
+// gdn_device.hpp -- device helpers shared by the gfx950 Gated DeltaNet kernels.
+//
+// Matrix-core fragments (v_mfma_f32_16x16x32_bf16, one wave of 64 lanes):
+//   A operand, 16 rows x 32 k:  lane l holds row (l % 16), k = 8*(l/16) + e,
+//                               e = 0..7 (eight bf16, 16 bytes)
+//   B operand, 32 k x 16 cols:  lane l holds col (l % 16), k = 8*(l/16) + e
+//   C/D,      16 x 16 fp32:     lane l holds col (l % 16), rows 4*(l/16) + i,
+//                               i = 0..3
+// gdn_selftest_mfma checks this layout on the device.
+//
+// Products run in split-bf16 form: x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi), and a*b ~= a_hi*b_hi + a_hi*b_lo + a_lo*b_hi with fp32
+// accumulation (Henry, Tang, Heinecke, "Leveraging the bfloat16 Artificial
+// Intelligence Datatype For Higher-Precision Computations", ARITH 2019).  The
+// dropped a_lo*b_lo term and the rounding of lo leave ~2^-16 relative error
+// per product, against 2^-8 for a single bf16 rounding.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+
+// ---- scalar conversions ---------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Split x into hi + lo, both bf16 bit patterns.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16_bits(x);
+    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+template <bool BF16>
+struct Act;
+template <>
+struct Act<true> {
+    using T = uint16_t;
+    __device__ __forceinline__ static float load(const T* p) { return bf16_bits_to_f32(*p); }
+    __device__ __forceinline__ static T from_f32(float x) { return f32_to_bf16_bits(x); }
+};
+template <>
+struct Act<false> {
+    using T = float;
+    __device__ __forceinline__ static float load(const T* p) { return *p; }
+    __device__ __forceinline__ static T from_f32(float x) { return x; }
+};
+
+// ---- elementwise math (ROCm device libm) ------------------------------------
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ float softplus(float x) {
+    return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ---- matrix-core product ---------------------------------------------------
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// acc += (a_hi + a_lo) * (b_hi + b_lo) without the lo*lo term.
+__device__ __forceinline__ f32x4 mfma3(u32x4 ahi, u32x4 alo, u32x4 bhi, u32x4 blo,
+                                        f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo), as_bf16x8(bhi), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi), as_bf16x8(blo), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi), as_bf16x8(bhi), acc, 0, 0, 0);
+    return acc;
+}
+
+// Pack 8 bf16 bit patterns (e = 0..7) into one 16-byte fragment register.
+__device__ __forceinline__ u32x4 pack8(const uint16_t* h) {
+    u32x4 r;
+    r[0] = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+    r[1] = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
+    r[2] = static_cast<uint32_t>(h[4]) | (static_cast<uint32_t>(h[5]) << 16);
+    r[3] = static_cast<uint32_t>(h[6]) | (static_cast<uint32_t>(h[7]) << 16);
+    return r;
+}
+
+// Deterministic wave-wide sum (xor butterfly: every lane ends with the same
+// bits because each level adds the same two partial sums).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+}  // namespace gdn

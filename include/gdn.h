@@ -1,0 +1,165 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet layer library.
+ *
+ * The layer is the recurrent block of the hybrid Qwen3.x models described on
+ * the llmxabe README ("Status" and the model section: three of every four
+ * layers are Gated DeltaNet, each carrying a fixed-size recurrent state of
+ * about 2 MiB per sequence, ~60 MiB over 30 layers) and on skindeep.ai "Our
+ * own inference runtime" ("What it is": 36 of 48 layers are gated delta net).
+ * It computes, per sequence and value head, token by token:
+ *
+ *   conv:   x~ = SiLU(causal depthwise conv1d_K(x)) over the q|k|v channels
+ *   norm:   q^ = scale * q~ / sqrt(|q~|^2 + eps_l2),  k^ = k~ / sqrt(|k~|^2 + eps_l2)
+ *   gates:  g = -exp(A_log) * softplus(a + dt_bias),  beta = sigmoid(b)
+ *   rule:   S_t = exp(g_t) S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v~_t k^_t^T,
+ *           o_t = S_t q^_t                      (Yang, Kautz, Hatamizadeh,
+ *           "Gated Delta Networks", ICLR 2025, gated delta rule)
+ *   gate:   out = norm_w (.) o / sqrt(mean(o^2) + eps_rms) (.) SiLU(z)
+ *
+ * Two entry points: gdn_prefill (many tokens per sequence, packed varlen,
+ * chunked WY/UT form, optional carried state in and out) and gdn_decode (one
+ * token per sequence against carried conv and recurrent state).  Batched
+ * results are bit-identical to the same sequence run alone -- the serving
+ * contract on the llmxabe README, "Status": a sequence decodes identically
+ * whether batched with others or alone.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *   allocates nothing, keeps no state besides its code objects, and never
+ *   synchronises the host; all work is enqueued on `stream` (a hipStream_t;
+ *   NULL = the default stream).  Device-side faults surface at the caller's
+ *   next synchronisation.
+ * - Layouts are row-major, innermost dimension contiguous:
+ *     q, k           [tokens][Hk][dk]    (token stride q_stride/k_stride)
+ *     v, z           [tokens][Hv][dv]    (token stride v_stride/z_stride)
+ *     a, b           [tokens][Hv]        (token stride a_stride/b_stride)
+ *     out, core_out  [tokens][Hv][dv]    dense
+ *     state          [seq][Hv][dk][dv]   fp32, holding S^T:
+ *                                        state[n][h][i][j] = S_{n,h}[j][i]
+ *     conv state     [seq][K-1][Cc]      act dtype, oldest tap first,
+ *                                        Cc = 2*Hk*dk + Hv*dv, channels
+ *                                        q (head-major), then k, then v
+ *     conv_w         [Cc][K] fp32, conv_w[c][K-1] multiplies the current token
+ *   Token strides are in elements; 0 means dense.  Value head h reads key
+ *   head h / (Hv/Hk).
+ * - Alignment: q, k, v, z, out, core_out, states and conv states 16 bytes;
+ *   strides of q/k/v/z multiples of 8 elements; a, b 4 bytes.
+ * - Errors: the return value is GDN_OK after a successful enqueue, otherwise
+ *   a status code with detail text in gdn_last_error() (thread-local).  No
+ *   work is enqueued when a call returns an error.  Device contents
+ *   (cu_seqlens values, NaNs) are not validated.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad sizes, bad aliasing */
+    GDN_ERR_UNSUPPORTED = 2,      /* shape or dtype combination not compiled */
+    GDN_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+    GDN_ERR_HIP = 4               /* a HIP runtime call failed */
+} gdn_status;
+
+typedef enum { GDN_DTYPE_FP32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+
+/* Static description of one layer.  Compiled shapes (dk, dv, chunk):
+ * (32, 32, 16), (32, 64, 16), (64, 64, 32), (128, 128, 64), (128, 128, 32);
+ * conv_K = 4; act_dtype fp32 or bf16; out_dtype fp32 or bf16. */
+typedef struct {
+    int32_t Hk, Hv;          /* key/query heads, value heads; Hv % Hk == 0 */
+    int32_t dk, dv;          /* key and value head dims */
+    int32_t conv_K;          /* conv taps (4) */
+    int32_t chunk;           /* prefill chunk length C */
+    int32_t act_dtype;       /* gdn_dtype of q, k, v, z, a, b and conv states */
+    int32_t out_dtype;       /* gdn_dtype of out */
+    float scale;             /* q scale (1/sqrt(dk) for the Qwen3.x layers) */
+    float eps_l2;            /* L2-norm epsilon */
+    float eps_rms;           /* RMSNorm epsilon */
+    const float* conv_w;     /* [Cc][K] */
+    const float* A_log;      /* [Hv] */
+    const float* dt_bias;    /* [Hv] */
+    const float* norm_w;     /* [dv], shared by all heads */
+} gdn_layer;
+
+/* Chunked prefill over N packed sequences.  Sequence n owns tokens
+ * [cu_seqlens[n], cu_seqlens[n+1]); lengths may be 0 (states pass through).
+ * initial_state NULL means zeros; final_state may equal initial_state
+ * (in-place update) but must not partially overlap it; NULL = not written.
+ * conv_state_in NULL means zero history; conv_state_out may equal
+ * conv_state_in; NULL = not written.  core_out (optional) receives o_t
+ * before the gated RMSNorm, in fp32. */
+typedef struct {
+    int32_t N;
+    int64_t T_total;               /* == cu_seqlens[N] */
+    const int32_t* cu_seqlens;     /* device int32 [N+1], non-decreasing, [0] = 0 */
+    const void *q, *k, *v, *z, *a, *b;
+    int64_t q_stride, k_stride, v_stride, z_stride, a_stride, b_stride;
+    const float* initial_state;
+    float* final_state;
+    const void* conv_state_in;
+    void* conv_state_out;
+    void* out;                     /* out_dtype */
+    float* core_out;               /* optional */
+} gdn_prefill_io;
+
+/* One token for each of B sequences.  state_out may equal state_in and
+ * conv_state_out may equal conv_state_in (in-place); partial overlap is an
+ * error.  state_in NULL means zeros; conv_state_in NULL means zero history. */
+typedef struct {
+    int32_t B;
+    const void *q, *k, *v, *z, *a, *b;   /* one token per sequence */
+    int64_t q_stride, k_stride, v_stride, z_stride, a_stride, b_stride;
+    const float* state_in;
+    float* state_out;                    /* required */
+    const void* conv_state_in;
+    void* conv_state_out;                /* required */
+    void* out;                           /* [B][Hv][dv], out_dtype */
+    float* core_out;                     /* optional [B][Hv][dv] fp32 */
+} gdn_decode_io;
+
+/* Version of this header's structs and layouts. */
+int gdn_abi_version(void);
+
+/* Bytes of device workspace gdn_prefill needs for N sequences holding
+ * T_total tokens in all (an upper bound over every length split).  Returns
+ * 0 and sets gdn_last_error() if the layer is invalid or unsupported. */
+size_t gdn_prefill_workspace_bytes(const gdn_layer* layer, int32_t N,
+                                   int64_t T_total);
+
+/* Enqueue the chunked prefill.  workspace: device memory of at least
+ * gdn_prefill_workspace_bytes(layer, N, T_total) bytes, 256-byte aligned,
+ * not shared with a concurrently running call. */
+gdn_status gdn_prefill(const gdn_layer* layer, const gdn_prefill_io* io,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Enqueue one decode step (no workspace needed). */
+gdn_status gdn_decode(const gdn_layer* layer, const gdn_decode_io* io,
+                      void* stream);
+
+/* Static text for a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Library self-test of the matrix-core fragment layout the kernels rely on:
+ * computes C[16][16] = A[16][32] * B[32][16] (row-major fp32 in/out, device
+ * pointers) through one bf16 hi/lo split product on v_mfma_f32_16x16x32_bf16
+ * and synchronises the stream.  Returns GDN_OK or GDN_ERR_HIP. */
+gdn_status gdn_selftest_mfma(const float* A, const float* B, float* C,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H_ */

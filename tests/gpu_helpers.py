@@ -1,0 +1,129 @@
+"""Shared helpers of the GPU parity tests: move a synthetic case to the
+device, run the HIP path through the C ABI, run the fp64 oracle on the same
+bits, and compute the error metric.
+
+Error metric (per output tensor and per sequence): max|y - r| / max|r|, the
+worst absolute error scaled by the largest reference magnitude of that
+sequence's tensor.  The bar is 2e-3 for fp32 outputs from bf16 inputs with
+fp32 state; conv states must match exactly."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import gated_deltanet_linear_03_amd as gdn
+import oracle
+
+TOL = 2e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    return t if dtype is None else t.to(dtype)
+
+
+def act_dtype(shape):
+    return torch.bfloat16 if shape.act_dtype == "bf16" else torch.float32
+
+
+def make_layer(case_or_shape, params, out_dtype=gdn.GDN_DTYPE_FP32):
+    sh = case_or_shape
+    return gdn.Layer(Hk=sh.Hk, Hv=sh.Hv, dk=sh.dk, dv=sh.dv, chunk=sh.chunk,
+                     conv_w=to_dev(params["conv_w"]), A_log=to_dev(params["A_log"]),
+                     dt_bias=to_dev(params["dt_bias"]), norm_w=to_dev(params["norm_w"]),
+                     act_dtype=gdn.GDN_DTYPE_BF16 if sh.act_dtype == "bf16" else gdn.GDN_DTYPE_FP32,
+                     out_dtype=out_dtype, scale=sh.scale, eps_l2=sh.eps_l2,
+                     eps_rms=sh.eps_rms)
+
+
+def dims(sh):
+    return oracle.Dims(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, sh.scale, sh.eps_l2, sh.eps_rms)
+
+
+def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=False):
+    sh = case.shape
+    ad = act_dtype(sh)
+    layer = make_layer(sh, case.params, out_dtype)
+    x = {k: to_dev(v, ad) for k, v in case.inputs.items()}
+    cu = to_dev(case.cu_seqlens)
+    S0 = None if case.initial_state is None else to_dev(case.initial_state)
+    C0 = None if case.conv_state is None else to_dev(case.conv_state, ad)
+    res = gdn.prefill(layer, x["q"], x["k"], x["v"], x["z"], x["a"], x["b"], cu,
+                      initial_state=S0, conv_state_in=C0, want_core=want_core,
+                      in_place=in_place)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_prefill(case, heads_of_key=None, nthreads=0):
+    """fp64 oracle on the same bits.  heads_of_key: restrict to the listed
+    key heads (and their value heads), returning arrays for those heads."""
+    sh = case.shape
+    x = case.inputs
+    p = case.params
+    if heads_of_key is None:
+        return oracle.gdn_forward(dims(sh), case.cu_seqlens, x["q"], x["k"], x["v"],
+                                  x["z"], x["a"], x["b"], p["conv_w"], p["A_log"],
+                                  p["dt_bias"], p["norm_w"], case.initial_state,
+                                  case.conv_state, nthreads=nthreads)
+    G = sh.Hv // sh.Hk
+    hk = list(heads_of_key)
+    hv = [h for k in hk for h in range(k * G, (k + 1) * G)]
+    qk = sh.Hk * sh.dk
+    ch = ([k * sh.dk + i for k in hk for i in range(sh.dk)] +
+          [qk + k * sh.dk + i for k in hk for i in range(sh.dk)] +
+          [2 * qk + h * sh.dv + j for h in hv for j in range(sh.dv)])
+    d = oracle.Dims(len(hk), len(hv), sh.dk, sh.dv, sh.K, sh.scale, sh.eps_l2, sh.eps_rms)
+    S0 = None if case.initial_state is None else case.initial_state[:, hv]
+    C0 = None if case.conv_state is None else case.conv_state[:, :, ch]
+    r = oracle.gdn_forward(d, case.cu_seqlens, x["q"][:, hk], x["k"][:, hk], x["v"][:, hv],
+                           x["z"][:, hv], x["a"][:, hv], x["b"][:, hv], p["conv_w"][ch],
+                           p["A_log"][hv], p["dt_bias"][hv], p["norm_w"], S0, C0,
+                           nthreads=nthreads)
+    r["heads"] = hv
+    r["channels"] = ch
+    return r
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.abs(ref).max()
+    if den == 0.0:
+        return float(np.abs(got).max())
+    return float(np.abs(got - ref).max() / den)
+
+
+def per_seq_errors(cu, got, ref):
+    """Token tensors [T, ...]: max over sequences of the metric."""
+    errs = []
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b > a:
+            errs.append(rel_err(got[a:b], ref[a:b]))
+    return max(errs) if errs else 0.0
+
+
+def state_errors(got, ref):
+    return max(rel_err(got[n], ref[n]) for n in range(got.shape[0])) if got.shape[0] else 0.0
+
+
+def check_prefill(case, res, ref, tol=TOL, heads=None, label=""):
+    cu = case.cu_seqlens
+    sel = slice(None) if heads is None else heads
+    out = res["out"].float().cpu().numpy()[:, sel]
+    e_out = per_seq_errors(cu, out, ref["out"])
+    e_core = per_seq_errors(cu, res["core_out"].cpu().numpy()[:, sel], ref["core_out"]) \
+        if "core_out" in res else 0.0
+    e_state = state_errors(res["final_state"].cpu().numpy()[:, sel], ref["final_state"])
+    print(f"{label} out {e_out:.3e} core {e_core:.3e} state {e_state:.3e}", flush=True)
+    assert e_out < tol and e_core < tol and e_state < tol, (e_out, e_core, e_state)
+    cs = res["conv_state_out"].float().cpu().numpy()
+    if heads is not None:
+        cs = cs[:, :, ref["channels"]]
+    assert np.array_equal(cs, ref["conv_state_out"]), "conv state differs"
+    return e_out, e_core, e_state

@@ -1,0 +1,158 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/gdn.h declares, and rejects bad arguments on the host (status code
+and message, no crash, nothing enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_linear_03_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("gdn_prefill", "gdn_decode", "gdn_prefill_workspace_bytes",
+              "gdn_abi_version", "gdn_status_string", "gdn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
+    assert L.gdn_abi_version() == 1
+
+
+def test_status_strings():
+    L = gdn.lib()
+    for st in range(5):
+        assert L.gdn_status_string(st)
+    assert L.gdn_status_string(99) == b"unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any device use
+
+
+def _layer(**kw):
+    base = dict(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=None, A_log=None,
+                dt_bias=None, norm_w=None)
+    base.update(kw)
+    L = gdn.Layer(**base)
+    cl = L.c()
+    for f in ("conv_w", "A_log", "dt_bias", "norm_w"):
+        if getattr(cl, f) is None and kw.get(f, "x") is None:
+            continue
+    return cl
+
+
+def _full_layer(**kw):
+    cl = _layer(**kw)
+    cl.conv_w = cl.A_log = cl.dt_bias = cl.norm_w = FAKE
+    for k_, v_ in kw.items():
+        setattr(cl, k_, v_)
+    return cl
+
+
+def _ws(cl, N, T):
+    return gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(cl), N, T)
+
+
+def test_workspace_query_monotone_and_rejects():
+    cl = _full_layer()
+    sizes = [_ws(cl, 1, T) for T in (0, 1, 64, 65, 4096, 131072)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert _ws(cl, 8, 4096) >= _ws(cl, 1, 4096)
+    assert _ws(_full_layer(Hv=30), 1, 64) == 0          # Hv % Hk != 0
+    assert b"multiple" in gdn.lib().gdn_last_error()
+    assert _ws(_full_layer(dk=96), 1, 64) == 0          # not compiled
+    assert _ws(_full_layer(conv_w=None), 1, 64) == 0
+
+
+def _pio(**kw):
+    io = gdn.CPrefillIO()
+    io.N, io.T_total, io.cu_seqlens = 1, 64, FAKE
+    for f in ("q", "k", "v", "z", "a", "b", "out"):
+        setattr(io, f, FAKE)
+    for k_, v_ in kw.items():
+        setattr(io, k_, v_)
+    return io
+
+
+def _prefill(cl, io, ws=FAKE, nb=1 << 40):
+    return gdn.lib().gdn_prefill(ctypes.byref(cl), ctypes.byref(io), ws, nb, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(N=-1), gdn.GDN_ERR_INVALID_ARGUMENT, b">= 0"),
+    (dict(cu_seqlens=None), gdn.GDN_ERR_INVALID_ARGUMENT, b"cu_seqlens"),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARGUMENT, b"NULL"),
+    (dict(out=None), gdn.GDN_ERR_INVALID_ARGUMENT, b"out"),
+    (dict(q=FAKE + 2), gdn.GDN_ERR_INVALID_ARGUMENT, b"aligned"),
+    (dict(q_stride=100), gdn.GDN_ERR_INVALID_ARGUMENT, b"stride"),
+    (dict(q_stride=16 * 128 + 4), gdn.GDN_ERR_INVALID_ARGUMENT, b"multiples"),
+    (dict(T_total=5, N=0), gdn.GDN_ERR_INVALID_ARGUMENT, b"N == 0"),
+    (dict(initial_state=FAKE, final_state=FAKE + 16), gdn.GDN_ERR_INVALID_ARGUMENT, b"overlaps"),
+    (dict(conv_state_in=FAKE, conv_state_out=FAKE + 256), gdn.GDN_ERR_INVALID_ARGUMENT, b"overlaps"),
+])
+def test_prefill_rejects(kw, status, msg):
+    st = _prefill(_full_layer(), _pio(**kw))
+    assert st == status
+    assert msg in gdn.lib().gdn_last_error()
+
+
+def test_prefill_workspace_errors():
+    cl = _full_layer()
+    assert _prefill(cl, _pio(), ws=None) == gdn.GDN_ERR_WORKSPACE
+    assert _prefill(cl, _pio(), ws=FAKE + 16) == gdn.GDN_ERR_WORKSPACE
+    assert _prefill(cl, _pio(), nb=1024) == gdn.GDN_ERR_WORKSPACE
+    assert b"need" in gdn.lib().gdn_last_error()
+
+
+def test_prefill_unsupported_shape():
+    assert _prefill(_full_layer(dk=64, dv=64, chunk=48), _pio()) == gdn.GDN_ERR_UNSUPPORTED
+    assert _prefill(_full_layer(conv_K=3), _pio()) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def _dio(**kw):
+    io = gdn.CDecodeIO()
+    io.B = 4
+    for f in ("q", "k", "v", "z", "a", "b", "out", "state_in", "state_out",
+              "conv_state_in", "conv_state_out"):
+        setattr(io, f, FAKE)
+    for k_, v_ in kw.items():
+        setattr(io, k_, v_)
+    return io
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(state_out=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(conv_state_out=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(out=FAKE + 4), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(state_out=FAKE + 4096), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(v_stride=3), gdn.GDN_ERR_INVALID_ARGUMENT),
+])
+def test_decode_rejects(kw, status):
+    st = gdn.lib().gdn_decode(ctypes.byref(_full_layer()), ctypes.byref(_dio(**kw)), None)
+    assert st == status
+    assert gdn.lib().gdn_last_error()
+
+
+def test_decode_zero_batch_is_a_no_op():
+    assert gdn.lib().gdn_decode(ctypes.byref(_full_layer()), ctypes.byref(_dio(B=0)), None) == 0
+
+
+def test_decode_unsupported_shape():
+    st = gdn.lib().gdn_decode(ctypes.byref(_full_layer(dk=48)), ctypes.byref(_dio()), None)
+    assert st == gdn.GDN_ERR_UNSUPPORTED

@@ -1,0 +1,121 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded bits.  Bar: max|y - r| / max|r| < 2e-3 per tensor and sequence
+(out, core_out, final_state); conv states exact."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_linear_03_amd as gdn
+from gated_deltanet_linear_03_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import (TOL, check_prefill, gpu_prefill, oracle_prefill,  # noqa: E402
+                         to_dev)
+
+
+def test_mfma_fragment_layout():
+    r = np.random.default_rng(0)
+    A = r.standard_normal((16, 32)).astype(np.float32)
+    B = r.standard_normal((32, 16)).astype(np.float32)
+    C = torch.empty((16, 16), dtype=torch.float32, device="cuda")
+    gdn.selftest_mfma(to_dev(A), to_dev(B), C)
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    err = np.abs(C.cpu().numpy() - ref).max() / np.abs(ref).max()
+    print("mfma split-bf16 product rel err", err)
+    assert err < 1e-4
+
+
+def test_prefill_tiny():
+    """1 x 64 tokens, 2/4 heads, dk = dv = 32, chunk 16, fp32, zero state."""
+    case = synth.tiny_case(0)
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="tiny")
+
+
+def test_prefill_tiny_varlen_states():
+    """ragged lengths (partial chunks, empty and one-token sequences) with
+    carried recurrent and conv states."""
+    case = synth.prefill_case(synth.TINY, [37, 0, 27, 1, 16, 3, 2], seed=5,
+                              with_state=True, with_conv_state=True,
+                              norm_w_jitter=True)
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="tiny-varlen")
+
+
+def test_prefill_dk_ne_dv():
+    """dk = 32, dv = 64: a transposed state would not match."""
+    sh = synth.LayerShape(Hk=2, Hv=4, dk=32, dv=64, chunk=16, act_dtype="bf16")
+    case = synth.prefill_case(sh, [45, 19], seed=6, with_state=True,
+                              with_conv_state=True)
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="dk!=dv")
+
+
+def test_prefill_full_shape_ragged():
+    """16/32 heads, 128/128, chunk 64, bf16: several chunks and ragged tails."""
+    case = synth.prefill_case(synth.FULL, [200, 64, 1, 130, 0], seed=7,
+                              with_state=True, with_conv_state=True)
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="full-ragged")
+
+
+def test_prefill_4k():
+    """1 x 4096 tokens at 16/32 heads, 128/128, chunk 64, bf16, zero state."""
+    case = synth.prefill_4k_case(1)
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="4k")
+
+
+def test_prefill_weak_decay():
+    """A_log in [ln 1e-4, ln 1e-3]: decay ~1, long-range state passing."""
+    case = synth.prefill_case(synth.FULL, [1000, 300], seed=9, with_state=True,
+                              A_log_range=(math.log(1e-4), math.log(1e-3)))
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="weak-decay")
+
+
+def test_prefill_bf16_out_is_rounded_fp32_out():
+    case = synth.prefill_case(synth.FULL, [150, 70], seed=10, with_state=True)
+    r32 = gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32)
+    r16 = gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_BF16)
+    assert torch.equal(r32["out"].to(torch.bfloat16), r16["out"])
+    assert torch.equal(r32["final_state"], r16["final_state"])
+
+
+def _decode_case(sh, B, seed):
+    x = synth.token_inputs(sh, B, seed)
+    S0 = synth.initial_states(sh, B, seed)
+    C0 = synth.conv_states(sh, B, seed)
+    return x, S0, C0
+
+
+def _gpu_decode(sh, params, x, S0, C0, in_place=True):
+    from gpu_helpers import act_dtype, make_layer
+    ad = act_dtype(sh)
+    layer = make_layer(sh, params)
+    t = {k: to_dev(v, ad) for k, v in x.items()}
+    st = to_dev(S0)
+    cs = to_dev(C0, ad)
+    res = gdn.decode(layer, t["q"], t["k"], t["v"], t["z"], t["a"], t["b"], st, cs,
+                     in_place=in_place, want_core=True)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("shape_name,B", [("full", 3), ("full", 64), ("tiny", 5)])
+def test_decode_parity(shape_name, B):
+    sh = synth.FULL if shape_name == "full" else synth.TINY
+    params = synth.layer_params(sh, 21)
+    x, S0, C0 = _decode_case(sh, B, 22)
+    res = _gpu_decode(sh, params, x, S0, C0)
+    import oracle
+    from gpu_helpers import dims, rel_err
+    ref = oracle.gdn_forward(dims(sh), np.arange(B + 1), x["q"], x["k"], x["v"], x["z"],
+                             x["a"], x["b"], params["conv_w"], params["A_log"],
+                             params["dt_bias"], params["norm_w"], S0, C0)
+    out = res["out"].cpu().numpy()
+    core = res["core_out"].cpu().numpy()
+    st = res["final_state"].cpu().numpy()
+    e = [max(rel_err(out[b], ref["out"][b]) for b in range(B)),
+         max(rel_err(core[b], ref["core_out"][b]) for b in range(B)),
+         max(rel_err(st[b], ref["final_state"][b]) for b in range(B))]
+    print(f"decode {shape_name} B={B} out {e[0]:.3e} core {e[1]:.3e} state {e[2]:.3e}")
+    assert max(e) < TOL
+    assert np.array_equal(res["conv_state_out"].float().cpu().numpy(), ref["conv_state_out"])
