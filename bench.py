@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet layer hot path on one MI355X.
+
+Headline (``value``): prefill tokens/s of one layer at the 35B-A3B shape
+(1 sequence x 4096 tokens, 16 key / 32 value heads, dk = dv = 128, chunk
+64, bf16 activations, fp32 state from zero), one ``gdn_prefill`` call per
+step with inputs resident in HBM.  The same JSON line carries
+
+* ``roofline``      the dominant prefill kernel against its peak, with its
+                    duration from HIP events recorded between the kernels
+                    inside the timed region (``gdn_prefill_timed``);
+* ``decode``        one decode step (one token per sequence) through 30
+                    stacked layers at B = 64 (plus B = 1 and 3): state GB/s
+                    against the 8 TB/s HBM peak, states carried in place;
+* ``long_prefill``  1 x 131072 tokens resuming from a N(0, 0.02) state;
+* ``varlen_prefill`` 8 packed sequences with log-uniform lengths;
+* ``cpu_baseline``  the fp64 oracle on the host cores over the same 4096
+                    token workload (a reported baseline, not a target).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--decode-batches", default="64,3,1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+# ---- algorithmic work per token / per sequence (definitions in the design doc) --
+
+def prefill_flops_per_token(Hk, Hv, dk, dv, C):
+    """Matrix products of the chunked form, counted once (triangles at
+    half): per value head, the scan's W H, Q H, K_d^T U (2 dk dv each) and
+    P U ((C+1) dv); the prep's Grams per key head ((C-1) dk + (C+1) dk),
+    the triangular solve (C^2/3), W and U~ ((C+1)(dk + dv))."""
+    scan = Hv * (3 * 2 * dk * dv + (C + 1) * dv)
+    prep = Hk * ((C - 1) * dk + (C + 1) * dk) + Hv * (C * C / 3 + (C + 1) * (dk + dv))
+    return scan, prep
+
+
+def decode_bytes_per_seq(Hk, Hv, dk, dv, act_bytes=2, out_bytes=4):
+    Cc = 2 * Hk * dk + Hv * dv
+    state = 2 * Hv * dk * dv * 4
+    conv = 2 * 3 * Cc * act_bytes
+    tok = (2 * Hk * dk + 2 * Hv * dv + 2 * Hv) * act_bytes
+    out = Hv * dv * out_bytes
+    return state + conv + tok + out, state
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer's data-parallel hot path "
+              "runs on a single MI355X (sequences shard across GPUs with no "
+              "exchange); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_linear_03_amd as gdn
+    from gated_deltanet_linear_03_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = synth.FULL
+
+    def layer_from(params):
+        t = {k: torch.from_numpy(v).to(dev) for k, v in params.items()}
+        return gdn.Layer(Hk=sh.Hk, Hv=sh.Hv, dk=sh.dk, dv=sh.dv, chunk=sh.chunk,
+                         act_dtype=gdn.GDN_DTYPE_BF16, out_dtype=gdn.GDN_DTYPE_FP32,
+                         scale=sh.scale, eps_l2=sh.eps_l2, eps_rms=sh.eps_rms, **t)
+
+    def bf16_dev(a):
+        return torch.from_numpy(a).to(dev).to(torch.bfloat16)
+
+    def gpu_inputs(T, gen):
+        """Seeded device-side draws with the workload's distributions."""
+        def n(*s):
+            return torch.randn(*s, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        return {"q": n(T, sh.Hk, sh.dk), "k": n(T, sh.Hk, sh.dk), "v": n(T, sh.Hv, sh.dv),
+                "z": n(T, sh.Hv, sh.dv), "a": n(T, sh.Hv), "b": n(T, sh.Hv)}
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)       # creates the underlying HIP event
+        return evs
+
+    # ---------------- prefill, 1 x 4096 (headline) ----------------
+    case = synth.prefill_4k_case(1)
+    T = case.T
+    layer = layer_from(case.params)
+    x = {k: bf16_dev(v) for k, v in case.inputs.items()}
+    cu = torch.from_numpy(case.cu_seqlens).to(dev)
+    out = torch.empty((T, sh.Hv, sh.dv), dtype=torch.float32, device=dev)
+    fs = torch.empty((1, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+    cs = torch.empty((1, 3, sh.Cc), dtype=torch.bfloat16, device=dev)
+    nb = gdn.prefill_workspace_bytes(layer, 1, T)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=None, events=None):
+        gdn.prefill_raw(lay, N=NN, T_total=TT, cu_seqlens=cuu, q=xx["q"], k=xx["k"],
+                        v=xx["v"], z=xx["z"], a=xx["a"], b=xx["b"], out=oo,
+                        initial_state=S0, final_state=ff, conv_state_out=cc,
+                        workspace=ws, events=events)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        prefill_step(layer, x, cu, 1, T, out, fs, cs)
+    torch.cuda.synchronize()
+    evs = [new_events(5) for _ in range(K)]
+    e0, e1 = new_events(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        prefill_step(layer, x, cu, 1, T, out, fs, cs, events=evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / K
+    kern_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
+               for j, name in enumerate(gdn.PREFILL_KERNELS)}
+    tok_s = T / (ms_step * 1e-3)
+    log(f"prefill 4k: {ms_step:.3f} ms/step ({wall / K * 1e3:.3f} wall) {tok_s:.4g} tok/s "
+        f"kernels {kern_ms}")
+
+    scan_f, prep_f = prefill_flops_per_token(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.chunk)
+    epi_bytes = sh.Hv * sh.dv * (4 + 2 + 4)
+    rl = {}
+    for name, ms in kern_ms.items():
+        if name == "scan":
+            a = scan_f * T / (ms * 1e-3) / 1e12
+            rl[name] = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        elif name == "prep":
+            a = prep_f * T / (ms * 1e-3) / 1e12
+            rl[name] = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        elif name == "epi":
+            a = epi_bytes * T / (ms * 1e-3) / 1e9
+            rl[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    dominant = max(("prep", "scan", "epi"), key=lambda n: kern_ms[n])
+    roof = dict(rl[dominant])
+    roof["kernel"] = dominant
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["avg_ms"] = kern_ms[dominant]
+    del out, fs, cs, x
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": "GDN prefill tokens/s (MFMA % peak) + decode state GB/s (% HBM peak), 1 GPU",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gdn_prefill 1x4096 tokens, Hk=16 Hv=32 dk=dv=128, chunk 64, "
+                               "bf16 inputs, fp32 state from zero, fp32 out",
+                   "N": 1, "T": T, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk, "dv": sh.dv,
+                   "chunk": sh.chunk, "parallelism": "single GPU"},
+        "roofline": roof,
+        "prefill_kernels_ms": kern_ms,
+        "prefill_kernel_roofline": {k: dict(v, frac=v["achieved"] / v["peak"]) for k, v in rl.items()},
+        "prefill_alg_tflops": (scan_f + prep_f) * T / (ms_step * 1e-3) / 1e12,
+    }
+
+    # ---------------- decode, 30 layers x B ----------------
+    if not args.no_decode:
+        L = args.layers
+        Bmax = max(int(b) for b in args.decode_batches.split(","))
+        gen = torch.Generator(device=dev)
+        layers, states, convs, toks = [], [], [], []
+        Tpre = 2048
+        for l in range(L):
+            lay = layer_from(synth.layer_params(sh, 100 + l))
+            gen.manual_seed(1000 + l)
+            xp = gpu_inputs(Bmax * Tpre, gen)
+            cup = torch.arange(0, Bmax * Tpre + 1, Tpre, dtype=torch.int32, device=dev)
+            st = torch.empty((Bmax, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+            cv = torch.empty((Bmax, 3, sh.Cc), dtype=torch.bfloat16, device=dev)
+            nbp = gdn.prefill_workspace_bytes(lay, Bmax, Bmax * Tpre)
+            if ws.numel() < nbp:
+                ws = torch.empty(nbp, dtype=torch.uint8, device=dev)
+            outp = torch.empty((Bmax * Tpre, sh.Hv, sh.dv), dtype=torch.float32, device=dev)
+            # the carried state is the one a 2048-token prefill leaves behind
+            prefill_step(lay, xp, cup, Bmax, Bmax * Tpre, outp, st, cv)
+            torch.cuda.synchronize()
+            del xp, outp
+            layers.append(lay)
+            states.append(st)
+            convs.append(cv)
+            toks.append(gpu_inputs(Bmax, gen))
+        log(f"decode setup: {L} layers x B={Bmax} states from a {Tpre}-token prefill")
+        dec = {}
+        per_seq, state_per_seq = decode_bytes_per_seq(sh.Hk, sh.Hv, sh.dk, sh.dv)
+        for B in [int(b) for b in args.decode_batches.split(",")]:
+            outs = [torch.empty((B, sh.Hv, sh.dv), dtype=torch.float32, device=dev) for _ in range(L)]
+
+            def dstep(events=None):
+                for l in range(L):
+                    t = toks[l]
+                    if events is not None:
+                        events[l][0].record(stream)
+                    gdn.decode_raw(layers[l], B=B, q=t["q"][:B], k=t["k"][:B], v=t["v"][:B],
+                                   z=t["z"][:B], a=t["a"][:B], b=t["b"][:B], out=outs[l],
+                                   state_in=states[l][:B], state_out=states[l][:B],
+                                   conv_state_in=convs[l][:B], conv_state_out=convs[l][:B])
+                    if events is not None:
+                        events[l][1].record(stream)
+            for _ in range(W):
+                dstep()
+            torch.cuda.synchronize()
+            devs = [[new_events(2) for _ in range(L)] for _ in range(K)]
+            d0, d1 = new_events(2)
+            torch.cuda.synchronize()
+            d0.record(stream)
+            for i in range(K):
+                dstep(devs[i])
+            d1.record(stream)
+            torch.cuda.synchronize()
+            ms = d0.elapsed_time(d1) / K
+            kms = sum(devs[i][l][0].elapsed_time(devs[i][l][1]) for i in range(K) for l in range(L)) / (K * L)
+            state_gbs = L * B * state_per_seq / (ms * 1e-3) / 1e9
+            all_gbs = L * B * per_seq / (ms * 1e-3) / 1e9
+            kern_gbs = B * per_seq / (kms * 1e-3) / 1e9
+            dec[f"B{B}"] = {"ms_per_step": ms, "layers": L, "state_GBps": state_gbs,
+                            "all_bytes_GBps": all_gbs, "state_frac_hbm": state_gbs / PEAK_HBM_GBS,
+                            "kernel_avg_ms": kms,
+                            "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
+                                         "traffic": None, "bytes_per_seq_layer": per_seq}}
+            log(f"decode B={B}: {ms:.3f} ms/step, state {state_gbs:.1f} GB/s, "
+                f"kernel {kms * 1e3:.1f} us = {kern_gbs:.1f} GB/s")
+        result["decode"] = dec
+        del layers, states, convs, toks
+        torch.cuda.empty_cache()
+
+    # ---------------- long prefill, 1 x 131072 from a random state ----------------
+    def timed_prefill(name, lengths, seed, reps):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        TT = int(sum(lengths))
+        NN = len(lengths)
+        lay = layer_from(synth.layer_params(sh, seed))
+        xx = gpu_inputs(TT, gen)
+        cuu = torch.from_numpy(synth.cu_from_lengths(lengths)).to(dev)
+        S0 = (torch.randn((NN, sh.Hv, sh.dk, sh.dv), generator=gen, device=dev) * math.sqrt(0.02))
+        oo = torch.empty((TT, sh.Hv, sh.dv), dtype=torch.float32, device=dev)
+        ff = torch.empty_like(S0)
+        cc = torch.empty((NN, 3, sh.Cc), dtype=torch.bfloat16, device=dev)
+        nonlocal_ws = gdn.prefill_workspace_bytes(lay, NN, TT)
+        nonlocal ws
+        if ws.numel() < nonlocal_ws:
+            ws = torch.empty(nonlocal_ws, dtype=torch.uint8, device=dev)
+        prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0)
+        torch.cuda.synchronize()
+        ev = [new_events(5) for _ in range(reps)]
+        a0, a1 = new_events(2)
+        a0.record(stream)
+        for i in range(reps):
+            prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0, events=ev[i])
+        a1.record(stream)
+        torch.cuda.synchronize()
+        ms = a0.elapsed_time(a1) / reps
+        km = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(reps)) / reps
+              for j, n in enumerate(gdn.PREFILL_KERNELS)}
+        alg = (scan_f + prep_f) * TT / (ms * 1e-3) / 1e12
+        r = {"N": NN, "T": TT, "ms": ms, "tokens_per_s": TT / (ms * 1e-3), "kernels_ms": km,
+             "alg_tflops": alg, "alg_mfma_frac": alg / PEAK_BF16_TFLOPS,
+             "scan_tflops": scan_f * TT / (km["scan"] * 1e-3) / 1e12}
+        log(f"{name}: {ms:.3f} ms, {r['tokens_per_s']:.4g} tok/s, kernels {km}")
+        del xx, oo, ff, cc, S0
+        torch.cuda.empty_cache()
+        return r
+
+    if not args.no_long:
+        result["long_prefill"] = timed_prefill("long prefill 1x131072", [131072], 3, 3)
+    if not args.no_varlen:
+        lens = [int(v) for v in synth.varlen_lengths(8, 4)]
+        r = timed_prefill("varlen prefill 8 seqs", lens, 4, 3)
+        r["lengths"] = lens
+        result["varlen_prefill"] = r
+
+    # ---------------- CPU baseline: the fp64 oracle on the host ----------------
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = min(os.cpu_count() or 1, 16)
+        d = oracle.Dims(sh.Hk, sh.Hv, sh.dk, sh.dv, 4, sh.scale, sh.eps_l2, sh.eps_rms)
+        reps, t_cpu = 0, 0.0
+        while t_cpu < 10.0 and reps < 20:
+            tc = time.perf_counter()
+            oracle.gdn_forward(d, case.cu_seqlens, *(case.inputs[n] for n in "qkvzab"),
+                               case.params["conv_w"], case.params["A_log"],
+                               case.params["dt_bias"], case.params["norm_w"], nthreads=cores)
+            t_cpu += time.perf_counter() - tc
+            reps += 1
+        result["cpu_baseline"] = {"value": T * reps / t_cpu, "unit": "tokens/s", "cores": cores,
+                                  "kind": "oracle",
+                                  "sample": f"the whole 1x{T}-token workload, all 32 heads, "
+                                            f"fp64 token-by-token, {reps} runs ({t_cpu:.1f} s)"}
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tok/s on {cores} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

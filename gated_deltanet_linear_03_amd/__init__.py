@@ -30,8 +30,9 @@ GDN_DTYPE_FP32 = 0
 GDN_DTYPE_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
-           "gdn_decode", "gdn_status_string", "gdn_last_error",
-           "gdn_selftest_mfma")
+           "gdn_prefill_timed", "gdn_decode", "gdn_status_string",
+           "gdn_last_error", "gdn_selftest_mfma")
+PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
 
 
 class GdnError(RuntimeError):
@@ -98,6 +99,10 @@ def lib():
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_prefill_timed.restype = ctypes.c_int
+        L.gdn_prefill_timed.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         L.gdn_decode.restype = ctypes.c_int
         L.gdn_decode.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CDecodeIO),
                                  ctypes.c_void_p]
@@ -174,8 +179,11 @@ def prefill_workspace_bytes(layer: Layer, N: int, T_total: int) -> int:
 def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
                 out, core_out=None, initial_state=None, final_state=None,
                 conv_state_in=None, conv_state_out=None, workspace=None,
-                workspace_bytes=None, stream=None):
-    """Call ``gdn_prefill`` on caller-provided buffers (no allocation)."""
+                workspace_bytes=None, stream=None, events=None):
+    """Call ``gdn_prefill`` on caller-provided buffers (no allocation).
+    events: optional list of 5 recorded torch.cuda.Event(enable_timing=True)
+    objects; the call then goes through ``gdn_prefill_timed`` and the event
+    pairs bracket the plan, prep, scan and epi kernels."""
     cl = layer.c()
     io = CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
                     _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
@@ -185,8 +193,14 @@ def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
                     _ptr(conv_state_out), _ptr(out), _ptr(core_out))
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().gdn_prefill(ctypes.byref(cl), ctypes.byref(io), _ptr(workspace),
-                             int(workspace_bytes), _stream(stream)))
+    if events is None:
+        _check(lib().gdn_prefill(ctypes.byref(cl), ctypes.byref(io), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream)))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        _check(lib().gdn_prefill_timed(ctypes.byref(cl), ctypes.byref(io), _ptr(workspace),
+                                       int(workspace_bytes), _stream(stream), arr,
+                                       len(events)))
 
 
 def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,

@@ -114,8 +114,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_layer* L, int32_t N, int64_t T) {
     return static_cast<size_t>(ws_layout(L, N, T, true).total);
 }
 
-gdn_status gdn_prefill(const gdn_layer* L, const gdn_prefill_io* io, void* ws, size_t ws_bytes,
-                       void* stream) {
+static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, void* ws,
+                               size_t ws_bytes, void* stream, hipEvent_t const* events) {
     g_err[0] = 0;
     gdn_status st = check_layer(L, true);
     if (st != GDN_OK) return st;
@@ -193,10 +193,25 @@ gdn_status gdn_prefill(const gdn_layer* L, const gdn_prefill_io* io, void* ws, s
 
     bool supported = false;
     hipError_t e = gdn::launch_prefill(dk, dv, L->chunk, L->act_dtype == GDN_DTYPE_BF16, p,
-                                       static_cast<hipStream_t>(stream), &supported);
+                                       static_cast<hipStream_t>(stream), &supported, events);
     if (!supported) return fail(GDN_ERR_UNSUPPORTED, "prefill shape not compiled");
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
+}
+
+gdn_status gdn_prefill(const gdn_layer* L, const gdn_prefill_io* io, void* ws, size_t ws_bytes,
+                       void* stream) {
+    return prefill_impl(L, io, ws, ws_bytes, stream, nullptr);
+}
+
+gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void* ws,
+                             size_t ws_bytes, void* stream, void* const* events, int n_events) {
+    g_err[0] = 0;
+    if (!events || n_events != GDN_PREFILL_KERNELS + 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "need %d timing events", GDN_PREFILL_KERNELS + 1);
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i]) return fail(GDN_ERR_INVALID_ARGUMENT, "timing event %d is NULL", i);
+    return prefill_impl(L, io, ws, ws_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
 gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream) {

@@ -61,8 +61,9 @@ __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
 
 hipError_t launch_decode(int DK, int DV, bool bf16, const DecodeParams& p, hipStream_t s,
                          bool* supported);
+// events: NULL, or 5 events recorded before each of the 4 kernels and after the last
 hipError_t launch_prefill(int DK, int DV, int C, bool bf16, const PrefillParams& p,
-                          hipStream_t s, bool* supported);
+                          hipStream_t s, bool* supported, hipEvent_t const* events);
 bool prefill_shape_supported(int DK, int DV, int C);
 bool decode_shape_supported(int DK, int DV);
 hipError_t launch_selftest_mfma(const float* A, const float* B, float* C, hipStream_t s);

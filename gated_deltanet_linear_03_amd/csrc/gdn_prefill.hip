@@ -605,23 +605,34 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
 
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int C, int DVS, bool BF16>
-static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
+static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
+                                   hipEvent_t const* ev) {
+    hipError_t e = hipSuccess;
+    auto mark = [&](int i) {
+        if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
+    };
+    mark(0);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.N, C, p.chunk_off);
+    mark(1);
     if (p.max_chunks > 0) {
         hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(p.max_chunks, p.Hk), dim3(256),
                            0, s, p);
     }
+    mark(2);
     const int pairs = p.N * p.Hv;
     if (pairs > 0) {
         const int groups = (pairs + 7) / 8;
         hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
                            dim3(256), 0, s, p);
     }
+    mark(3);
     if (p.T > 0) {
         const int64_t rows = p.T * p.Hv;
         hipLaunchKernelGGL((epi_kernel<DV, BF16>), dim3(static_cast<unsigned>((rows + 3) / 4)),
                            dim3(256), 0, s, p);
     }
+    mark(4);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
@@ -631,12 +642,12 @@ bool prefill_shape_supported(int DK, int DV, int C) {
 }
 
 hipError_t launch_prefill(int DK, int DV, int C, bool bf16, const PrefillParams& p,
-                          hipStream_t s, bool* supported) {
+                          hipStream_t s, bool* supported, hipEvent_t const* events) {
     *supported = true;
 #define GDN_PF(dk, dv, c, dvs)                                                            \
     if (DK == dk && DV == dv && C == c)                                                   \
-        return bf16 ? launch_prefill_t<dk, dv, c, dvs, true>(p, s)                        \
-                    : launch_prefill_t<dk, dv, c, dvs, false>(p, s);
+        return bf16 ? launch_prefill_t<dk, dv, c, dvs, true>(p, s, events)                \
+                    : launch_prefill_t<dk, dv, c, dvs, false>(p, s, events);
     GDN_PF(128, 128, 64, 32)
     GDN_PF(32, 32, 16, 32)
     GDN_PF(32, 64, 16, 32)

@@ -36,9 +36,13 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bf16 (ties to even); returned as fp32
     arrays whose values are exactly representable in bf16."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                                  # wraps only for NaN payloads
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 @dataclass
@@ -90,17 +94,35 @@ def layer_params(shape: LayerShape, seed: int, norm_w_jitter: bool = False,
             "norm_w": norm_w}
 
 
+TOKEN_BLOCK = 4096
+
+
 def token_inputs(shape: LayerShape, T: int, seed: int):
     """q, k [T, Hk, dk]; v, z [T, Hv, dv]; a, b [T, Hv] in the activation
-    dtype's values (held as fp32 arrays)."""
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2])))
-    out = {}
-    out["q"] = _act(_normal(rng, (T, shape.Hk, shape.dk)), shape)
-    out["k"] = _act(_normal(rng, (T, shape.Hk, shape.dk)), shape)
-    out["v"] = _act(_normal(rng, (T, shape.Hv, shape.dv)), shape)
-    out["z"] = _act(_normal(rng, (T, shape.Hv, shape.dv)), shape)
-    out["a"] = _act(_normal(rng, (T, shape.Hv)), shape)
-    out["b"] = _act(_normal(rng, (T, shape.Hv)), shape)
+    dtype's values (held as fp32 arrays).  Each tensor is drawn in blocks of
+    TOKEN_BLOCK tokens, block j of tensor i from its own stream
+    SeedSequence([seed, 2, i, j]), so values do not depend on how many
+    threads fill them."""
+    import concurrent.futures as cf
+    import os
+    inner = {"q": (shape.Hk, shape.dk), "k": (shape.Hk, shape.dk),
+             "v": (shape.Hv, shape.dv), "z": (shape.Hv, shape.dv),
+             "a": (shape.Hv,), "b": (shape.Hv,)}
+    out = {n: np.empty((T,) + s, dtype=np.float32) for n, s in inner.items()}
+    jobs = [(i, n, j) for i, n in enumerate(inner) for j in range(0, T, TOKEN_BLOCK)]
+
+    def fill(job):
+        i, n, j = job
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2, i, j // TOKEN_BLOCK])))
+        t1 = min(T, j + TOKEN_BLOCK)
+        out[n][j:t1] = _act(_normal(rng, (t1 - j,) + inner[n]), shape)
+
+    if len(jobs) > 8:
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for job in jobs:
+            fill(job)
     return out
 
 

@@ -142,6 +142,20 @@ size_t gdn_prefill_workspace_bytes(const gdn_layer* layer, int32_t N,
 gdn_status gdn_prefill(const gdn_layer* layer, const gdn_prefill_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Number of kernels gdn_prefill enqueues, in order: plan (chunk table),
+ * prep (chunk-parallel operands), scan (sequential state passing), epi
+ * (gated RMSNorm). */
+#define GDN_PREFILL_KERNELS 4
+
+/* gdn_prefill that also records caller-created timing events (hipEvent_t
+ * handles) on `stream`: events[i] just before kernel i and
+ * events[GDN_PREFILL_KERNELS] after the last, so event pairs bracket each
+ * kernel.  n_events must be GDN_PREFILL_KERNELS + 1.  Same results as
+ * gdn_prefill; meant for per-kernel timing. */
+gdn_status gdn_prefill_timed(const gdn_layer* layer, const gdn_prefill_io* io,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events, int n_events);
+
 /* Enqueue one decode step (no workspace needed). */
 gdn_status gdn_decode(const gdn_layer* layer, const gdn_decode_io* io,
                       void* stream);

@@ -43,20 +43,11 @@ def test_status_strings():
 FAKE = 0x1000  # never dereferenced: validation fails before any device use
 
 
-def _layer(**kw):
-    base = dict(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=None, A_log=None,
-                dt_bias=None, norm_w=None)
-    base.update(kw)
-    L = gdn.Layer(**base)
-    cl = L.c()
-    for f in ("conv_w", "A_log", "dt_bias", "norm_w"):
-        if getattr(cl, f) is None and kw.get(f, "x") is None:
-            continue
-    return cl
-
-
 def _full_layer(**kw):
-    cl = _layer(**kw)
+    """A CLayer at the 16/32-head, 128/128, chunk-64 shape with fake (never
+    dereferenced) parameter pointers; keyword arguments override fields."""
+    cl = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=None, A_log=None,
+                   dt_bias=None, norm_w=None).c()
     cl.conv_w = cl.A_log = cl.dt_bias = cl.norm_w = FAKE
     for k_, v_ in kw.items():
         setattr(cl, k_, v_)
@@ -156,3 +147,59 @@ def test_decode_zero_batch_is_a_no_op():
 def test_decode_unsupported_shape():
     st = gdn.lib().gdn_decode(ctypes.byref(_full_layer(dk=48)), ctypes.byref(_dio()), None)
     assert st == gdn.GDN_ERR_UNSUPPORTED
+
+
+class _FakeTensor:
+    """Stands in for a device tensor: only data_ptr/stride/numel are read."""
+    def __init__(self, ptr, stride0=0, numel=0, esize=1):
+        self._p, self._s, self._n, self._e = ptr, stride0, numel, esize
+
+    def data_ptr(self):
+        return self._p
+
+    def stride(self, i):
+        return self._s
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+
+class _FakeStream:
+    cuda_stream = 0
+
+
+class _FakeEvent:
+    cuda_event = 0
+
+
+def test_binding_marshals_to_the_abi_and_raises():
+    """The Python wrappers reach the C ABI and turn its status into GdnError
+    (validation fails on the host before anything touches a device)."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    t = _FakeTensor(FAKE, 16 * 128)
+    kw = dict(N=1, T_total=64, cu_seqlens=_FakeTensor(FAKE), q=t, k=t,
+              v=_FakeTensor(FAKE, 32 * 128), z=_FakeTensor(FAKE, 32 * 128),
+              a=_FakeTensor(FAKE, 32), b=_FakeTensor(FAKE, 32), out=_FakeTensor(FAKE),
+              stream=_FakeStream())
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.prefill_raw(lay, workspace=None, **kw)
+    assert ei.value.status == gdn.GDN_ERR_WORKSPACE
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16), events=[_FakeEvent()] * 5, **kw)
+    assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT      # NULL event handles
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16), events=[_FakeEvent()] * 3, **kw)
+    assert b"timing events" in gdn.lib().gdn_last_error()
+    with pytest.raises(gdn.GdnError):
+        gdn.decode_raw(lay, B=2, q=t, k=t, v=_FakeTensor(FAKE, 32 * 128),
+                       z=_FakeTensor(FAKE, 32 * 128), a=_FakeTensor(FAKE, 32),
+                       b=_FakeTensor(FAKE, 32), out=_FakeTensor(FAKE + 4),
+                       state_in=None, state_out=_FakeTensor(FAKE),
+                       conv_state_in=None, conv_state_out=_FakeTensor(FAKE),
+                       stream=_FakeStream())
+    assert gdn.prefill_workspace_bytes(lay, 1, 4096) > 0

@@ -1,0 +1,251 @@
+"""GPU parity at the full workload sizes, batch invariance, determinism,
+carried-state semantics and the binding's in-place / strided forms.
+
+Full-size cases compare every output of a subset of key heads (with their
+value heads) against the fp64 oracle run on the whole sequence for those
+heads: heads are independent, so a head subset is an exact sample."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_linear_03_amd as gdn
+import oracle
+from gated_deltanet_linear_03_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import (TOL, act_dtype, check_prefill, dims, gpu_prefill,  # noqa: E402
+                         make_layer, oracle_prefill, per_seq_errors, rel_err,
+                         state_errors, to_dev)
+
+
+def _bits_equal(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def test_prefill_long_131072_head_sample():
+    """1 x 131072 tokens resuming from a N(0, 0.02) state (zero conv state);
+    key heads 0 and 11 (value heads 0, 1, 22, 23) against the oracle."""
+    case = synth.long_case(3)
+    res = gpu_prefill(case, want_core=True)
+    heads = [0, 11]
+    ref = oracle_prefill(case, heads_of_key=heads, nthreads=4)
+    check_prefill(case, res, ref, heads=ref["heads"], label="long")
+
+
+def test_prefill_varlen_parity_and_batch_invariance():
+    """8 packed sequences (log-uniform lengths in [512, 32768]) with random
+    initial states: oracle parity on a head sample, and every sequence's
+    outputs bit-identical to the same sequence run alone and to a permuted
+    packing."""
+    case = synth.varlen_case(4)
+    packed = gpu_prefill(case, want_core=True)
+    ref = oracle_prefill(case, heads_of_key=[5], nthreads=8)
+    check_prefill(case, packed, ref, heads=ref["heads"], label="varlen")
+    cu = case.cu_seqlens
+    N = case.N
+    lens = np.diff(cu)
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        alone = synth.PrefillCase(case.shape, np.array([0, b - a], dtype=np.int32),
+                                  {k: v[a:b] for k, v in case.inputs.items()}, case.params,
+                                  case.initial_state[n:n + 1], None)
+        r = gpu_prefill(alone, want_core=True)
+        assert _bits_equal(r["out"], packed["out"][a:b]), n
+        assert _bits_equal(r["core_out"], packed["core_out"][a:b]), n
+        assert _bits_equal(r["final_state"][0], packed["final_state"][n]), n
+        assert _bits_equal(r["conv_state_out"][0], packed["conv_state_out"][n]), n
+    perm = [3, 0, 7, 5, 1, 6, 2, 4]
+    order = np.concatenate([np.arange(cu[p], cu[p + 1]) for p in perm])
+    pcase = synth.PrefillCase(case.shape, synth.cu_from_lengths(lens[perm]),
+                              {k: v[order] for k, v in case.inputs.items()}, case.params,
+                              case.initial_state[perm], None)
+    pr = gpu_prefill(pcase, want_core=True)
+    pcu = pcase.cu_seqlens
+    for i, p in enumerate(perm):
+        assert _bits_equal(pr["out"][pcu[i]:pcu[i + 1]], packed["out"][cu[p]:cu[p + 1]])
+        assert _bits_equal(pr["final_state"][i], packed["final_state"][p])
+
+
+def test_prefill_deterministic_and_writes_every_output():
+    """Two runs on NaN-poisoned outputs give identical bits and no NaN."""
+    case = synth.prefill_case(synth.FULL, [333, 64, 5], seed=31, with_state=True,
+                              with_conv_state=True)
+    sh = case.shape
+    ad = act_dtype(sh)
+    layer = make_layer(sh, case.params)
+    x = {k: to_dev(v, ad) for k, v in case.inputs.items()}
+    cu = to_dev(case.cu_seqlens)
+    S0, C0 = to_dev(case.initial_state), to_dev(case.conv_state, ad)
+    outs = []
+    for _ in range(2):
+        T, N = case.T, case.N
+        out = torch.full((T, sh.Hv, sh.dv), float("nan"), device="cuda")
+        core = torch.full((T, sh.Hv, sh.dv), float("nan"), device="cuda")
+        fs = torch.full((N, sh.Hv, sh.dk, sh.dv), float("nan"), device="cuda")
+        cs = torch.full((N, 3, sh.Cc), float("nan"), device="cuda", dtype=ad)
+        nb = gdn.prefill_workspace_bytes(layer, N, T)
+        ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+        gdn.prefill_raw(layer, N=N, T_total=T, cu_seqlens=cu, q=x["q"], k=x["k"], v=x["v"],
+                        z=x["z"], a=x["a"], b=x["b"], out=out, core_out=core,
+                        initial_state=S0, final_state=fs, conv_state_in=C0,
+                        conv_state_out=cs, workspace=ws)
+        torch.cuda.synchronize()
+        for t in (out, core, fs, cs):
+            assert not torch.isnan(t.float()).any()
+        outs.append((out, core, fs, cs))
+    for a, b in zip(*outs):
+        assert _bits_equal(a, b)
+
+
+def test_prefill_in_place_states_and_split_resume():
+    """final_state aliasing initial_state and conv_state_out aliasing
+    conv_state_in; prefill(x[0:T1]) then prefill(x[T1:]) from the carried
+    states matches one prefill of x within the bar, and the oracle."""
+    sh = synth.FULL
+    T, T1 = 300, 131
+    case = synth.prefill_case(sh, [T], seed=41, with_state=True, with_conv_state=True)
+    ad = act_dtype(sh)
+    layer = make_layer(sh, case.params)
+    x = {k: to_dev(v, ad) for k, v in case.inputs.items()}
+    st = to_dev(case.initial_state)
+    cs = to_dev(case.conv_state, ad)
+    outs = []
+    for lo, hi in ((0, T1), (T1, T)):
+        xs = {k: v[lo:hi] for k, v in x.items()}
+        r = gdn.prefill(layer, xs["q"], xs["k"], xs["v"], xs["z"], xs["a"], xs["b"],
+                        to_dev(np.array([0, hi - lo], dtype=np.int32)), initial_state=st,
+                        conv_state_in=cs, in_place=True)
+        assert r["final_state"].data_ptr() == st.data_ptr()
+        assert r["conv_state_out"].data_ptr() == cs.data_ptr()
+        outs.append(r["out"])
+    torch.cuda.synchronize()
+    ref = oracle_prefill(case)
+    got = torch.cat(outs).cpu().numpy()
+    e = per_seq_errors(case.cu_seqlens, got, ref["out"])
+    es = state_errors(st.cpu().numpy(), ref["final_state"])
+    print(f"split-resume out {e:.3e} state {es:.3e}")
+    assert e < TOL and es < TOL
+    assert np.array_equal(cs.float().cpu().numpy(), ref["conv_state_out"])
+
+
+def test_prefill_strided_projection_views():
+    """q, k, v, z, a, b as column views of one packed projection output
+    (token stride = the packed row) give the same bits as dense copies."""
+    sh = synth.FULL
+    case = synth.prefill_case(sh, [150, 77], seed=51, with_state=True)
+    ad = act_dtype(sh)
+    widths = [sh.Hk * sh.dk, sh.Hk * sh.dk, sh.Hv * sh.dv, sh.Hv * sh.dv, sh.Hv, sh.Hv]
+    pad = 8
+    row = sum(widths) + pad
+    T = case.T
+    big = torch.zeros((T, row), dtype=ad, device="cuda")
+    views = {}
+    off = 0
+    for name, w in zip("qkvzab", widths):
+        big[:, off:off + w] = to_dev(case.inputs[name].reshape(T, -1), ad)
+        v = big[:, off:off + w]
+        if name in "qk":
+            v = v.unflatten(1, (sh.Hk, sh.dk))
+        elif name in "vz":
+            v = v.unflatten(1, (sh.Hv, sh.dv))
+        views[name] = v
+        off += w
+    layer = make_layer(sh, case.params)
+    cu = to_dev(case.cu_seqlens)
+    S0 = to_dev(case.initial_state)
+    r1 = gdn.prefill(layer, *(views[n] for n in "qkvzab"), cu, initial_state=S0)
+    dense = {k: to_dev(v, ad) for k, v in case.inputs.items()}
+    r2 = gdn.prefill(layer, *(dense[n] for n in "qkvzab"), cu, initial_state=S0)
+    torch.cuda.synchronize()
+    assert _bits_equal(r1["out"], r2["out"])
+    assert _bits_equal(r1["final_state"], r2["final_state"])
+
+
+# ---------------------------- decode ------------------------------------------
+
+def _decode(layer, t, st, cs, B=None, want_core=False):
+    B = B or t["q"].shape[0]
+    return gdn.decode(layer, t["q"][:B], t["k"][:B], t["v"][:B], t["z"][:B], t["a"][:B],
+                      t["b"][:B], st, cs, in_place=False, want_core=want_core)
+
+
+def test_decode_batch_invariance():
+    """A sequence's decode step is bit-identical at B = 1, 3 and 64 and at
+    any position in the batch."""
+    sh = synth.FULL
+    params = synth.layer_params(sh, 61)
+    layer = make_layer(sh, params)
+    ad = act_dtype(sh)
+    B = 64
+    t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, B, 62).items()}
+    st = to_dev(synth.initial_states(sh, B, 63))
+    cs = to_dev(synth.conv_states(sh, B, 64), ad)
+    full = _decode(layer, t, st, cs)
+    for sel in ([0], [5, 17, 63], [63, 0, 40]):
+        idx = torch.tensor(sel, device="cuda")
+        sub = {k: v[idx] for k, v in t.items()}
+        r = _decode(layer, sub, st[idx], cs[idx])
+        torch.cuda.synchronize()
+        for j, b in enumerate(sel):
+            assert _bits_equal(r["out"][j], full["out"][b])
+            assert _bits_equal(r["final_state"][j], full["final_state"][b])
+            assert _bits_equal(r["conv_state_out"][j], full["conv_state_out"][b])
+
+
+def test_decode_chain_matches_prefill_and_oracle():
+    """T single-token decode steps from carried states equal one prefill of
+    the same T tokens within the bar (they reassociate differently, so only
+    within tolerance), and both match the oracle."""
+    sh = synth.FULL
+    T = 40
+    case = synth.prefill_case(sh, [T], seed=71, with_state=True, with_conv_state=True)
+    ad = act_dtype(sh)
+    layer = make_layer(sh, case.params)
+    st = to_dev(case.initial_state)
+    cs = to_dev(case.conv_state, ad)
+    x = {k: to_dev(v, ad) for k, v in case.inputs.items()}
+    outs = []
+    for t in range(T):
+        r = gdn.decode(layer, *(x[n][t:t + 1] for n in "qkvzab"), st, cs, in_place=True)
+        outs.append(r["out"])
+    torch.cuda.synchronize()
+    dec_out = torch.cat(outs).cpu().numpy()
+    ref = oracle_prefill(case)
+    e = rel_err(dec_out, ref["out"])
+    es = rel_err(st.cpu().numpy(), ref["final_state"])
+    pf = gpu_prefill(case)
+    ep = rel_err(dec_out, pf["out"].cpu().numpy())
+    print(f"decode chain vs oracle out {e:.3e} state {es:.3e}; vs prefill {ep:.3e}")
+    assert e < TOL and es < TOL and ep < TOL
+    assert np.array_equal(cs.float().cpu().numpy(), ref["conv_state_out"])
+
+
+def test_decode_state_from_oracle_prefill():
+    """Decode against the state a short prefill leaves behind (computed by
+    the oracle), B = 3, with bf16 output equal to rounded fp32 output."""
+    sh = synth.FULL
+    B, Tp = 3, 96
+    case = synth.prefill_case(sh, [Tp] * B, seed=81)
+    pre = oracle_prefill(case)
+    params = case.params
+    ad = act_dtype(sh)
+    xd = synth.token_inputs(sh, B, 82)
+    S0 = pre["final_state"].astype(np.float32)
+    C0 = pre["conv_state_out"].astype(np.float32)
+    ref = oracle.gdn_forward(dims(sh), np.arange(B + 1), *(xd[n] for n in "qkvzab"),
+                             params["conv_w"], params["A_log"], params["dt_bias"],
+                             params["norm_w"], S0, C0)
+    t = {k: to_dev(v, ad) for k, v in xd.items()}
+    layer = make_layer(sh, params)
+    r = _decode(layer, t, to_dev(S0), to_dev(C0, ad), want_core=True)
+    lay16 = make_layer(sh, params, out_dtype=gdn.GDN_DTYPE_BF16)
+    r16 = _decode(lay16, t, to_dev(S0), to_dev(C0, ad))
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert rel_err(r["out"][b].cpu().numpy(), ref["out"][b]) < TOL
+        assert rel_err(r["final_state"][b].cpu().numpy(), ref["final_state"][b]) < TOL
+    assert torch.equal(r["out"].to(torch.bfloat16), r16["out"])
+    assert np.array_equal(r["conv_state_out"].float().cpu().numpy(), ref["conv_state_out"])
