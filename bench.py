@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (3 times): "
+                         "the reference for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -93,6 +96,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mb:
+        nbytes = args.calib_copy_mb << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": nbytes, "copies": 3}), flush=True)
+        return
     sh = synth.FULL
 
     def layer_from(params):

@@ -50,6 +50,9 @@ gdn_status check_layer(const gdn_layer* L, bool prefill) {
         return fail(GDN_ERR_INVALID_ARGUMENT, "epsilons must be >= 0");
     if (!L->conv_w || !L->A_log || !L->dt_bias || !L->norm_w)
         return fail(GDN_ERR_INVALID_ARGUMENT, "layer parameter pointer is NULL");
+    if (!aligned(L->conv_w, 16) || !aligned(L->A_log, 4) || !aligned(L->dt_bias, 4) ||
+        !aligned(L->norm_w, 4))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "conv_w must be 16-byte aligned, other parameters 4-byte");
     if (prefill) {
         if (L->chunk <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "chunk must be positive");
         if (!gdn::prefill_shape_supported(L->dk, L->dv, L->chunk))

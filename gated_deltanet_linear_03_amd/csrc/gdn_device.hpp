@@ -32,17 +32,22 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Split x into hi + lo, both bf16 bit patterns.
+// Split x into hi + lo, both bf16 bit patterns: hi = bf16(x), lo = bf16(x - hi)
+// (x - hi is exact in fp32).
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
     hi = f32_to_bf16_bits(x);
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// e^x for x <= 0 through the hardware 2^x (v_exp_f32); relative error about
+// |x| * 2^-24 + 2 ulp, used for in-chunk decay factors only.
+__device__ __forceinline__ float exp_neg(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
 template <bool BF16>
@@ -74,6 +79,10 @@ __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
 }
 
 // acc += (a_hi + a_lo) * (b_hi + b_lo) without the lo*lo term.

@@ -17,10 +17,11 @@
 // Kernels, in stream order:
 //   plan_kernel   first chunk index of every sequence (chunks restart at each
 //                 sequence start, so results do not depend on the packing)
-//   prep_kernel   chunk-parallel over (chunk, key head): conv1d+SiLU, L2 norms,
-//                 gates, Gram matrices, triangular solve, and the per-chunk
-//                 operands -W, Q_G = diag(e^gamma) Q, K_d^T, P, U~ written in
-//                 matrix-core fragment order (split bf16 hi/lo)
+//   prep_kernel   chunk-parallel over (chunk, value head): conv1d+SiLU, L2
+//                 norms, gates, Gram matrices, triangular inverse and the
+//                 per-chunk operands -W, Q_G = diag(e^gamma) Q, K_d^T, P, U~
+//                 written in matrix-core fragment order (split bf16 hi/lo);
+//                 see gdn_prep.hpp
 //   scan_kernel   sequential over the chunks of one (sequence, value head,
 //                 dv slice): U, O and H' on split-bf16 matrix-core products,
 //                 H kept in fp32 accumulators for the whole sequence; also
@@ -85,244 +86,11 @@ struct VchLayout {
     static_assert(bytes == vch_bytes(DK, DV, C), "layout");
 };
 
-// Raw input of channel c at token position pos of the sequence starting at
-// `start`; earlier positions read the conv state row (K-1) + (pos - start).
-template <bool BF16>
-__device__ __forceinline__ float raw_in(const PrefillParams& p, int n, int64_t start,
-                                        int64_t pos, int c, int Cc, int qk) {
-    using A = Act<BF16>;
-    using T = typename A::T;
-    if (pos < start) {
-        const int64_t r = 3 + (pos - start);
-        if (r < 0 || !p.conv_in) return 0.f;
-        return A::load(static_cast<const T*>(p.conv_in) + (static_cast<int64_t>(n) * 3 + r) * Cc + c);
-    }
-    if (c < qk) return A::load(static_cast<const T*>(p.q) + pos * p.qs + c);
-    if (c < 2 * qk) return A::load(static_cast<const T*>(p.k) + pos * p.ks + (c - qk));
-    return A::load(static_cast<const T*>(p.v) + pos * p.vs + (c - 2 * qk));
-}
+}  // namespace gdn
 
-template <bool BF16>
-__device__ __forceinline__ float conv_silu_at(const PrefillParams& p, int n, int64_t start,
-                                              int64_t pos, int c, int Cc, int qk) {
-    const float* w = p.conv_w + static_cast<size_t>(c) * 4;
-    float acc = w[0] * raw_in<BF16>(p, n, start, pos - 3, c, Cc, qk);
-    acc = fmaf(w[1], raw_in<BF16>(p, n, start, pos - 2, c, Cc, qk), acc);
-    acc = fmaf(w[2], raw_in<BF16>(p, n, start, pos - 1, c, Cc, qk), acc);
-    acc = fmaf(w[3], raw_in<BF16>(p, n, start, pos, c, Cc, qk), acc);
-    return silu(acc);
-}
+#include "gdn_prep.hpp"
 
-// Store 8 fp32 values as one A-fragment slot (hi and lo bf16 halves).
-__device__ __forceinline__ void store_afrag(uint8_t* tile, int lane, const float* x8) {
-    uint16_t hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(x8[e], hi[e], lo[e]);
-    *reinterpret_cast<u32x4*>(tile + lane * 16) = pack8(hi);
-    *reinterpret_cast<u32x4*>(tile + 1024 + lane * 16) = pack8(lo);
-}
-
-// ---------------------------------------------------------------------------
-// prep: one work-group per (chunk slot, key head).
-// ---------------------------------------------------------------------------
-template <int DK, int DV, int C, bool BF16>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
-    using L = VchLayout<DK, DV, C>;
-    constexpr int CK = L::CK;
-    constexpr int NT = 256;
-    constexpr int SD = DK + 4, SV = DV + 4, SC = C + 1;
-    __shared__ float sQ[C * SD], sK[C * SD], sV[C * SV];
-    __shared__ float sGkk[C * SC], sGqk[C * SC], sT[C * SC];
-    __shared__ float sg[C], sbeta[C], sgam[C], cW[C], cU[C], eG[C], eD[C], sacc[C];
-
-    const int slot = blockIdx.x;
-    const int hk = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int total = p.chunk_off[p.N];
-    if (slot >= total) return;
-    const int n = seq_of_chunk(p.chunk_off, p.N, slot);
-    const int64_t start = p.cu[n], end = p.cu[n + 1];
-    const int64_t t0 = start + static_cast<int64_t>(slot - p.chunk_off[n]) * C;
-    const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
-    const int qk = p.Hk * DK;
-    const int Cc = 2 * qk + p.Hv * DV;
-
-    // 1. conv + SiLU of q and k; padding rows are zero.
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        float yq = 0.f, yk = 0.f;
-        if (r < Lc) {
-            yq = conv_silu_at<BF16>(p, n, start, t0 + r, hk * DK + i, Cc, qk);
-            yk = conv_silu_at<BF16>(p, n, start, t0 + r, qk + hk * DK + i, Cc, qk);
-        }
-        sQ[r * SD + i] = yq;
-        sK[r * SD + i] = yk;
-    }
-    __syncthreads();
-    // 2. L2 norms per token (one wave per token).
-    for (int r = wave; r < C; r += NT / kWave) {
-        float sq = 0.f, sk = 0.f;
-        for (int i = lane; i < DK; i += kWave) {
-            sq = fmaf(sQ[r * SD + i], sQ[r * SD + i], sq);
-            sk = fmaf(sK[r * SD + i], sK[r * SD + i], sk);
-        }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        const float rq = p.scale / sqrtf(sq + p.eps_l2);
-        const float rk = 1.0f / sqrtf(sk + p.eps_l2);
-        for (int i = lane; i < DK; i += kWave) {
-            sQ[r * SD + i] *= rq;
-            sK[r * SD + i] *= rk;
-        }
-    }
-    __syncthreads();
-    // 3. Gram matrices K K^T (strict lower) and Q K^T (lower incl. diagonal).
-    for (int idx = tid; idx < C * C; idx += NT) {
-        const int r = idx / C, s = idx % C;
-        float gkk = 0.f, gqk = 0.f;
-        if (s <= r) {
-            for (int i = 0; i < DK; ++i) {
-                gkk = fmaf(sK[r * SD + i], sK[s * SD + i], gkk);
-                gqk = fmaf(sQ[r * SD + i], sK[s * SD + i], gqk);
-            }
-        }
-        sGkk[r * SC + s] = gkk;
-        sGqk[r * SC + s] = gqk;
-    }
-    __syncthreads();
-
-    for (int gi = 0; gi < p.G; ++gi) {
-        const int h = hk * p.G + gi;
-        uint8_t* blk = p.vch + (static_cast<int64_t>(slot) * p.Hv + h) * L::bytes;
-        // 4. v conv, gates.
-        for (int idx = tid; idx < C * DV; idx += NT) {
-            const int r = idx / DV, j = idx % DV;
-            float y = 0.f;
-            if (r < Lc) y = conv_silu_at<BF16>(p, n, start, t0 + r, 2 * qk + h * DV + j, Cc, qk);
-            sV[r * SV + j] = y;
-        }
-        if (tid < C) {
-            float g = 0.f, beta = 0.f;
-            if (tid < Lc) {
-                using A = Act<BF16>;
-                using T = typename A::T;
-                const float av = A::load(static_cast<const T*>(p.a) + (t0 + tid) * p.as + h);
-                const float bv = A::load(static_cast<const T*>(p.b) + (t0 + tid) * p.bs + h);
-                g = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
-                beta = sigmoid(bv);
-            }
-            sg[tid] = g;
-            sbeta[tid] = beta;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) {
-                acc += sg[r];
-                sgam[r] = acc;
-            }
-        }
-        __syncthreads();
-        const float glast = sgam[C - 1];
-        if (tid < C) {
-            const float gm = sgam[tid];
-            cW[tid] = sbeta[tid] * expf(gm);
-            cU[tid] = sbeta[tid];
-            eG[tid] = expf(gm);
-            eD[tid] = expf(glast - gm);
-        }
-        // A (strict lower) into sT; forward substitution in place, row by row.
-        for (int idx = tid; idx < C * C; idx += NT) {
-            const int r = idx / C, s = idx % C;
-            sT[r * SC + s] = (s < r) ? sbeta[r] * expf(sgam[r] - sgam[s]) * sGkk[r * SC + s] : 0.f;
-        }
-        __syncthreads();
-        // Row r of Tm: Tm[r][c] = delta_rc - sum_{c<=s<r} A[r][s] Tm[s][c].
-        // Rows < r of sT already hold Tm; row r still holds A.
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-            if (tid < C) {
-                const int c = tid;
-                if (c < r) {
-                    for (int s = c; s < r; ++s) acc = fmaf(sT[r * SC + s], sT[s * SC + c], acc);
-                    acc = -acc;
-                } else {
-                    acc = (c == r) ? 1.f : 0.f;
-                }
-                sacc[c] = acc;
-            }
-            __syncthreads();
-            if (tid < C) sT[r * SC + tid] = sacc[tid];
-            __syncthreads();
-        }
-        // 5. operands in fragment order.
-        // -W [C][DK]: A tiles (mt, kt), 8 consecutive k per lane slot.
-        for (int slotf = tid; slotf < C * DK / 8; slotf += NT) {
-            const int tile = slotf / 64, ln = slotf % 64;
-            const int mt = tile / (DK / 32), kt = tile % (DK / 32);
-            const int r = mt * 16 + ln % 16, c0 = kt * 32 + 8 * (ln / 16);
-            float w8[8], q8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { w8[e] = 0.f; }
-            for (int s = 0; s <= r; ++s) {
-                const float coef = sT[r * SC + s] * cW[s];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w8[e] = fmaf(coef, sK[s * SD + c0 + e], w8[e]);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                w8[e] = -w8[e];
-                q8[e] = eG[r] * sQ[r * SD + c0 + e];
-            }
-            store_afrag(blk + L::negW + tile * 2048, ln, w8);
-            store_afrag(blk + L::QG + tile * 2048, ln, q8);
-        }
-        // K_d^T [DK][CK]: row i, col s = e^{glast - gamma_s} k_s[i] (0 for s >= C).
-        for (int slotf = tid; slotf < DK * CK / 8; slotf += NT) {
-            const int tile = slotf / 64, ln = slotf % 64;
-            const int mt = tile / (CK / 32), kt = tile % (CK / 32);
-            const int i = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
-            float x8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = s0 + e;
-                x8[e] = (s < C) ? eD[s] * sK[s * SD + i] : 0.f;
-            }
-            store_afrag(blk + L::KdT + tile * 2048, ln, x8);
-        }
-        // P [C][CK]: row r, col s = (s <= r) Gqk[r][s] e^{gamma_r - gamma_s}.
-        for (int slotf = tid; slotf < C * CK / 8; slotf += NT) {
-            const int tile = slotf / 64, ln = slotf % 64;
-            const int mt = tile / (CK / 32), kt = tile % (CK / 32);
-            const int r = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
-            float x8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = s0 + e;
-                x8[e] = (s <= r && s < C) ? sGqk[r * SC + s] * expf(sgam[r] - sgam[s]) : 0.f;
-            }
-            store_afrag(blk + L::P + tile * 2048, ln, x8);
-        }
-        // U~ [C][DV] in accumulator order: tile (mt, nt), lane: rows 4*(l/16)+i, col l%16.
-        for (int slotf = tid; slotf < C * DV / 4; slotf += NT) {
-            const int tile = slotf / 64, ln = slotf % 64;
-            const int mt = tile / (DV / 16), nt = tile % (DV / 16);
-            const int j = nt * 16 + ln % 16, r0 = mt * 16 + 4 * (ln / 16);
-            f32x4 u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = r0 + i;
-                float acc = 0.f;
-                for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * SC + s] * cU[s], sV[s * SV + j], acc);
-                u[i] = acc;
-            }
-            *reinterpret_cast<f32x4*>(blk + L::Ut + tile * 1024 + ln * 16) = u;
-        }
-        if (tid == 0) p.decay[static_cast<int64_t>(slot) * p.Hv + h] = expf(glast);
-        __syncthreads();   // sV, sT, gates reused by the next value head
-    }
-}
+namespace gdn {
 
 // ---------------------------------------------------------------------------
 // scan: one work-group per (sequence, value head, dv slice of DVS columns).
@@ -342,6 +110,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     constexpr int QH = (MTH + NW - 1) / NW;
     constexpr int HS = DK + 8;            // LDS row stride (bf16) of H^T
     constexpr int US = CK + 8;            // LDS row stride (bf16) of U^T
+    constexpr bool ALL_H = (MTH % NW) == 0;   // every wave owns QH H row tiles
     static_assert(DV % DVS == 0 && DVS % 16 == 0 && DK % 32 == 0 && C % 16 == 0, "shape");
 
     __shared__ __align__(16) uint16_t HThi[DVS * HS], HTlo[DVS * HS];
@@ -388,7 +157,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
 #pragma unroll
         for (int qh = 0; qh < QH; ++qh) {
             const int mth = wave + NW * qh;
-            if (mth >= MTH) continue;
+            if (!ALL_H && mth >= MTH) continue;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
                 uint16_t hi[4], lo[4];
@@ -407,38 +176,110 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
 
     const int c_begin = p.chunk_off[n], c_end = p.chunk_off[n + 1];
     const int64_t start = p.cu[n], end = p.cu[n + 1];
+    static_assert(QU == 1, "one U/O row tile per wave");
+    const int mt = wave;                     // this wave's chunk-row tile (if < MT)
+    // when every wave has a row tile / its H tiles, the role tests fold away
+    const bool has_u = (MT >= NW) || mt < MT;
+
+    // Software pipeline: every operand of chunk c+1 is loaded right after its
+    // last use in chunk c, so each load has a whole chunk step to land.  No
+    // fragment register is copied (a copy would make the in-order memory
+    // counter wait for the loads issued after it).
+    u32x4 w_h[KTH], w_l[KTH], q_h[KTH], q_l[KTH];
+    f32x4 ut[NTL];
+    u32x4 p_h[KTC], p_l[KTC], k_h[QH][KTC], k_l[QH][KTC];
+    float dec = 0.f;
+    auto blk_of = [&](int c) {
+        return p.vch + (static_cast<int64_t>(c) * p.Hv + h) * L::bytes;
+    };
+    auto load_wqu = [&](int c) {
+        const uint8_t* blk = blk_of(c);
+#pragma unroll
+        for (int kt = 0; kt < KTH; ++kt) {
+            const uint8_t* tw = blk + L::negW + (mt * KTH + kt) * 2048;
+            const uint8_t* tq = blk + L::QG + (mt * KTH + kt) * 2048;
+            w_h[kt] = *reinterpret_cast<const u32x4*>(tw + lane * 16);
+            w_l[kt] = *reinterpret_cast<const u32x4*>(tw + 1024 + lane * 16);
+            q_h[kt] = *reinterpret_cast<const u32x4*>(tq + lane * 16);
+            q_l[kt] = *reinterpret_cast<const u32x4*>(tq + 1024 + lane * 16);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+            const int tile = mt * (DV / 16) + sl * NTL + nt;
+            ut[nt] = *reinterpret_cast<const f32x4*>(blk + L::Ut + tile * 1024 + lane * 16);
+        }
+    };
+    auto load_p = [&](int c) {
+        const uint8_t* blk = blk_of(c);
+#pragma unroll
+        for (int kt = 0; kt < KTC; ++kt) {
+            const uint8_t* tp = blk + L::P + (mt * KTC + kt) * 2048;
+            p_h[kt] = *reinterpret_cast<const u32x4*>(tp + lane * 16);
+            p_l[kt] = *reinterpret_cast<const u32x4*>(tp + 1024 + lane * 16);
+        }
+    };
+    auto load_k = [&](int c) {
+        const uint8_t* blk = blk_of(c);
+#pragma unroll
+        for (int qh = 0; qh < QH; ++qh) {
+            const int mth = wave + NW * qh;
+            if (!ALL_H && mth >= MTH) continue;
+#pragma unroll
+            for (int kt = 0; kt < KTC; ++kt) {
+                const uint8_t* tk = blk + L::KdT + (mth * KTC + kt) * 2048;
+                k_h[qh][kt] = *reinterpret_cast<const u32x4*>(tk + lane * 16);
+                k_l[qh][kt] = *reinterpret_cast<const u32x4*>(tk + 1024 + lane * 16);
+            }
+        }
+    };
+    auto load_dec = [&](int c) { dec = p.decay[static_cast<int64_t>(c) * p.Hv + h]; };
+    if (c_begin < c_end) {
+        load_dec(c_begin);
+        if (has_u) {
+            load_wqu(c_begin);
+            load_p(c_begin);
+        }
+        load_k(c_begin);
+    }
+
     for (int c = c_begin; c < c_end; ++c) {
         const int64_t t0 = start + static_cast<int64_t>(c - c_begin) * C;
         const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
-        const uint8_t* blk = p.vch + (static_cast<int64_t>(c) * p.Hv + h) * L::bytes;
+        const int cn = (c + 1 < c_end) ? c + 1 : c;   // prefetch target (clamped)
 
-        f32x4 accu[QU][NTL], acco[QU][NTL];
-        // (1) U = U~ - W H and O = Q_G H for this wave's chunk rows.
-#pragma unroll
-        for (int qu = 0; qu < QU; ++qu) {
-            const int mt = wave + NW * qu;
-            if (mt >= MT) continue;
+        f32x4 accu[NTL], acco[NTL];
+        if (has_u) {
+            // (1) U = U~ - W H and O = Q_G H for this wave's chunk rows; the
+            // three split terms go term-major over the independent
+            // accumulators so dependent matrix-core ops are not back to back.
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                const int tile = mt * (DV / 16) + sl * NTL + nt;
-                accu[qu][nt] = *reinterpret_cast<const f32x4*>(blk + L::Ut + tile * 1024 + lane * 16);
-                acco[qu][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accu[nt] = ut[nt];
+                acco[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int kt = 0; kt < KTH; ++kt) {
-                const uint8_t* tw = blk + L::negW + (mt * KTH + kt) * 2048;
-                const uint8_t* tq = blk + L::QG + (mt * KTH + kt) * 2048;
-                const u32x4 awh = *reinterpret_cast<const u32x4*>(tw + lane * 16);
-                const u32x4 awl = *reinterpret_cast<const u32x4*>(tw + 1024 + lane * 16);
-                const u32x4 aqh = *reinterpret_cast<const u32x4*>(tq + lane * 16);
-                const u32x4 aql = *reinterpret_cast<const u32x4*>(tq + 1024 + lane * 16);
+                u32x4 bh[NTL], bl[NTL];
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
                     const int off = (nt * 16 + l16) * HS + kt * 32 + lq * 8;
-                    const u32x4 bh = *reinterpret_cast<const u32x4*>(&HThi[off]);
-                    const u32x4 bl = *reinterpret_cast<const u32x4*>(&HTlo[off]);
-                    accu[qu][nt] = mfma3(awh, awl, bh, bl, accu[qu][nt]);
-                    acco[qu][nt] = mfma3(aqh, aql, bh, bl, acco[qu][nt]);
+                    bh[nt] = *reinterpret_cast<const u32x4*>(&HThi[off]);
+                    bl[nt] = *reinterpret_cast<const u32x4*>(&HTlo[off]);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    accu[nt] = mfma(w_l[kt], bh[nt], accu[nt]);
+                    acco[nt] = mfma(q_l[kt], bh[nt], acco[nt]);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    accu[nt] = mfma(w_h[kt], bl[nt], accu[nt]);
+                    acco[nt] = mfma(q_h[kt], bl[nt], acco[nt]);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    accu[nt] = mfma(w_h[kt], bh[nt], accu[nt]);
+                    acco[nt] = mfma(q_h[kt], bh[nt], acco[nt]);
                 }
             }
             // (2) U^T into LDS (split).
@@ -446,7 +287,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
             for (int nt = 0; nt < NTL; ++nt) {
                 uint16_t hi[4], lo[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) split_bf16(accu[qu][nt][i], hi[i], lo[i]);
+                for (int i = 0; i < 4; ++i) split_bf16(accu[nt][i], hi[i], lo[i]);
                 const int off = (nt * 16 + l16) * US + mt * 16 + lq * 4;
                 *reinterpret_cast<uint2*>(&UThi[off]) =
                     make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
@@ -455,60 +296,73 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
             }
         }
         __syncthreads();
-        // (3) O += P U, store valid rows.
+        // (4) H' = e^{gamma_last} H + K_d^T U  (first: it is on the chain)
+        {
+            const float dcur = dec;
+            load_dec(cn);
+            if (has_u) load_wqu(cn);
+            u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
 #pragma unroll
-        for (int qu = 0; qu < QU; ++qu) {
-            const int mt = wave + NW * qu;
-            if (mt >= MT) continue;
-#pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) {
-                const uint8_t* tp = blk + L::P + (mt * KTC + kt) * 2048;
-                const u32x4 aph = *reinterpret_cast<const u32x4*>(tp + lane * 16);
-                const u32x4 apl = *reinterpret_cast<const u32x4*>(tp + 1024 + lane * 16);
+            for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
                     const int off = (nt * 16 + l16) * US + kt * 32 + lq * 8;
-                    const u32x4 bh = *reinterpret_cast<const u32x4*>(&UThi[off]);
-                    const u32x4 bl = *reinterpret_cast<const u32x4*>(&UTlo[off]);
-                    acco[qu][nt] = mfma3(aph, apl, bh, bl, acco[qu][nt]);
+                    ubh[kt][nt] = *reinterpret_cast<const u32x4*>(&UThi[off]);
+                    ubl[kt][nt] = *reinterpret_cast<const u32x4*>(&UTlo[off]);
                 }
+#pragma unroll
+            for (int qh = 0; qh < QH; ++qh) {
+                if (!ALL_H && wave + NW * qh >= MTH) continue;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hacc[qh][nt][i] *= dcur;
             }
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = mt * 16 + lq * 4 + i;
-                    if (r < Lc)
-                        p.core[((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16] = acco[qu][nt][i];
-                }
-            }
-        }
-        // (4) H' = e^{gamma_last} H + K_d^T U.
-        const float dec = p.decay[static_cast<int64_t>(c) * p.Hv + h];
-#pragma unroll
-        for (int qh = 0; qh < QH; ++qh) {
-            const int mth = wave + NW * qh;
-            if (mth >= MTH) continue;
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hacc[qh][nt][i] *= dec;
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
-                const uint8_t* tk = blk + L::KdT + (mth * KTC + kt) * 2048;
-                const u32x4 akh = *reinterpret_cast<const u32x4*>(tk + lane * 16);
-                const u32x4 akl = *reinterpret_cast<const u32x4*>(tk + 1024 + lane * 16);
+#pragma unroll
+                for (int term = 0; term < 3; ++term) {
+#pragma unroll
+                    for (int qh = 0; qh < QH; ++qh) {
+                        if (!ALL_H && wave + NW * qh >= MTH) continue;
+#pragma unroll
+                        for (int nt = 0; nt < NTL; ++nt) {
+                            const u32x4 a = term == 1 ? k_h[qh][kt] : (term == 0 ? k_l[qh][kt] : k_h[qh][kt]);
+                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
+                            hacc[qh][nt] = mfma(a, b, hacc[qh][nt]);
+                        }
+                    }
+                }
+            }
+            load_k(cn);
+            // (5) H into LDS for the next chunk (all waves finished reading H in (1)).
+            store_H_lds();
+            if (has_u) {
+                // (3) O += P U, store valid rows.
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) {
+#pragma unroll
+                    for (int term = 0; term < 3; ++term) {
+#pragma unroll
+                        for (int nt = 0; nt < NTL; ++nt) {
+                            const u32x4 a = term == 1 ? p_h[kt] : (term == 0 ? p_l[kt] : p_h[kt]);
+                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
+                            acco[nt] = mfma(a, b, acco[nt]);
+                        }
+                    }
+                }
+                load_p(cn);
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
-                    const int off = (nt * 16 + l16) * US + kt * 32 + lq * 8;
-                    const u32x4 bh = *reinterpret_cast<const u32x4*>(&UThi[off]);
-                    const u32x4 bl = *reinterpret_cast<const u32x4*>(&UTlo[off]);
-                    hacc[qh][nt] = mfma3(akh, akl, bh, bl, hacc[qh][nt]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = mt * 16 + lq * 4 + i;
+                        if (r < Lc)
+                            p.core[((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16] = acco[nt][i];
+                    }
                 }
             }
         }
-        // (5) H into LDS for the next chunk (all waves finished reading H in (1)).
-        store_H_lds();
         __syncthreads();
     }
 
@@ -615,7 +469,7 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.N, C, p.chunk_off);
     mark(1);
     if (p.max_chunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(p.max_chunks, p.Hk), dim3(256),
+        hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(p.max_chunks, p.Hv), dim3(256),
                            0, s, p);
     }
     mark(2);

@@ -43,8 +43,9 @@
  *     conv_w         [Cc][K] fp32, conv_w[c][K-1] multiplies the current token
  *   Token strides are in elements; 0 means dense.  Value head h reads key
  *   head h / (Hv/Hk).
- * - Alignment: q, k, v, z, out, core_out, states and conv states 16 bytes;
- *   strides of q/k/v/z multiples of 8 elements; a, b 4 bytes.
+ * - Alignment: q, k, v, z, out, core_out, states, conv states and conv_w
+ *   16 bytes; strides of q/k/v/z multiples of 8 elements; a, b element
+ *   aligned; A_log, dt_bias, norm_w 4 bytes.
  * - Errors: the return value is GDN_OK after a successful enqueue, otherwise
  *   a status code with detail text in gdn_last_error() (thread-local).  No
  *   work is enqueued when a call returns an error.  Device contents
