@@ -205,6 +205,22 @@ def main():
         "prefill_alg_tflops": (scan_f + prep_f) * T / (ms_step * 1e-3) / 1e12,
     }
 
+    # ---------------- context: measured device-copy bandwidth ----------------
+    cp_src = torch.empty(1 << 29, dtype=torch.float32, device=dev)     # 2 GiB
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    c0, c1 = new_events(2)
+    c0.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * cp_src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    result["hbm_copy_GBps"] = copy_gbs      # read + write bytes of a 2 GiB device copy
+    log(f"device copy: {copy_gbs:.1f} GB/s (read + write)")
+    del cp_src, cp_dst
+    torch.cuda.empty_cache()
+
     # ---------------- decode, 30 layers x B ----------------
     if not args.no_decode:
         L = args.layers

@@ -18,9 +18,11 @@
 // fixed state size per sequence is the one the llmxabe README's model
 // section gives (~60 MiB over 30 layers, i.e. 2 MiB per layer).
 //
+// The work-group has 512 threads: each half streams one value head of the
+// group, so the two heads' state loads, arithmetic and stores overlap.
 // Thread layout over H: DV/4 column groups (one float4 each) x RG row groups;
-// thread (rg, cg) holds rows rg + RG*m.  Loads of one instruction cover whole
-// 512-byte rows, so the stream is fully coalesced.  Column sums over the row
+// thread (rg, cg) holds a block of DK/RG consecutive rows.  Loads of one
+// instruction cover whole 512-byte rows, so the stream is fully coalesced.  Column sums over the row
 // groups are combined through LDS in a fixed order, so the result does not
 // depend on the batch: a sequence is bit-identical batched or alone (llmxabe
 // README, "Status").
@@ -29,50 +31,117 @@
 
 namespace gdn {
 
+constexpr int kDecodeHalf = 256;                 // threads per value head
+constexpr int kDecodeThreads = 2 * kDecodeHalf;  // two value heads stream at once
+
 template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams p) {
     using A = Act<BF16>;
     using T = typename A::T;
-    constexpr int NT = 256;
+    constexpr int NT = kDecodeHalf;
     constexpr int CG = DV / 4;          // float4 column groups
     constexpr int RG = NT / CG;         // row groups
     constexpr int RPT = DK / RG;        // rows per thread
     static_assert(CG <= 64 && NT % CG == 0 && DK % RG == 0 && RPT >= 1, "shape");
-    static_assert(2 * DK <= NT, "one thread per q/k channel");
+    static_assert(2 * DK <= kDecodeThreads, "one thread per q/k channel");
 
-    __shared__ float sq[DK], sk[DK], sv[DV], sz[DV];
-    __shared__ f32x4 red_k[RG][CG], red_q[RG][CG];
-    __shared__ float s_r[2], s_kq, s_eg, s_beta;
+    __shared__ float sq[DK], sk[DK], sv[2][DV], sz[2][DV];
+    __shared__ f32x4 red_k[2][RG][CG], red_q[2][RG][CG];
+    __shared__ float s_r[2], s_kq, s_eg[2], s_beta[2];
 
     const int b = blockIdx.x / p.Hk;
     const int hk = blockIdx.x % p.Hk;
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
+    // value head slot (uniform per wave, so the state base lives in SGPRs)
+    const int half = __builtin_amdgcn_readfirstlane(tid / NT);
+    const int t = tid % NT;
     const int Cc = 2 * p.Hk * DK + p.Hv * DV;
     const T* cin = static_cast<const T*>(p.conv_in);
     T* cout = static_cast<T*>(p.conv_out);
     const size_t crow = static_cast<size_t>(b) * 3 * Cc;
 
-    // conv1d(K=4) + SiLU of the q and k channels; shift their conv state.
-    if (tid < 2 * DK) {
-        const int isk = tid >= DK;
-        const int i = tid - isk * DK;
-        const int c = isk * p.Hk * DK + hk * DK + i;
-        const T* src = isk ? static_cast<const T*>(p.k) + b * p.ks + hk * DK + i
-                           : static_cast<const T*>(p.q) + b * p.qs + hk * DK + i;
-        T x = *src;
-        T t0 = cin ? cin[crow + c] : T(0);
-        T t1 = cin ? cin[crow + Cc + c] : T(0);
-        T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
-        const float* w = p.conv_w + static_cast<size_t>(c) * 4;
-        float acc = w[0] * A::load(&t0);
-        acc = fmaf(w[1], A::load(&t1), acc);
-        acc = fmaf(w[2], A::load(&t2), acc);
-        acc = fmaf(w[3], A::load(&x), acc);
-        (isk ? sk : sq)[i] = silu(acc);
-        cout[crow + c] = t1;
-        cout[crow + Cc + c] = t2;
-        cout[crow + 2 * Cc + c] = x;
+    // thread (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 of columns 4cg..4cg+3;
+    // one load instruction still covers whole 512-byte rows.  The first pair
+    // of heads' state stream is issued before anything else so its latency
+    // overlaps the conv and the norms.
+    const int cg = t % CG, rg = t / CG;
+    const uint32_t toff = static_cast<uint32_t>(rg * RPT * DV + 4 * cg);
+    f32x4 H[RPT];
+    auto load_state = [&](int g0) {
+        const int g = g0 + half;
+        if (g < p.G && p.state_in) {
+            const float* sb = p.state_in + (static_cast<size_t>(b) * p.Hv + hk * p.G + g) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < RPT; ++m)
+                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sb + toff + m * DV));
+        } else {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    load_state(0);
+
+    // One conv channel per thread, all loads issued before any arithmetic:
+    // threads [0, 2 DK) take the key head's q and k channels, threads
+    // [NT, NT + 2 DV) the v channels of the first pair of value heads (with
+    // their z and, on each head's first thread, the gate inputs a, b).
+    static_assert(DV <= NT, "one thread per v channel of a head pair");
+    {
+        const bool is_qk = tid < 2 * DK;
+        const int vj = tid - NT;
+        const int vg = vj / DV, vjj = vj - vg * DV;
+        const bool is_v = vj >= 0 && vj < 2 * DV && vg < p.G;
+        int c = 0;
+        const T* src = nullptr;
+        const T* zsrc = nullptr;
+        if (is_qk) {
+            const int isk = tid >= DK;
+            const int i = tid - isk * DK;
+            c = isk * p.Hk * DK + hk * DK + i;
+            src = isk ? static_cast<const T*>(p.k) + b * p.ks + hk * DK + i
+                      : static_cast<const T*>(p.q) + b * p.qs + hk * DK + i;
+        } else if (is_v) {
+            const int h = hk * p.G + vg;
+            c = 2 * p.Hk * DK + h * DV + vjj;
+            src = static_cast<const T*>(p.v) + b * p.vs + h * DV + vjj;
+            zsrc = static_cast<const T*>(p.z) + b * p.zs + h * DV + vjj;
+        }
+        if (is_qk || is_v) {
+            const T x = *src;
+            const T t0 = cin ? cin[crow + c] : T(0);
+            const T t1 = cin ? cin[crow + Cc + c] : T(0);
+            const T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
+            const f32x4 w = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c) * 4);
+            float zz = 0.f, av = 0.f, bv = 0.f;
+            const bool gate = is_v && vjj == 0;
+            if (is_v) zz = A::load(zsrc);
+            if (gate) {
+                const int h = hk * p.G + vg;
+                av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
+                bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
+            }
+            float acc = w[0] * A::load(&t0);
+            acc = fmaf(w[1], A::load(&t1), acc);
+            acc = fmaf(w[2], A::load(&t2), acc);
+            acc = fmaf(w[3], A::load(&x), acc);
+            const float y = silu(acc);
+            if (is_qk) {
+                (tid >= DK ? sk : sq)[tid >= DK ? tid - DK : tid] = y;
+            } else {
+                sv[vg][vjj] = y;
+                sz[vg][vjj] = zz;
+            }
+            if (gate) {
+                const int h = hk * p.G + vg;
+                const float gg = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
+                s_eg[vg] = expf(gg);
+                s_beta[vg] = sigmoid(bv);
+            }
+            cout[crow + c] = t1;
+            cout[crow + Cc + c] = t2;
+            cout[crow + 2 * Cc + c] = x;
+        }
     }
     __syncthreads();
     if (wave < 2) {
@@ -95,52 +164,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         if (lane == 0) s_kq = d;
     }
 
-    const int cg = tid % CG, rg = tid / CG;
-    for (int g = 0; g < p.G; ++g) {
+    for (int g0 = 0; g0 < p.G; g0 += 2) {
+        const int g = g0 + half;
+        const bool active = g < p.G;
         const int h = hk * p.G + g;
-        // conv + SiLU of this head's v channels, gate inputs.
-        for (int j = tid; j < DV; j += NT) {
-            const int c = 2 * p.Hk * DK + h * DV + j;
-            T x = static_cast<const T*>(p.v)[b * p.vs + h * DV + j];
-            T t0 = cin ? cin[crow + c] : T(0);
-            T t1 = cin ? cin[crow + Cc + c] : T(0);
-            T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
-            const float* w = p.conv_w + static_cast<size_t>(c) * 4;
-            float acc = w[0] * A::load(&t0);
-            acc = fmaf(w[1], A::load(&t1), acc);
-            acc = fmaf(w[2], A::load(&t2), acc);
-            acc = fmaf(w[3], A::load(&x), acc);
-            sv[j] = silu(acc);
-            sz[j] = A::load(static_cast<const T*>(p.z) + b * p.zs + h * DV + j);
-            cout[crow + c] = t1;
-            cout[crow + Cc + c] = t2;
-            cout[crow + 2 * Cc + c] = x;
-        }
-        if (tid == 0) {
-            const float av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
-            const float bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
-            const float gg = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
-            s_eg = expf(gg);
-            s_beta = sigmoid(bv);
-        }
-        __syncthreads();
-
         const size_t hbase = (static_cast<size_t>(b) * p.Hv + h) * DK * DV;
-        f32x4 H[RPT];
+        if (g0 > 0) load_state(g0);
+        // conv + SiLU of this head's v channels, gate inputs (the first pair
+        // was done in the prologue).
+        if (active && g0 > 0) {
+            for (int j = t; j < DV; j += NT) {
+                const int c = 2 * p.Hk * DK + h * DV + j;
+                T x = static_cast<const T*>(p.v)[b * p.vs + h * DV + j];
+                T t0 = cin ? cin[crow + c] : T(0);
+                T t1 = cin ? cin[crow + Cc + c] : T(0);
+                T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
+                const float* w = p.conv_w + static_cast<size_t>(c) * 4;
+                float acc = w[0] * A::load(&t0);
+                acc = fmaf(w[1], A::load(&t1), acc);
+                acc = fmaf(w[2], A::load(&t2), acc);
+                acc = fmaf(w[3], A::load(&x), acc);
+                sv[half][j] = silu(acc);
+                sz[half][j] = A::load(static_cast<const T*>(p.z) + b * p.zs + h * DV + j);
+                cout[crow + c] = t1;
+                cout[crow + Cc + c] = t2;
+                cout[crow + 2 * Cc + c] = x;
+            }
+            if (t == 0) {
+                const float av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
+                const float bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
+                const float gg = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
+                s_eg[half] = expf(gg);
+                s_beta[half] = sigmoid(bv);
+            }
+        }
         f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const int i = rg + RG * m;
-            if (p.state_in) {
-                H[m] = __builtin_nontemporal_load(
-                    reinterpret_cast<const f32x4*>(p.state_in + hbase + static_cast<size_t>(i) * DV) + cg);
-            } else {
-                H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + RG * m;
+            const int i = rg * RPT + m;
             const float kk = sk[i], qq = sq[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -148,65 +209,67 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
                 rq[e] = fmaf(H[m][e], qq, rq[e]);
             }
         }
-        red_k[rg][cg] = rk;
-        red_q[rg][cg] = rq;
+        red_k[half][rg][cg] = rk;
+        red_q[half][rg][cg] = rq;
         __syncthreads();
-        f32x4 RK = red_k[0][cg], RQ = red_q[0][cg];
+        if (active) {
+            f32x4 RK = red_k[half][0][cg], RQ = red_q[half][0][cg];
 #pragma unroll
-        for (int r = 1; r < RG; ++r) {
-            f32x4 a = red_k[r][cg], c = red_q[r][cg];
+            for (int r = 1; r < RG; ++r) {
+                f32x4 a = red_k[half][r][cg], c = red_q[half][r][cg];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { RK[e] += a[e]; RQ[e] += c[e]; }
-        }
-        const float eg = s_eg, beta = s_beta, kq = s_kq;
-        f32x4 u, o;
+                for (int e = 0; e < 4; ++e) { RK[e] += a[e]; RQ[e] += c[e]; }
+            }
+            const float eg = s_eg[half], beta = s_beta[half], kq = s_kq;
+            f32x4 u, o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            u[e] = beta * (sv[4 * cg + e] - eg * RK[e]);
-            o[e] = fmaf(eg, RQ[e], kq * u[e]);
-        }
+            for (int e = 0; e < 4; ++e) {
+                u[e] = beta * (sv[half][4 * cg + e] - eg * RK[e]);
+                o[e] = fmaf(eg, RQ[e], kq * u[e]);
+            }
+            float* so = p.state_out + hbase;
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + RG * m;
-            const float kk = sk[i];
-            f32x4 hn;
+            for (int m = 0; m < RPT; ++m) {
+                const float kk = sk[rg * RPT + m];
+                f32x4 hn;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hn[e] = fmaf(eg, H[m][e], kk * u[e]);
-            __builtin_nontemporal_store(
-                hn, reinterpret_cast<f32x4*>(p.state_out + hbase + static_cast<size_t>(i) * DV) + cg);
-        }
-        // z-gated RMSNorm over dv: row group 0 (lanes 0..CG-1 of wave 0).
-        if (wave == 0) {
-            float ps = 0.f;
-            if (lane < CG) ps = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-            ps = wave_sum(ps);
-            if (lane < CG) {
-                const float r = 1.0f / sqrtf(ps / DV + p.eps_rms);
-                const size_t obase = (static_cast<size_t>(b) * p.Hv + h) * DV + 4 * cg;
-                float y[4];
+                for (int e = 0; e < 4; ++e) hn[e] = fmaf(eg, H[m][e], kk * u[e]);
+                __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(so + toff + m * DV));
+            }
+            // z-gated RMSNorm over dv: row group 0 = lanes 0..CG-1 of the
+            // half's first wave.
+            if (t < kWave) {
+                float ps = 0.f;
+                if (t < CG) ps = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+                ps = wave_sum(ps);
+                if (t < CG) {
+                    const float r = 1.0f / sqrtf(ps / DV + p.eps_rms);
+                    const size_t obase = (static_cast<size_t>(b) * p.Hv + h) * DV + 4 * cg;
+                    float y[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = p.norm_w[4 * cg + e] * (o[e] * r) * silu(sz[4 * cg + e]);
-                if (p.out_bf16) {
-                    uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = p.norm_w[4 * cg + e] * (o[e] * r) * silu(sz[half][4 * cg + e]);
+                    if (p.out_bf16) {
+                        uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
-                } else {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) =
-                        f32x4{y[0], y[1], y[2], y[3]};
+                        for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
+                    } else {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) =
+                            f32x4{y[0], y[1], y[2], y[3]};
+                    }
+                    if (p.core_out)
+                        *reinterpret_cast<f32x4*>(p.core_out + obase) = o;
                 }
-                if (p.core_out)
-                    *reinterpret_cast<f32x4*>(p.core_out + obase) = o;
             }
         }
-        __syncthreads();   // LDS (sv, sz, red_*) reused by the next value head
+        __syncthreads();   // LDS (sv, sz, red_*) reused by the next pair of heads
     }
 }
 
 template <int DK, int DV, bool BF16>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.Hk));
-    hipLaunchKernelGGL((decode_kernel<DK, DV, BF16>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_kernel<DK, DV, BF16>), grid, dim3(kDecodeThreads), 0, s, p);
     return hipGetLastError();
 }
 

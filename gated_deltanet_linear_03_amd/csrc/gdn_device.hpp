@@ -75,6 +75,13 @@ __device__ __forceinline__ float softplus(float x) {
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// SiLU on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32, each about
+// 1 ulp): a few ulp of relative error, used on the prefill path where it is
+// evaluated for every conv output.  x -> -inf gives -0.
+__device__ __forceinline__ float silu_fast(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
 // ---- matrix-core product ---------------------------------------------------
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {

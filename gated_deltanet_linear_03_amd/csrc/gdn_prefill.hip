@@ -469,7 +469,7 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.N, C, p.chunk_off);
     mark(1);
     if (p.max_chunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(p.max_chunks, p.Hv), dim3(256),
+        hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(p.max_chunks, p.Hv), dim3(kPrepThreads),
                            0, s, p);
     }
     mark(2);

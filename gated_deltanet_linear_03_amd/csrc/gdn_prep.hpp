@@ -1,6 +1,6 @@
 // gdn_prep.hpp -- chunk-parallel operand kernel of the chunked prefill.
 //
-// One work-group (256 threads, 4 waves) per (chunk slot, value head h).  For
+// One work-group (512 threads, 8 waves) per (chunk slot, value head h).  For
 // the chunk's C tokens it computes, entirely on chip:
 //   q^, k^  conv1d(K=4) + SiLU + L2 norm of key head h/G (row items of 8
 //           channels: 16-byte loads, norms reduced across the lanes of a row)
@@ -98,7 +98,7 @@ __device__ __forceinline__ void conv8x4(const PrefillParams& p, int n, int64_t s
             acc = fmaf(w[e][1], x[t + 1][e], acc);
             acc = fmaf(w[e][2], x[t + 2][e], acc);
             acc = fmaf(w[e][3], x[t + 3][e], acc);
-            y[t][e] = (r0 + t < valid) ? silu(acc) : 0.f;
+            y[t][e] = (r0 + t < valid) ? silu_fast(acc) : 0.f;
         }
     }
 }
@@ -131,13 +131,16 @@ __device__ __forceinline__ float hl(const uint16_t* h, const uint16_t* l, int i)
     return bf16_bits_to_f32(h[i]) + bf16_bits_to_f32(l[i]);
 }
 
+constexpr int kPrepThreads = 512;     // 8 waves: two per SIMD share the 160 KiB LDS
+
 template <int DK, int DV, int C, bool BF16>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     using S = PrepSmem<DK, DV, C>;
     using L = VchLayout<DK, DV, C>;
     constexpr int CK = S::CK, SQ = S::SQ, ST = S::ST, SG = S::SG;
     constexpr int NB = C / 16;           // 16-token blocks in a chunk
-    constexpr int NT = 256;
+    constexpr int NT = kPrepThreads;
+    constexpr int NW = NT / kWave;
     static_assert(C % 16 == 0 && DK % 32 == 0 && DV % 16 == 0 && DK <= 128, "shape");
     static_assert(S::total <= 160 * 1024, "LDS");
     __shared__ __align__(16) uint8_t smem[S::total];
@@ -263,8 +266,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
         const float glast = __shfl(v, C - 1, kWave);
         if (lane < C) {
             sgam[lane] = v;
-            sE[lane] = expf(v);
-            sD[lane] = expf(glast - v);
+            sE[lane] = exp_neg(v);
+            sD[lane] = exp_neg(glast - v);
         }
         if (lane == 0) p.decay[static_cast<int64_t>(slot) * p.Hv + h] = expf(glast);
     }
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
     // ---- 2. Gram matrices on the matrix cores (lower tiles) ----
     {
         constexpr int NTI = NB * (NB + 1) / 2;
-        for (int job = wave; job < 2 * NTI; job += NT / kWave) {
+        for (int job = wave; job < 2 * NTI; job += NW) {
             const int which = job / NTI;          // 0: K K^T, 1: Q K^T
             int idx = job % NTI, mt = 0;
             while (idx > mt) { idx -= mt + 1; ++mt; }
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int s = s0 + e;
-            x[e] = (s <= r && s < C) ? sGqk[r * SG + s] * expf(sgam[r] - sgam[s]) : 0.f;
+            x[e] = (s <= r && s < C) ? sGqk[r * SG + s] * exp_neg(sgam[r] - sgam[s]) : 0.f;
         }
         u32x4 hi, lo;
         split8(x, hi, lo);
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
     }
     for (int idx = tid; idx < C * C; idx += NT) {             // A, strict lower
         const int r = idx / C, s = idx % C;
-        sGkk[r * SG + s] = (s < r) ? sbeta[r] * expf(sgam[r] - sgam[s]) * sGkk[r * SG + s] : 0.f;
+        sGkk[r * SG + s] = (s < r) ? sbeta[r] * exp_neg(sgam[r] - sgam[s]) * sGkk[r * SG + s] : 0.f;
     }
     __syncthreads();
 
@@ -414,11 +417,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
     // ---- 7. [W | U~] = Tp [e^gamma K^ | V^] on the matrix cores ----
     constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU;
     constexpr int JOBS = NB * NTT;
-    constexpr int JPW = (JOBS + 3) / 4;
+    constexpr int JPW = (JOBS + NW - 1) / NW;
     f32x4 wres[JPW];
 #pragma unroll
     for (int q = 0; q < JPW; ++q) {
-        const int job = wave + 4 * q;
+        const int job = wave + NW * q;
         if (job >= JOBS) continue;
         const int mt = job / NTT, nt = job % NTT;
         const bool isw = nt < NTW;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p) {
     // ---- 8. stage -W (split) over K^, then copy out as A fragments ----
 #pragma unroll
     for (int q = 0; q < JPW; ++q) {
-        const int job = wave + 4 * q;
+        const int job = wave + NW * q;
         if (job >= JOBS) continue;
         const int mt = job / NTT, nt = job % NTT;
         if (nt >= NTW) continue;
