@@ -181,107 +181,108 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     // when every wave has a row tile / its H tiles, the role tests fold away
     const bool has_u = (MT >= NW) || mt < MT;
 
-    // Software pipeline: every operand of chunk c+1 is loaded right after its
-    // last use in chunk c, so each load has a whole chunk step to land.  No
-    // fragment register is copied (a copy would make the in-order memory
-    // counter wait for the loads issued after it).
-    u32x4 w_h[KTH], w_l[KTH], q_h[KTH], q_l[KTH];
-    f32x4 ut[NTL];
-    u32x4 p_h[KTC], p_l[KTC], k_h[QH][KTC], k_l[QH][KTC];
-    float dec = 0.f;
-    auto blk_of = [&](int c) {
-        return p.vch + (static_cast<int64_t>(c) * p.Hv + h) * L::bytes;
+    // Software pipeline with two operand sets in registers (ping-pong): while
+    // chunk c computes from one set, chunk c+1's fragments load into the
+    // other, in four groups issued between chunk c's first matrix-core ops,
+    // so load issue overlaps arithmetic instead of stalling a phase.
+    struct Ops {
+        u32x4 w_h[KTH], w_l[KTH], q_h[KTH], q_l[KTH];
+        f32x4 ut[NTL];
+        u32x4 p_h[KTC], p_l[KTC], k_h[QH][KTC], k_l[QH][KTC];
+        float dec;
     };
-    auto load_wqu = [&](int c) {
-        const uint8_t* blk = blk_of(c);
+    auto load_group = [&](Ops& o, int c, int grp) {
+        const uint8_t* blk = p.vch + (static_cast<int64_t>(c) * p.Hv + h) * L::bytes;
+        if (grp == 0) {
+            o.dec = p.decay[static_cast<int64_t>(c) * p.Hv + h];
+            if (has_u) {
 #pragma unroll
-        for (int kt = 0; kt < KTH; ++kt) {
-            const uint8_t* tw = blk + L::negW + (mt * KTH + kt) * 2048;
-            const uint8_t* tq = blk + L::QG + (mt * KTH + kt) * 2048;
-            w_h[kt] = *reinterpret_cast<const u32x4*>(tw + lane * 16);
-            w_l[kt] = *reinterpret_cast<const u32x4*>(tw + 1024 + lane * 16);
-            q_h[kt] = *reinterpret_cast<const u32x4*>(tq + lane * 16);
-            q_l[kt] = *reinterpret_cast<const u32x4*>(tq + 1024 + lane * 16);
-        }
+                for (int kt = 0; kt < KTH; ++kt) {
+                    const uint8_t* tw = blk + L::negW + (mt * KTH + kt) * 2048;
+                    o.w_h[kt] = *reinterpret_cast<const u32x4*>(tw + lane * 16);
+                    o.w_l[kt] = *reinterpret_cast<const u32x4*>(tw + 1024 + lane * 16);
+                }
+            }
+        } else if (grp == 1) {
+            if (has_u) {
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-            const int tile = mt * (DV / 16) + sl * NTL + nt;
-            ut[nt] = *reinterpret_cast<const f32x4*>(blk + L::Ut + tile * 1024 + lane * 16);
-        }
-    };
-    auto load_p = [&](int c) {
-        const uint8_t* blk = blk_of(c);
+                for (int kt = 0; kt < KTH; ++kt) {
+                    const uint8_t* tq = blk + L::QG + (mt * KTH + kt) * 2048;
+                    o.q_h[kt] = *reinterpret_cast<const u32x4*>(tq + lane * 16);
+                    o.q_l[kt] = *reinterpret_cast<const u32x4*>(tq + 1024 + lane * 16);
+                }
+            }
+        } else if (grp == 2) {
+            if (has_u) {
 #pragma unroll
-        for (int kt = 0; kt < KTC; ++kt) {
-            const uint8_t* tp = blk + L::P + (mt * KTC + kt) * 2048;
-            p_h[kt] = *reinterpret_cast<const u32x4*>(tp + lane * 16);
-            p_l[kt] = *reinterpret_cast<const u32x4*>(tp + 1024 + lane * 16);
-        }
-    };
-    auto load_k = [&](int c) {
-        const uint8_t* blk = blk_of(c);
+                for (int nt = 0; nt < NTL; ++nt) {
+                    const int tile = mt * (DV / 16) + sl * NTL + nt;
+                    o.ut[nt] = *reinterpret_cast<const f32x4*>(blk + L::Ut + tile * 1024 + lane * 16);
+                }
 #pragma unroll
-        for (int qh = 0; qh < QH; ++qh) {
-            const int mth = wave + NW * qh;
-            if (!ALL_H && mth >= MTH) continue;
+                for (int kt = 0; kt < KTC; ++kt) {
+                    const uint8_t* tp = blk + L::P + (mt * KTC + kt) * 2048;
+                    o.p_h[kt] = *reinterpret_cast<const u32x4*>(tp + lane * 16);
+                    o.p_l[kt] = *reinterpret_cast<const u32x4*>(tp + 1024 + lane * 16);
+                }
+            }
+        } else {
 #pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) {
-                const uint8_t* tk = blk + L::KdT + (mth * KTC + kt) * 2048;
-                k_h[qh][kt] = *reinterpret_cast<const u32x4*>(tk + lane * 16);
-                k_l[qh][kt] = *reinterpret_cast<const u32x4*>(tk + 1024 + lane * 16);
+            for (int qh = 0; qh < QH; ++qh) {
+                const int mth = wave + NW * qh;
+                if (!ALL_H && mth >= MTH) continue;
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) {
+                    const uint8_t* tk = blk + L::KdT + (mth * KTC + kt) * 2048;
+                    o.k_h[qh][kt] = *reinterpret_cast<const u32x4*>(tk + lane * 16);
+                    o.k_l[qh][kt] = *reinterpret_cast<const u32x4*>(tk + 1024 + lane * 16);
+                }
             }
         }
     };
-    auto load_dec = [&](int c) { dec = p.decay[static_cast<int64_t>(c) * p.Hv + h]; };
-    if (c_begin < c_end) {
-        load_dec(c_begin);
-        if (has_u) {
-            load_wqu(c_begin);
-            load_p(c_begin);
-        }
-        load_k(c_begin);
-    }
 
-    for (int c = c_begin; c < c_end; ++c) {
+    auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
         const int64_t t0 = start + static_cast<int64_t>(c - c_begin) * C;
         const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
-        const int cn = (c + 1 < c_end) ? c + 1 : c;   // prefetch target (clamped)
-
         f32x4 accu[NTL], acco[NTL];
-        if (has_u) {
-            // (1) U = U~ - W H and O = Q_G H for this wave's chunk rows; the
-            // three split terms go term-major over the independent
-            // accumulators so dependent matrix-core ops are not back to back.
+        // (1) U = U~ - W H and O = Q_G H for this wave's chunk rows; the
+        // three split terms go term-major over the independent accumulators
+        // so dependent matrix-core ops are not back to back.
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+            accu[nt] = cur.ut[nt];
+            acco[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kt = 0; kt < KTH; ++kt) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp)
+                if (grp * KTH / 4 == kt) load_group(nxt, cn, grp);
+            if (!has_u) continue;
+            u32x4 bh[NTL], bl[NTL];
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                accu[nt] = ut[nt];
-                acco[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int off = (nt * 16 + l16) * HS + kt * 32 + lq * 8;
+                bh[nt] = *reinterpret_cast<const u32x4*>(&HThi[off]);
+                bl[nt] = *reinterpret_cast<const u32x4*>(&HTlo[off]);
             }
 #pragma unroll
-            for (int kt = 0; kt < KTH; ++kt) {
-                u32x4 bh[NTL], bl[NTL];
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    const int off = (nt * 16 + l16) * HS + kt * 32 + lq * 8;
-                    bh[nt] = *reinterpret_cast<const u32x4*>(&HThi[off]);
-                    bl[nt] = *reinterpret_cast<const u32x4*>(&HTlo[off]);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    accu[nt] = mfma(w_l[kt], bh[nt], accu[nt]);
-                    acco[nt] = mfma(q_l[kt], bh[nt], acco[nt]);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    accu[nt] = mfma(w_h[kt], bl[nt], accu[nt]);
-                    acco[nt] = mfma(q_h[kt], bl[nt], acco[nt]);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    accu[nt] = mfma(w_h[kt], bh[nt], accu[nt]);
-                    acco[nt] = mfma(q_h[kt], bh[nt], acco[nt]);
-                }
+            for (int nt = 0; nt < NTL; ++nt) {
+                accu[nt] = mfma(cur.w_l[kt], bh[nt], accu[nt]);
+                acco[nt] = mfma(cur.q_l[kt], bh[nt], acco[nt]);
             }
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                accu[nt] = mfma(cur.w_h[kt], bl[nt], accu[nt]);
+                acco[nt] = mfma(cur.q_h[kt], bl[nt], acco[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                accu[nt] = mfma(cur.w_h[kt], bh[nt], accu[nt]);
+                acco[nt] = mfma(cur.q_h[kt], bh[nt], acco[nt]);
+            }
+        }
+        if (has_u) {
             // (2) U^T into LDS (split).
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
@@ -296,75 +297,80 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
             }
         }
         __syncthreads();
-        // (4) H' = e^{gamma_last} H + K_d^T U  (first: it is on the chain)
-        {
-            const float dcur = dec;
-            load_dec(cn);
-            if (has_u) load_wqu(cn);
-            u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
+        u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
 #pragma unroll
-            for (int kt = 0; kt < KTC; ++kt)
+        for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    const int off = (nt * 16 + l16) * US + kt * 32 + lq * 8;
-                    ubh[kt][nt] = *reinterpret_cast<const u32x4*>(&UThi[off]);
-                    ubl[kt][nt] = *reinterpret_cast<const u32x4*>(&UTlo[off]);
-                }
-#pragma unroll
-            for (int qh = 0; qh < QH; ++qh) {
-                if (!ALL_H && wave + NW * qh >= MTH) continue;
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hacc[qh][nt][i] *= dcur;
+            for (int nt = 0; nt < NTL; ++nt) {
+                const int off = (nt * 16 + l16) * US + kt * 32 + lq * 8;
+                ubh[kt][nt] = *reinterpret_cast<const u32x4*>(&UThi[off]);
+                ubl[kt][nt] = *reinterpret_cast<const u32x4*>(&UTlo[off]);
             }
+        // (4) H' = e^{gamma_last} H + K_d^T U  (first: it is on the chain)
+#pragma unroll
+        for (int qh = 0; qh < QH; ++qh) {
+            if (!ALL_H && wave + NW * qh >= MTH) continue;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hacc[qh][nt][i] *= cur.dec;
+        }
+#pragma unroll
+        for (int kt = 0; kt < KTC; ++kt) {
+#pragma unroll
+            for (int term = 0; term < 3; ++term) {
+#pragma unroll
+                for (int qh = 0; qh < QH; ++qh) {
+                    if (!ALL_H && wave + NW * qh >= MTH) continue;
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) {
+                        const u32x4 a = term == 1 ? cur.k_h[qh][kt] : (term == 0 ? cur.k_l[qh][kt] : cur.k_h[qh][kt]);
+                        const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
+                        hacc[qh][nt] = mfma(a, b, hacc[qh][nt]);
+                    }
+                }
+            }
+        }
+        // (5) H into LDS for the next chunk (all waves finished reading H in (1)).
+        store_H_lds();
+        if (has_u) {
+            // (3) O += P U, store valid rows.
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
 #pragma unroll
                 for (int term = 0; term < 3; ++term) {
 #pragma unroll
-                    for (int qh = 0; qh < QH; ++qh) {
-                        if (!ALL_H && wave + NW * qh >= MTH) continue;
-#pragma unroll
-                        for (int nt = 0; nt < NTL; ++nt) {
-                            const u32x4 a = term == 1 ? k_h[qh][kt] : (term == 0 ? k_l[qh][kt] : k_h[qh][kt]);
-                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
-                            hacc[qh][nt] = mfma(a, b, hacc[qh][nt]);
-                        }
+                    for (int nt = 0; nt < NTL; ++nt) {
+                        const u32x4 a = term == 1 ? cur.p_h[kt] : (term == 0 ? cur.p_l[kt] : cur.p_h[kt]);
+                        const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
+                        acco[nt] = mfma(a, b, acco[nt]);
                     }
                 }
             }
-            load_k(cn);
-            // (5) H into LDS for the next chunk (all waves finished reading H in (1)).
-            store_H_lds();
-            if (has_u) {
-                // (3) O += P U, store valid rows.
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt) {
+            for (int nt = 0; nt < NTL; ++nt) {
 #pragma unroll
-                    for (int term = 0; term < 3; ++term) {
-#pragma unroll
-                        for (int nt = 0; nt < NTL; ++nt) {
-                            const u32x4 a = term == 1 ? p_h[kt] : (term == 0 ? p_l[kt] : p_h[kt]);
-                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
-                            acco[nt] = mfma(a, b, acco[nt]);
-                        }
-                    }
-                }
-                load_p(cn);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = mt * 16 + lq * 4 + i;
-                        if (r < Lc)
-                            p.core[((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16] = acco[nt][i];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int r = mt * 16 + lq * 4 + i;
+                    if (r < Lc)
+                        p.core[((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16] = acco[nt][i];
                 }
             }
         }
         __syncthreads();
+    };
+
+    Ops opA, opB;
+    if (c_begin < c_end) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) load_group(opA, c_begin, grp);
     }
+    int c = c_begin;
+    for (; c + 1 < c_end; c += 2) {
+        step(opA, opB, c, c + 1);
+        step(opB, opA, c + 1, (c + 2 < c_end) ? c + 2 : c + 1);
+    }
+    if (c < c_end) step(opA, opB, c, c);
 
     // final state
     if (p.state_out) {

@@ -64,32 +64,70 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float* x) {
     }
 }
 
-// conv1d(K=4) + SiLU of 8 channels [c0, c0+8) for the 4 tokens r0..r0+3 of
-// a chunk starting at token t0 of sequence n (tokens at or past `valid` give
-// zeros).  `src` is q, k or v (row stride `rs`, in-row offset `col`); history
-// before `start` comes from the conv state rows.  The 7 input rows are all
-// loaded before any arithmetic, so their latencies overlap.
+// Raw input rows of one conv item: 8 channels [c0, c0+8) for the 7 token
+// positions r0-3 .. r0+3 of a chunk (chunk rows at or past `valid` and
+// history before the first conv-state row read as zeros).
 template <bool BF16>
-__device__ __forceinline__ void conv8x4(const PrefillParams& p, int n, int64_t start,
-                                        int64_t t0, int r0, int valid, const void* src,
-                                        int64_t rs, int col, int c0, int Cc, float (*y)[8]) {
-    float x[7][8];
+struct RawRows {
+    u32x4 r[7][BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_rows(const PrefillParams& p, int n, int64_t start, int64_t t0,
+                                          int r0, int valid, const void* src, int64_t rs, int col,
+                                          int c0, int Cc, RawRows<BF16>& raw) {
+    constexpr int W = BF16 ? 1 : 2;
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
-        const int rr = r0 - 3 + j;                 // chunk-relative row
+        const int rr = r0 - 3 + j;
         const int64_t pp = t0 + rr;
+        const void* base = nullptr;
+        int64_t off = 0;
         if (rr < valid && pp >= start) {
-            load8<BF16>(src, pp * rs + col, x[j]);
+            base = src;
+            off = pp * rs + col;
         } else if (rr < valid && p.conv_in && pp - start >= -3) {
-            load8<BF16>(p.conv_in, (static_cast<int64_t>(n) * 3 + 3 + (pp - start)) * Cc + c0, x[j]);
-        } else {
+            base = p.conv_in;
+            off = (static_cast<int64_t>(n) * 3 + 3 + (pp - start)) * Cc + c0;
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[j][e] = 0.f;
+        for (int w = 0; w < W; ++w) {
+            if (base) {
+                const u32x4* q = BF16 ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off)
+                                      : reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + off);
+                raw.r[j][w] = q[w];
+            } else {
+                raw.r[j][w] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
     }
-    f32x4 w[8];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void row8(const RawRows<BF16>& raw, int j, float* x) {
+    if constexpr (BF16) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const f32x4*>(p.conv_w + (c0 + e) * 4);
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(raw.r[j][0][e] << 16);
+            x[2 * e + 1] = __uint_as_float(raw.r[j][0][e] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = __uint_as_float(raw.r[j][0][e]);
+            x[4 + e] = __uint_as_float(raw.r[j][1][e]);
+        }
+    }
+}
+
+// conv1d(K=4) + SiLU of the item's 8 channels at its 4 tokens; tokens at or
+// past `valid` give zeros.
+template <bool BF16>
+__device__ __forceinline__ void conv_rows(const RawRows<BF16>& raw, const f32x4* w, int r0,
+                                          int valid, float (*y)[8]) {
+    float x[7][8];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) row8<BF16>(raw, j, x[j]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -179,53 +217,73 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     const int Cc = 2 * qk + p.Hv * DV;
     uint8_t* blk = p.vch + (static_cast<int64_t>(slot) * p.Hv + h) * L::bytes;
 
-    // ---- 1. q^, k^ rows: conv + SiLU + L2 norm; an item is 4 tokens x 8 channels ----
+    // ---- 1. conv inputs, then conv + SiLU (+ L2 norm for q, k) ----
+    // An item is 4 tokens x 8 channels.  Each thread owns at most one q/k
+    // item and one v item and issues all of its loads (both items' 7 input
+    // rows, their conv weights, the gate inputs) before any arithmetic, so
+    // the chunk's inputs cost one memory round trip.
     static_assert(C % 4 == 0, "row groups");
     {
-        constexpr int GPR = DK / 8;                 // lanes per token row
-        constexpr int ITEMS = 2 * (C / 4) * GPR;
-        static_assert(kWave % GPR == 0, "row segment");
-        for (int it = tid; it < ITEMS; it += NT) {
-            const int tensor = it / ((C / 4) * GPR);
-            const int rem = it % ((C / 4) * GPR);
-            const int grp = rem % GPR, r0 = (rem / GPR) * 4;
+        constexpr int GPRK = DK / 8, GPRV = DV / 8;        // lanes per token row
+        constexpr int IQK = 2 * (C / 4) * GPRK, IV = (C / 4) * GPRV;
+        static_assert(IQK <= NT && IV <= NT && kWave % GPRK == 0, "one item of a kind per thread");
+        const bool has_qk = tid < IQK, has_v = tid < IV;
+        const int qtensor = tid / ((C / 4) * GPRK);
+        const int qrem = tid % ((C / 4) * GPRK);
+        const int qgrp = qrem % GPRK, qr0 = (qrem / GPRK) * 4;
+        const int vgrp = tid % GPRV, vr0 = (tid / GPRV) * 4;
+        const int qc0 = qtensor * qk + hk * DK + qgrp * 8;
+        const int vc0 = 2 * qk + h * DV + vgrp * 8;
+        RawRows<BF16> rq, rv;
+        f32x4 wq[8], wv[8];
+        float av = 0.f, bv = 0.f;
+        if (has_qk)
+            load_rows<BF16>(p, n, start, t0, qr0, Lc, qtensor ? p.k : p.q, qtensor ? p.ks : p.qs,
+                            hk * DK + qgrp * 8, qc0, Cc, rq);
+        if (has_v)
+            load_rows<BF16>(p, n, start, t0, vr0, Lc, p.v, p.vs, h * DV + vgrp * 8, vc0, Cc, rv);
+        if (tid < Lc) {
+            using A = Act<BF16>;
+            using T = typename A::T;
+            av = A::load(static_cast<const T*>(p.a) + (t0 + tid) * p.as + h);
+            bv = A::load(static_cast<const T*>(p.b) + (t0 + tid) * p.bs + h);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (has_qk) wq[e] = *reinterpret_cast<const f32x4*>(p.conv_w + (qc0 + e) * 4);
+            if (has_v) wv[e] = *reinterpret_cast<const f32x4*>(p.conv_w + (vc0 + e) * 4);
+        }
+        if (has_qk) {
             float y[4][8];
-            conv8x4<BF16>(p, n, start, t0, r0, Lc, tensor ? p.k : p.q, tensor ? p.ks : p.qs,
-                          hk * DK + grp * 8, tensor * qk + hk * DK + grp * 8, Cc, y);
-            uint16_t* dh = tensor ? sKh : sQh;
-            uint16_t* dl = tensor ? sKl : sQl;
-            const float sc = tensor ? 1.0f : p.scale;
+            conv_rows<BF16>(rq, wq, qr0, Lc, y);
+            uint16_t* dh = qtensor ? sKh : sQh;
+            uint16_t* dl = qtensor ? sKl : sQl;
+            const float sc = qtensor ? 1.0f : p.scale;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = fmaf(y[t][e], y[t][e], ss);
 #pragma unroll
-                for (int off = GPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+                for (int off = GPRK / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
                 const float f = sc / sqrtf(ss + p.eps_l2);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[t][e] *= f;
                 u32x4 hi, lo;
                 split8(y[t], hi, lo);
-                *reinterpret_cast<u32x4*>(dh + (r0 + t) * SQ + grp * 8) = hi;
-                *reinterpret_cast<u32x4*>(dl + (r0 + t) * SQ + grp * 8) = lo;
+                *reinterpret_cast<u32x4*>(dh + (qr0 + t) * SQ + qgrp * 8) = hi;
+                *reinterpret_cast<u32x4*>(dl + (qr0 + t) * SQ + qgrp * 8) = lo;
             }
         }
-    }
-    // ---- v^ (transposed into V^T [DV][ST]), zero token padding ----
-    {
-        constexpr int GPR = DV / 8;
-        for (int it = tid; it < (C / 4) * GPR; it += NT) {
-            const int grp = it % GPR, r0 = (it / GPR) * 4;
+        if (has_v) {
             float y[4][8];
-            conv8x4<BF16>(p, n, start, t0, r0, Lc, p.v, p.vs, h * DV + grp * 8,
-                          2 * qk + h * DV + grp * 8, Cc, y);
+            conv_rows<BF16>(rv, wv, vr0, Lc, y);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 uint16_t hi[4], lo[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) split_bf16(y[t][e], hi[t], lo[t]);
-                const int off = (grp * 8 + e) * ST + r0;
+                const int off = (vgrp * 8 + e) * ST + vr0;
                 *reinterpret_cast<uint2*>(sVTh + off) =
                     make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
                 *reinterpret_cast<uint2*>(sVTl + off) =
@@ -239,20 +297,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 sVTl[j * ST + s] = 0;
             }
         }
-    }
-    // ---- gates ----
-    if (tid < C) {
-        float g = 0.f, beta = 0.f;
-        if (tid < Lc) {
-            using A = Act<BF16>;
-            using T = typename A::T;
-            const float av = A::load(static_cast<const T*>(p.a) + (t0 + tid) * p.as + h);
-            const float bv = A::load(static_cast<const T*>(p.b) + (t0 + tid) * p.bs + h);
-            g = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
-            beta = sigmoid(bv);
+        // ---- gates ----
+        if (tid < C) {
+            float g = 0.f, beta = 0.f;
+            if (tid < Lc) {
+                g = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
+                beta = sigmoid(bv);
+            }
+            sg[tid] = g;
+            sbeta[tid] = beta;
         }
-        sg[tid] = g;
-        sbeta[tid] = beta;
     }
     __syncthreads();
     if (wave == 0) {
@@ -359,15 +413,26 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         *reinterpret_cast<u32x4*>(sKTl + i * ST + s0) = lo;
     }
     if (wave == 0 && lq < NB) {
-        // lane (block lq, column l16): x_r = delta_rc - sum_{s<r} A_rs x_s
+        // lane (block lq, column l16): x_r = delta_rc - sum_{s<r} A_rs x_s;
+        // row r+1 of the block is read while row r is computed
         const int b0 = lq * 16;
         float x[16];
+        f32x4 arow[4], anext[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) arow[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            if (r + 1 < 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    anext[q] = *reinterpret_cast<const f32x4*>(sGkk + (b0 + r + 1) * SG + b0 + 4 * q);
+            }
             float acc = (r == l16) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s) acc = fmaf(-sGkk[(b0 + r) * SG + b0 + s], x[s], acc);
+            for (int s = 0; s < r; ++s) acc = fmaf(-arow[s / 4][s % 4], x[s], acc);
             x[r] = acc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) arow[q] = anext[q];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sTm[(b0 + r) * SG + b0 + l16] = x[r];
