@@ -78,6 +78,25 @@ def decode_bytes_per_seq(Hk, Hv, dk, dv, act_bytes=2, out_bytes=4):
     return state + conv + tok + out, state
 
 
+def measured_traffic(key):
+    """HBM bytes per dispatch recorded in profiles/hbm_traffic.json for this
+    kernel, or None once the kernel sources differ from the ones measured."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_deltanet_linear_03_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != data.get("source_sha256"):
+        return None
+    k = data["kernels"].get(key)
+    return None if k is None else k["read_bytes"] + k["write_bytes"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,7 +204,7 @@ def main():
     roof = dict(rl[dominant])
     roof["kernel"] = dominant
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(f"prefill_4k/{dominant}")
     roof["avg_ms"] = kern_ms[dominant]
     del out, fs, cs, x
     torch.cuda.empty_cache()
@@ -285,7 +304,8 @@ def main():
                             "kernel_avg_ms": kms,
                             "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
-                                         "traffic": None, "bytes_per_seq_layer": per_seq}}
+                                         "traffic": measured_traffic("decode_b64/decode") if B == 64 else None,
+                                         "bytes_per_launch": B * per_seq}}
             log(f"decode B={B}: {ms:.3f} ms/step, state {state_gbs:.1f} GB/s, "
                 f"kernel {kms * 1e3:.1f} us = {kern_gbs:.1f} GB/s")
         result["decode"] = dec
