@@ -432,34 +432,56 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
 // epilogue: out = norm_w (.) o / sqrt(mean(o^2) + eps) (.) SiLU(z); one wave
 // per (token, value head) row, fixed-order reduction.
 // ---------------------------------------------------------------------------
+// DV/4 lanes per (token, head) row, 16-byte accesses, fixed-order reduction
+// over the row's lanes.
+template <int DV>
+struct EpiGeom {
+    static constexpr int LPR = DV / 4;                 // lanes per row
+    static constexpr int RPB = 256 / LPR;              // rows per 256-thread block
+    static_assert(DV % 4 == 0 && LPR <= kWave && kWave % LPR == 0, "row geometry");
+};
+
 template <int DV, bool BF16>
 __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
-    using A = Act<BF16>;
-    using T = typename A::T;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (row >= p.T * p.Hv) return;
-    const int64_t t = row / p.Hv;
-    const int h = static_cast<int>(row % p.Hv);
-    constexpr int PER = (DV + kWave - 1) / kWave;
-    float o[PER];
-    float ss = 0.f;
+    using G = EpiGeom<DV>;
+    const int lr = threadIdx.x % G::LPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * G::RPB + threadIdx.x / G::LPR;
+    const bool valid = row < p.T * p.Hv;
+    const int64_t rr = valid ? row : 0;
+    const int64_t t = rr / p.Hv;
+    const int h = static_cast<int>(rr % p.Hv);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.core + rr * DV + 4 * lr);
+    float z[4];
+    if constexpr (BF16) {
+        const uint2 zz = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.z) + t * p.zs + h * DV + 4 * lr);
+        z[0] = __uint_as_float(zz.x << 16);
+        z[1] = __uint_as_float(zz.x & 0xFFFF0000u);
+        z[2] = __uint_as_float(zz.y << 16);
+        z[3] = __uint_as_float(zz.y & 0xFFFF0000u);
+    } else {
+        const f32x4 zz = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.z) + t * p.zs + h * DV + 4 * lr);
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-        const int j = lane + kWave * m;
-        o[m] = (j < DV) ? p.core[row * DV + j] : 0.f;
-        ss = fmaf(o[m], o[m], ss);
+        for (int e = 0; e < 4; ++e) z[e] = zz[e];
     }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / DV + p.eps_rms);
+    const f32x4 w = *reinterpret_cast<const f32x4*>(p.norm_w + 4 * lr);
+    float ss = o[0] * o[0];
+    ss = fmaf(o[1], o[1], ss);
+    ss = fmaf(o[2], o[2], ss);
+    ss = fmaf(o[3], o[3], ss);
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-        const int j = lane + kWave * m;
-        if (j >= DV) continue;
-        const float zz = A::load(static_cast<const T*>(p.z) + t * p.zs + h * DV + j);
-        const float y = p.norm_w[j] * (o[m] * r) * silu(zz);
-        if (p.out_bf16) static_cast<uint16_t*>(p.out)[row * DV + j] = f32_to_bf16_bits(y);
-        else static_cast<float*>(p.out)[row * DV + j] = y;
+    for (int off = G::LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    const float r = 1.0f / sqrtf(ss / DV + p.eps_rms);
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = w[e] * (o[e] * r) * silu(z[e]);
+    if (!valid) return;
+    if (p.out_bf16) {
+        uint2 v;
+        v.x = f32_to_bf16_bits(y[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(y[1])) << 16);
+        v.y = f32_to_bf16_bits(y[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(y[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * DV + 4 * lr) = v;
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row * DV + 4 * lr) = f32x4{y[0], y[1], y[2], y[3]};
     }
 }
 
@@ -488,7 +510,8 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
     mark(3);
     if (p.T > 0) {
         const int64_t rows = p.T * p.Hv;
-        hipLaunchKernelGGL((epi_kernel<DV, BF16>), dim3(static_cast<unsigned>((rows + 3) / 4)),
+        constexpr int RPB = EpiGeom<DV>::RPB;
+        hipLaunchKernelGGL((epi_kernel<DV, BF16>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)),
                            dim3(256), 0, s, p);
     }
     mark(4);
