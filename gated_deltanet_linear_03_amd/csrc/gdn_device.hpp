@@ -1,12 +1,15 @@
 // gdn_device.hpp -- device helpers shared by the gfx950 Gated DeltaNet kernels.
 //
-// Matrix-core fragments (v_mfma_f32_16x16x32_bf16, one wave of 64 lanes):
-//   A operand, 16 rows x 32 k:  lane l holds row (l % 16), k = 8*(l/16) + e,
-//                               e = 0..7 (eight bf16, 16 bytes)
-//   B operand, 32 k x 16 cols:  lane l holds col (l % 16), k = 8*(l/16) + e
-//   C/D,      16 x 16 fp32:     lane l holds col (l % 16), rows 4*(l/16) + i,
-//                               i = 0..3
-// gdn_selftest_mfma checks this layout on the device.
+// Matrix-core fragments (one wave of 64 lanes):
+//   v_mfma_f32_16x16x32_bf16
+//     A operand, 16 rows x 32 k:  lane l holds row (l % 16), k = 8*(l/16) + e,
+//                                 e = 0..7 (eight bf16, 16 bytes)
+//     B operand, 32 k x 16 cols:  lane l holds col (l % 16), k = 8*(l/16) + e
+//   v_mfma_f32_16x16x16_bf16: the same with k = 4*(l/16) + e, e = 0..3
+//     (four bf16, 8 bytes), so its B operand is laid out like C/D below
+//   C/D,        16 x 16 fp32:     lane l holds col (l % 16), rows 4*(l/16) + i,
+//                                 i = 0..3
+// gdn_selftest_mfma checks both layouts on the device.
 //
 // Products run in split-bf16 form: x = hi + lo with hi = bf16(x) and
 // lo = bf16(x - hi), and a*b ~= a_hi*b_hi + a_hi*b_lo + a_lo*b_hi with fp32
@@ -23,6 +26,7 @@ namespace gdn {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -99,6 +103,27 @@ __device__ __forceinline__ f32x4 mfma3(u32x4 ahi, u32x4 alo, u32x4 bhi, u32x4 bl
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi), as_bf16x8(blo), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi), as_bf16x8(bhi), acc, 0, 0, 0);
     return acc;
+}
+
+// acc += (a_hi + a_lo) * (b_hi + b_lo) without the lo*lo term, on the
+// 16x16x16 shape (a, b: two dwords = four bf16 each).
+__device__ __forceinline__ f32x4 mfma3_k16(uint2 ahi, uint2 alo, uint2 bhi, uint2 blo, f32x4 acc) {
+    const s16x4 ah = __builtin_bit_cast(s16x4, ahi), al = __builtin_bit_cast(s16x4, alo);
+    const s16x4 bh = __builtin_bit_cast(s16x4, bhi), bl = __builtin_bit_cast(s16x4, blo);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    return acc;
+}
+
+// Split four floats into packed bf16 hi and lo words (element e in bits
+// 16*(e%2) of word e/2).
+__device__ __forceinline__ void split4(f32x4 x, uint2& hi, uint2& lo) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(x[e], h[e], l[e]);
+    hi = make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
+    lo = make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
 }
 
 // Pack 8 bf16 bit patterns (e = 0..7) into one 16-byte fragment register.

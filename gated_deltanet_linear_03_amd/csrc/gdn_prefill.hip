@@ -18,10 +18,11 @@
 //   plan_kernel   first chunk index of every sequence (chunks restart at each
 //                 sequence start, so results do not depend on the packing)
 //   prep_kernel   chunk-parallel over (chunk, value head): conv1d+SiLU, L2
-//                 norms, gates, Gram matrices, triangular inverse and the
-//                 per-chunk operands -W, Q_G = diag(e^gamma) Q, K_d^T, P, U~
-//                 written in matrix-core fragment order (split bf16 hi/lo);
-//                 see gdn_prep.hpp
+//                 norms, gates, Gram matrices, the diagonal blocks of
+//                 (I + A)^{-1} and a block forward substitution for W and U~;
+//                 writes the per-chunk operands -W, Q_G = diag(e^gamma) Q,
+//                 K_d^T, P, U~ in matrix-core fragment order (split bf16
+//                 hi/lo); see gdn_prep.hpp
 //   scan_kernel   sequential over the chunks of one (sequence, value head,
 //                 dv slice): U, O and H' on split-bf16 matrix-core products,
 //                 H kept in fp32 accumulators for the whole sequence; also
@@ -556,6 +557,24 @@ __global__ __launch_bounds__(64) void selftest_mfma_kernel(const float* A, const
     acc = mfma3(pack8(ah), pack8(al), pack8(bh), pack8(bl), acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) Cm[(4 * (l / 16) + i) * 16 + (l % 16)] = acc[i];
+    // the same product as two k = 16 halves on v_mfma_f32_16x16x16_bf16
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = 16 * half + 4 * (l / 16) + e;
+            a[e] = A[(l % 16) * 32 + k];
+            b[e] = B[k * 16 + (l % 16)];
+        }
+        uint2 a_h, a_l, b_h, b_l;
+        split4(a, a_h, a_l);
+        split4(b, b_h, b_l);
+        acc2 = mfma3_k16(a_h, a_l, b_h, b_l, acc2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Cm[256 + (4 * (l / 16) + i) * 16 + (l % 16)] = acc2[i];
 }
 
 hipError_t launch_selftest_mfma(const float* A, const float* B, float* Cm, hipStream_t s) {

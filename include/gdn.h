@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -167,10 +167,12 @@ const char* gdn_status_string(gdn_status status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* gdn_last_error(void);
 
-/* Library self-test of the matrix-core fragment layout the kernels rely on:
- * computes C[16][16] = A[16][32] * B[32][16] (row-major fp32 in/out, device
- * pointers) through one bf16 hi/lo split product on v_mfma_f32_16x16x32_bf16
- * and synchronises the stream.  Returns GDN_OK or GDN_ERR_HIP. */
+/* Library self-test of the matrix-core fragment layouts the kernels rely on:
+ * computes C = A[16][32] * B[32][16] twice through bf16 hi/lo split
+ * products, into C[0][16][16] on v_mfma_f32_16x16x32_bf16 and into
+ * C[1][16][16] on v_mfma_f32_16x16x16_bf16 (two k halves); row-major fp32
+ * in/out, device pointers (C holds 512 floats).  Synchronises the stream.
+ * Returns GDN_OK or GDN_ERR_HIP. */
 gdn_status gdn_selftest_mfma(const float* A, const float* B, float* C,
                              void* stream);
 
