@@ -167,25 +167,53 @@ def main():
                         workspace=ws, events=events)
 
     K, W = args.steps, args.warmup
-    for _ in range(W):
-        prefill_step(layer, x, cu, 1, T, out, fs, cs)
+    names = gdn.prefill_launches(layer, 1, T, nb)
+
+    def kernel_ms(evl, reps):
+        """Per-step time of each kernel kind (summed over its launches), and
+        the launch count of each kind per step."""
+        tot, cnt = {}, {}
+        for j, name in enumerate(names):
+            tot[name] = tot.get(name, 0.0) + sum(evl[i][j].elapsed_time(evl[i][j + 1])
+                                                 for i in range(reps)) / reps
+            cnt[name] = cnt.get(name, 0) + 1
+        return tot, cnt
+
+    # Rotate over NSET independent input sets (~100 MB each), so the 256 MiB
+    # Infinity Cache does not hold a step's inputs from an earlier step; set
+    # 0 is the seeded host-side case, the others device-side draws.
+    NSET = 5
+    gen_in = torch.Generator(device=dev)
+    gen_in.manual_seed(11)
+    sets = [x] + [gpu_inputs(T, gen_in) for _ in range(NSET - 1)]
+    for i in range(W):
+        prefill_step(layer, sets[i % NSET], cu, 1, T, out, fs, cs)
     torch.cuda.synchronize()
-    evs = [new_events(5) for _ in range(K)]
+    evs = [new_events(len(names) + 1) for _ in range(K)]
     e0, e1 = new_events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(K):
-        prefill_step(layer, x, cu, 1, T, out, fs, cs, events=evs[i])
+        prefill_step(layer, sets[i % NSET], cu, 1, T, out, fs, cs, events=evs[i])
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / K
-    kern_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
-               for j, name in enumerate(gdn.PREFILL_KERNELS)}
+    steps_ms = sorted(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K))
+    pct = lambda q: steps_ms[min(K - 1, int(round(q * (K - 1))))]
+    kern_ms, kern_n = kernel_ms(evs, K)
     tok_s = T / (ms_step * 1e-3)
-    log(f"prefill 4k: {ms_step:.3f} ms/step ({wall / K * 1e3:.3f} wall) {tok_s:.4g} tok/s "
-        f"kernels {kern_ms}")
+    log(f"prefill 4k: {ms_step:.3f} ms/step ({wall / K * 1e3:.3f} wall; median {pct(0.5):.3f}, "
+        f"p10 {pct(0.1):.3f}, p90 {pct(0.9):.3f}) {tok_s:.4g} tok/s kernels {kern_ms} launches {kern_n}")
+    # the same with one input set: Infinity-Cache-warm inputs (context only)
+    warm_ev = [new_events(len(names) + 1) for _ in range(K)]
+    for i in range(K):
+        prefill_step(layer, x, cu, 1, T, out, fs, cs, events=warm_ev[i])
+    torch.cuda.synchronize()
+    warm_ms = sum(warm_ev[i][0].elapsed_time(warm_ev[i][-1]) for i in range(K)) / K
+    log(f"prefill 4k, one input set (cache-warm): {warm_ms:.3f} ms/step")
+    del sets
 
     scan_f, prep_f = prefill_flops_per_token(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.chunk)
     epi_bytes = sh.Hv * sh.dv * (4 + 2 + 4)
@@ -205,7 +233,8 @@ def main():
     roof["kernel"] = dominant
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(f"prefill_4k/{dominant}")
-    roof["avg_ms"] = kern_ms[dominant]
+    roof["avg_ms"] = kern_ms[dominant] / kern_n[dominant]      # per launch
+    roof["launches_per_step"] = kern_n[dominant]
     del out, fs, cs, x
     torch.cuda.empty_cache()
 
@@ -220,6 +249,10 @@ def main():
                    "chunk": sh.chunk, "parallelism": "single GPU"},
         "roofline": roof,
         "prefill_kernels_ms": kern_ms,
+        "prefill_kernel_launches": kern_n,
+        "ms_per_step_median_p10_p90": [pct(0.5), pct(0.1), pct(0.9)],
+        "input_sets": NSET,
+        "ms_per_step_one_input_set": warm_ms,
         "prefill_kernel_roofline": {k: dict(v, frac=v["achieved"] / v["peak"]) for k, v in rl.items()},
         "prefill_alg_tflops": (scan_f + prep_f) * T / (ms_step * 1e-3) / 1e12,
     }
@@ -331,7 +364,8 @@ def main():
             ws = torch.empty(nonlocal_ws, dtype=torch.uint8, device=dev)
         prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0)
         torch.cuda.synchronize()
-        ev = [new_events(5) for _ in range(reps)]
+        lnames = gdn.prefill_launches(lay, NN, TT, ws.numel())
+        ev = [new_events(len(lnames) + 1) for _ in range(reps)]
         a0, a1 = new_events(2)
         a0.record(stream)
         for i in range(reps):
@@ -339,8 +373,9 @@ def main():
         a1.record(stream)
         torch.cuda.synchronize()
         ms = a0.elapsed_time(a1) / reps
-        km = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(reps)) / reps
-              for j, n in enumerate(gdn.PREFILL_KERNELS)}
+        km = {}
+        for j, n in enumerate(lnames):
+            km[n] = km.get(n, 0.0) + sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(reps)) / reps
         alg = (scan_f + prep_f) * TT / (ms * 1e-3) / 1e12
         r = {"N": NN, "T": TT, "ms": ms, "tokens_per_s": TT / (ms * 1e-3), "kernels_ms": km,
              "alg_tflops": alg, "alg_mfma_frac": alg / PEAK_BF16_TFLOPS,

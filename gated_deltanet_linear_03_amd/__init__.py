@@ -30,7 +30,7 @@ GDN_DTYPE_FP32 = 0
 GDN_DTYPE_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
-           "gdn_prefill_timed", "gdn_decode", "gdn_status_string",
+           "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_status_string",
            "gdn_last_error", "gdn_selftest_mfma")
 PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
 
@@ -99,6 +99,9 @@ def lib():
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_prefill_launches.restype = ctypes.c_int64
+        L.gdn_prefill_launches.argtypes = [ctypes.POINTER(CLayer), ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_size_t]
         L.gdn_prefill_timed.restype = ctypes.c_int
         L.gdn_prefill_timed.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -176,14 +179,27 @@ def prefill_workspace_bytes(layer: Layer, N: int, T_total: int) -> int:
     return int(n)
 
 
+def prefill_launches(layer: Layer, N: int, T_total: int, workspace_bytes: int | None = None):
+    """Names of the kernels gdn_prefill enqueues, in order, for these sizes
+    and workspace size (default: gdn_prefill_workspace_bytes): plan, then
+    prep and scan per window of chunks, then epi."""
+    if workspace_bytes is None:
+        workspace_bytes = prefill_workspace_bytes(layer, N, T_total)
+    cl = layer.c()
+    n = lib().gdn_prefill_launches(ctypes.byref(cl), int(N), int(T_total), int(workspace_bytes))
+    if n < 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return ["plan"] + ["prep", "scan"] * ((n - 2) // 2) + ["epi"]
+
+
 def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
                 out, core_out=None, initial_state=None, final_state=None,
                 conv_state_in=None, conv_state_out=None, workspace=None,
                 workspace_bytes=None, stream=None, events=None):
     """Call ``gdn_prefill`` on caller-provided buffers (no allocation).
-    events: optional list of 5 recorded torch.cuda.Event(enable_timing=True)
-    objects; the call then goes through ``gdn_prefill_timed`` and the event
-    pairs bracket the plan, prep, scan and epi kernels."""
+    events: optional list of len(prefill_launches(...)) + 1 recorded
+    torch.cuda.Event(enable_timing=True) objects; the call then goes through
+    ``gdn_prefill_timed`` and consecutive events bracket each kernel."""
     cl = layer.c()
     io = CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
                     _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),

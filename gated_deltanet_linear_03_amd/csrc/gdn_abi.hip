@@ -65,22 +65,35 @@ gdn_status check_layer(const gdn_layer* L, bool prefill) {
 }
 
 struct WsLayout {
-    int64_t max_chunks = 0;
-    int64_t off_chunk = 0, off_decay = 0, off_core = 0, off_vch = 0, total = 0;
+    int64_t max_chunks = 0, win_slots = 0;
+    int64_t off_chunk = 0, off_sink = 0, off_decay = 0, off_core = 0, off_carry = 0, off_vch = 0;
+    int64_t slot_bytes = 0, total = 0;
 };
 
-WsLayout ws_layout(const gdn_layer* L, int32_t N, int64_t T, bool need_core) {
+// Workspace: chunk table, store sink, per-chunk decays, the fp32 pre-norm
+// output when the caller gives no core_out, two state carry slots, and the
+// operand blocks of one window of win_slots chunk slots (win_slots = 0:
+// the default window).
+WsLayout ws_layout(const gdn_layer* L, int32_t N, int64_t T, bool need_core, int64_t win_slots) {
     WsLayout w;
-    w.max_chunks = (L->chunk > 0 ? T / L->chunk : 0) + N;
+    // sum_n ceil(L_n / C) <= (T + N (C - 1)) / C for every split of T into N lengths
+    w.max_chunks = L->chunk > 0 ? (T + static_cast<int64_t>(N) * (L->chunk - 1)) / L->chunk : N;
+    w.win_slots = win_slots > 0 ? win_slots
+                                : gdn::prefill_window_slots(L->dk, L->dv, L->chunk, L->Hv, N, w.max_chunks);
+    w.slot_bytes = static_cast<int64_t>(L->Hv) * gdn::vch_bytes(L->dk, L->dv, L->chunk);
     int64_t o = 0;
     w.off_chunk = o;
     o = round_up(o + 4 * (static_cast<int64_t>(N) + 1), 256);
+    w.off_sink = o;                       // 64 floats that absorb masked-off stores
+    o += 256;
     w.off_decay = o;
     o = round_up(o + 4 * w.max_chunks * L->Hv, 256);
     w.off_core = o;
     if (need_core) o = round_up(o + 4 * T * L->Hv * L->dv, 256);
+    w.off_carry = o;
+    o = round_up(o + 2ll * 4 * L->Hv * L->dk * L->dv, 256);
     w.off_vch = o;
-    o += w.max_chunks * L->Hv * gdn::vch_bytes(L->dk, L->dv, L->chunk);
+    o += w.win_slots * w.slot_bytes;
     w.total = round_up(o, 256);
     return w;
 }
@@ -114,7 +127,26 @@ size_t gdn_prefill_workspace_bytes(const gdn_layer* L, int32_t N, int64_t T) {
         return 0;
     }
     // sized for the case without a caller core_out (the larger one)
-    return static_cast<size_t>(ws_layout(L, N, T, true).total);
+    return static_cast<size_t>(ws_layout(L, N, T, true, 0).total);
+}
+
+// Window for the workspace the caller gave: the default one, or a smaller
+// one when the workspace holds fewer operand blocks (at least one slot).
+static gdn_status fit_workspace(const gdn_layer* L, int32_t N, int64_t T, bool need_core, const void* ws,
+                                size_t ws_bytes, WsLayout* out) {
+    WsLayout w = ws_layout(L, N, T, need_core, 0);
+    if (w.max_chunks > (int64_t(1) << 30)) return fail(GDN_ERR_INVALID_ARGUMENT, "too many chunks");
+    if (!ws) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (need %lld bytes)", static_cast<long long>(w.total));
+    if (!aligned(ws, 256)) return fail(GDN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < static_cast<size_t>(w.total)) {
+        const int64_t fits = (static_cast<int64_t>(ws_bytes) - w.off_vch) / w.slot_bytes;
+        if (fits < 1)
+            return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, need %lld (at least %lld)", ws_bytes,
+                        static_cast<long long>(w.total), static_cast<long long>(w.off_vch + w.slot_bytes));
+        w = ws_layout(L, N, T, need_core, fits);
+    }
+    *out = w;
+    return GDN_OK;
 }
 
 static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, void* ws,
@@ -169,13 +201,9 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
     if (io->core_out && static_cast<const void*>(io->out) == static_cast<const void*>(io->core_out) && T > 0)
         return fail(GDN_ERR_INVALID_ARGUMENT, "out and core_out must be different buffers");
 
-    const WsLayout w = ws_layout(L, N, T, io->core_out == nullptr);
-    if (!ws) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (need %lld bytes)", static_cast<long long>(w.total));
-    if (!aligned(ws, 256)) return fail(GDN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (ws_bytes < static_cast<size_t>(w.total))
-        return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, need %lld", ws_bytes,
-                    static_cast<long long>(w.total));
-    if (w.max_chunks > (int64_t(1) << 30)) return fail(GDN_ERR_INVALID_ARGUMENT, "too many chunks");
+    WsLayout w;
+    st = fit_workspace(L, N, T, io->core_out == nullptr, ws, ws_bytes, &w);
+    if (st != GDN_OK) return st;
 
     gdn::PrefillParams p{};
     p.N = N; p.Hk = Hk; p.Hv = Hv; p.G = Hv / Hk; p.T = T;
@@ -192,7 +220,10 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
     p.core = io->core_out ? io->core_out : reinterpret_cast<float*>(base + w.off_core);
     p.chunk_off = reinterpret_cast<int32_t*>(base + w.off_chunk);
     p.decay = reinterpret_cast<float*>(base + w.off_decay);
+    p.sink = reinterpret_cast<float*>(base + w.off_sink);
+    p.carry = reinterpret_cast<float*>(base + w.off_carry);
     p.vch = base + w.off_vch;
+    p.win_slots = static_cast<int>(w.win_slots);
 
     bool supported = false;
     hipError_t e = gdn::launch_prefill(dk, dv, L->chunk, L->act_dtype == GDN_DTYPE_BF16, p,
@@ -207,11 +238,32 @@ gdn_status gdn_prefill(const gdn_layer* L, const gdn_prefill_io* io, void* ws, s
     return prefill_impl(L, io, ws, ws_bytes, stream, nullptr);
 }
 
+int64_t gdn_prefill_launches(const gdn_layer* L, int32_t N, int64_t T, size_t ws_bytes) {
+    g_err[0] = 0;
+    if (check_layer(L, true) != GDN_OK) return -1;
+    if (N < 0 || T < 0) {
+        fail(GDN_ERR_INVALID_ARGUMENT, "N and T_total must be >= 0");
+        return -1;
+    }
+    // the fit does not depend on where the workspace is, only on its size
+    WsLayout w;
+    static const uint8_t probe[256] __attribute__((aligned(256))) = {0};
+    if (fit_workspace(L, N, T, true, probe, ws_bytes, &w) != GDN_OK) return -1;
+    return gdn::prefill_launches(w.max_chunks, w.win_slots);
+}
+
 gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void* ws,
                              size_t ws_bytes, void* stream, void* const* events, int n_events) {
     g_err[0] = 0;
-    if (!events || n_events != GDN_PREFILL_KERNELS + 1)
-        return fail(GDN_ERR_INVALID_ARGUMENT, "need %d timing events", GDN_PREFILL_KERNELS + 1);
+    gdn_status st = check_layer(L, true);
+    if (st != GDN_OK) return st;
+    if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
+    WsLayout w;
+    st = fit_workspace(L, io->N, io->T_total, io->core_out == nullptr, ws, ws_bytes, &w);
+    if (st != GDN_OK) return st;
+    const int64_t need = gdn::prefill_launches(w.max_chunks, w.win_slots) + 1;
+    if (!events || n_events != need)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "need %lld timing events", static_cast<long long>(need));
     for (int i = 0; i < n_events; ++i)
         if (!events[i]) return fail(GDN_ERR_INVALID_ARGUMENT, "timing event %d is NULL", i);
     return prefill_impl(L, io, ws, ws_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));

@@ -46,7 +46,13 @@ struct PrefillParams {
     // workspace views
     int32_t* chunk_off;                   // [N+1] first chunk of each sequence
     float* decay;                         // [max_chunks][Hv] exp(gamma_last)
-    uint8_t* vch;                         // [max_chunks][Hv] per-chunk operand blocks
+    float* sink;                          // [64] target of stores to rows past a sequence end
+    float* carry;                         // [2][Hv][dk][dv] state across a window boundary
+    uint8_t* vch;                         // [win_slots][Hv] per-chunk operand blocks of a window
+    // chunk-slot window [win_lo, win_hi) of one prep + scan pass (window
+    // win_idx of ceil(max_chunks / win_slots)); the operand blocks of a
+    // window are reused by the next one
+    int win_slots, win_lo, win_hi, win_idx;
 };
 
 // Bytes of the per-(chunk, value head) operand block for a compiled shape.
@@ -59,9 +65,32 @@ __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
          + 4ll * C * DV;       // U~   (fp32 accumulator fragments)
 }
 
+// Target size of one window's operand blocks.  One sequence: small enough
+// to stay in the 256 MiB Infinity Cache between the kernel that writes them
+// and the one that reads them.  Several sequences run their chunks
+// concurrently in one window (a window boundary would serialise them), up to
+// a cap that bounds the workspace.
+constexpr int64_t kPrefillWindowBytes = 144ll << 20;
+constexpr int64_t kPrefillBatchWindowBytes = 4ll << 30;
+
+// Chunk slots per window for a layer.
+inline int64_t prefill_window_slots(int DK, int DV, int C, int Hv, int N, int64_t max_chunks) {
+    const int64_t slot = static_cast<int64_t>(Hv) * vch_bytes(DK, DV, C);
+    int64_t w = (N > 1 ? kPrefillBatchWindowBytes : kPrefillWindowBytes) / slot;
+    const int64_t cap = max_chunks > 1 ? max_chunks : 1;
+    return w < 1 ? 1 : (w > cap ? cap : w);
+}
+
+// Kernel launches of one prefill: plan, (prep, scan) per window, epi.
+inline int64_t prefill_launches(int64_t max_chunks, int64_t win_slots) {
+    const int64_t nwin = max_chunks > win_slots ? (max_chunks + win_slots - 1) / win_slots : 1;
+    return 2 + 2 * nwin;
+}
+
 hipError_t launch_decode(int DK, int DV, bool bf16, const DecodeParams& p, hipStream_t s,
                          bool* supported);
-// events: NULL, or 5 events recorded before each of the 4 kernels and after the last
+// events: NULL, or prefill_launches() + 1 events: one before the first
+// kernel and one after each
 hipError_t launch_prefill(int DK, int DV, int C, bool bf16, const PrefillParams& p,
                           hipStream_t s, bool* supported, hipEvent_t const* events);
 bool prefill_shape_supported(int DK, int DV, int C);

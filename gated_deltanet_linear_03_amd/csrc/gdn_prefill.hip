@@ -126,6 +126,14 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     const int pair = (j / NS) * 8 + xcd;
     if (pair >= p.N * p.Hv) return;
     const int n = pair / p.Hv, h = pair % p.Hv;
+    // this window's chunks of sequence n; a sequence without chunks passes
+    // its states through in window 0
+    const int cb = p.chunk_off[n], ce = p.chunk_off[n + 1];
+    const bool no_chunks = cb == ce;
+    const int c_begin = max(cb, p.win_lo), c_end = min(ce, p.win_hi);
+    if (no_chunks ? p.win_idx != 0 : c_begin >= c_end) return;
+    const bool seq_first = no_chunks || c_begin == cb;   // the sequence starts in this window
+    const bool seq_last = no_chunks || c_end == ce;      // ... and ends in it
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
@@ -136,19 +144,27 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     for (int i = tid; i < DVS * US; i += 256) { UThi[i] = 0; UTlo[i] = 0; }
 
     // H slice in accumulator fragments: tile (mth = wave + NW*qh, nt).
+    // entering state: the caller's initial state where the sequence starts,
+    // else what the previous window left in the carry slot of its parity
     f32x4 hacc[QH][NTL];
     const size_t sbase = (static_cast<size_t>(n) * p.Hv + h) * DK * DV;
+    const size_t cbase = static_cast<size_t>(h) * DK * DV;
+    const size_t cslot = static_cast<size_t>(p.Hv) * DK * DV;
+    const float* hin = seq_first ? (p.state_in ? p.state_in + sbase : nullptr)
+                                 : p.carry + ((p.win_idx - 1) & 1) * cslot + cbase;
+    float* hout = seq_last ? (p.state_out ? p.state_out + sbase : nullptr)
+                           : p.carry + (p.win_idx & 1) * cslot + cbase;
 #pragma unroll
     for (int qh = 0; qh < QH; ++qh) {
         const int mth = wave + NW * qh;
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (mth < MTH && p.state_in) {
+            if (mth < MTH && hin) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = mth * 16 + lq * 4 + i;
-                    v[i] = p.state_in[sbase + static_cast<size_t>(row) * DV + col0 + nt * 16 + l16];
+                    v[i] = hin[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16];
                 }
             }
             hacc[qh][nt] = v;
@@ -175,7 +191,6 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     store_H_lds();
     __syncthreads();
 
-    const int c_begin = p.chunk_off[n], c_end = p.chunk_off[n + 1];
     const int64_t start = p.cu[n], end = p.cu[n + 1];
     static_assert(QU == 1, "one U/O row tile per wave");
     const int mt = wave;                     // this wave's chunk-row tile (if < MT)
@@ -193,7 +208,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
         float dec;
     };
     auto load_group = [&](Ops& o, int c, int grp) {
-        const uint8_t* blk = p.vch + (static_cast<int64_t>(c) * p.Hv + h) * L::bytes;
+        const uint8_t* blk = p.vch + (static_cast<int64_t>(c - p.win_lo) * p.Hv + h) * L::bytes;
         if (grp == 0) {
             o.dec = p.decay[static_cast<int64_t>(c) * p.Hv + h];
             if (has_u) {
@@ -243,7 +258,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     };
 
     auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
-        const int64_t t0 = start + static_cast<int64_t>(c - c_begin) * C;
+        const int64_t t0 = start + static_cast<int64_t>(c - cb) * C;
         const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
         f32x4 accu[NTL], acco[NTL];
         // (1) U = U~ - W H and O = Q_G H for this wave's chunk rows; the
@@ -348,13 +363,17 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
                     }
                 }
             }
+            // rows past the sequence end go to a sink, so that every lane
+            // issues the same stores (the memory counter the next chunk's
+            // operand waits rely on then counts them exactly)
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = mt * 16 + lq * 4 + i;
-                    if (r < Lc)
-                        p.core[((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16] = acco[nt][i];
+                    float* dst = r < Lc ? p.core + ((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16
+                                        : p.sink + lane;
+                    *dst = acco[nt][i];
                 }
             }
         }
@@ -366,6 +385,9 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) load_group(opA, c_begin, grp);
     }
+    // drain the memory counter once before the loop, so the loop's waits are
+    // set by its own steady-state load/store order (s_waitcnt vmcnt(0))
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     int c = c_begin;
     for (; c + 1 < c_end; c += 2) {
         step(opA, opB, c, c + 1);
@@ -373,8 +395,8 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     }
     if (c < c_end) step(opA, opB, c, c);
 
-    // final state
-    if (p.state_out) {
+    // leaving state
+    if (hout) {
 #pragma unroll
         for (int qh = 0; qh < QH; ++qh) {
             const int mth = wave + NW * qh;
@@ -384,8 +406,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = mth * 16 + lq * 4 + i;
-                    p.state_out[sbase + static_cast<size_t>(row) * DV + col0 + nt * 16 + l16] =
-                        hacc[qh][nt][i];
+                    hout[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16] = hacc[qh][nt][i];
                 }
         }
     }
@@ -393,7 +414,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     // Slice 0 of each value head owns its v channels, and head h % G == 0
     // also owns its key head's q and k channels; one thread per channel reads
     // all taps before writing, so conv_state_out may alias conv_state_in.
-    if (sl == 0 && p.conv_out) {
+    if (seq_last && sl == 0 && p.conv_out) {
         using A = Act<BF16>;
         using T = typename A::T;
         const int qk = p.Hk * DK;
@@ -494,28 +515,39 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
     auto mark = [&](int i) {
         if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
     };
-    mark(0);
+    int ev_i = 0;
+    mark(ev_i++);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.N, C, p.chunk_off);
-    mark(1);
-    if (p.max_chunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(p.max_chunks, p.Hv), dim3(kPrepThreads),
-                           0, s, p);
-    }
-    mark(2);
+    mark(ev_i++);
+    // windows of chunk slots: prep writes a window's operand blocks, scan
+    // consumes them while they are still cache-resident, then the next
+    // window reuses the blocks
+    const int W = p.win_slots;
+    const int nwin = static_cast<int>(prefill_launches(p.max_chunks, W) - 2) / 2;
     const int pairs = p.N * p.Hv;
-    if (pairs > 0) {
-        const int groups = (pairs + 7) / 8;
-        hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
-                           dim3(256), 0, s, p);
+    for (int w = 0; w < nwin; ++w) {
+        PrefillParams q = p;
+        q.win_idx = w;
+        q.win_lo = w * W;
+        q.win_hi = min(p.max_chunks, (w + 1) * W);
+        if (q.win_hi > q.win_lo)
+            hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(q.win_hi - q.win_lo, p.Hv),
+                               dim3(kPrepThreads), 0, s, q);
+        mark(ev_i++);
+        if (pairs > 0) {
+            const int groups = (pairs + 7) / 8;
+            hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
+                               dim3(256), 0, s, q);
+        }
+        mark(ev_i++);
     }
-    mark(3);
     if (p.T > 0) {
         const int64_t rows = p.T * p.Hv;
         constexpr int RPB = EpiGeom<DV>::RPB;
         hipLaunchKernelGGL((epi_kernel<DV, BF16>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)),
                            dim3(256), 0, s, p);
     }
-    mark(4);
+    mark(ev_i++);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // gdn_prep.hpp -- chunk-parallel operand kernel of the chunked prefill.
 //
-// One work-group (1024 threads, 16 waves) per (chunk slot, value head h).
+// One work-group (1024 threads, 16 waves) per (chunk slot, value head h) of
+// a window of chunk slots.
 // For the chunk's C tokens it computes, entirely on chip:
 //   q^, k^  conv1d(K=4) + SiLU + L2 norm of key head h/G (items of 4 tokens x
 //           8 channels: 16-byte loads, norms reduced across a row's lanes)
@@ -198,13 +199,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     float* sE = sgam + C;       // e^{gamma_r}
     float* sD = sE + C;         // e^{gamma_last - gamma_r}
 
-    const int slot = blockIdx.x;
+    const int slot = p.win_lo + blockIdx.x;
     const int h = blockIdx.y;
     const int hk = h / p.G;
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
-    const int total = p.chunk_off[p.N];
+    const int total = min(p.chunk_off[p.N], p.win_hi);
     if (slot >= total) return;
     const int n = seq_of_chunk(p.chunk_off, p.N, slot);
     const int64_t start = p.cu[n], end = p.cu[n + 1];
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
     const int qk = p.Hk * DK;
     const int Cc = 2 * qk + p.Hv * DV;
-    uint8_t* blk = p.vch + (static_cast<int64_t>(slot) * p.Hv + h) * L::bytes;
+    uint8_t* blk = p.vch + (static_cast<int64_t>(slot - p.win_lo) * p.Hv + h) * L::bytes;
 
     // ---- 1. conv inputs, then conv + SiLU (+ L2 norm for q, k), gates ----
     // The first NSW waves (dispatched first) stage the head's conv weights in

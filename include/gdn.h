@@ -73,9 +73,10 @@ typedef enum {
 
 typedef enum { GDN_DTYPE_FP32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
 
-/* Static description of one layer.  Compiled shapes (dk, dv, chunk):
- * (32, 32, 16), (32, 64, 16), (64, 64, 32), (128, 128, 64), (128, 128, 32);
- * conv_K = 4; act_dtype fp32 or bf16; out_dtype fp32 or bf16. */
+/* Static description of one layer.  Compiled shapes: prefill (dk, dv,
+ * chunk) = (128, 128, 64), (32, 32, 16), (32, 64, 16); decode (dk, dv) =
+ * (128, 128), (64, 64), (32, 32), (32, 64); conv_K = 4; act_dtype fp32 or
+ * bf16; out_dtype fp32 or bf16.  Other shapes return GDN_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t Hk, Hv;          /* key/query heads, value heads; Hv % Hk == 0 */
     int32_t dk, dv;          /* key and value head dims */
@@ -132,27 +133,40 @@ typedef struct {
 int gdn_abi_version(void);
 
 /* Bytes of device workspace gdn_prefill needs for N sequences holding
- * T_total tokens in all (an upper bound over every length split).  Returns
- * 0 and sets gdn_last_error() if the layer is invalid or unsupported. */
+ * T_total tokens in all (an upper bound over every length split).  It holds
+ * the chunk table, the fp32 pre-norm output (when no core_out is given),
+ * two recurrent-state carry slots and the per-chunk operand blocks of one
+ * window of chunks.  The prefill runs window by window: for one sequence
+ * the window is about 144 MiB of operand blocks (sized for the Infinity
+ * Cache), so the size grows with T_total only through the pre-norm output;
+ * for N > 1 the sequences share windows of up to 4 GiB (all of a batch's
+ * chunks at once, unless it is larger).  Returns 0 and sets
+ * gdn_last_error() if the layer is invalid or unsupported. */
 size_t gdn_prefill_workspace_bytes(const gdn_layer* layer, int32_t N,
                                    int64_t T_total);
 
-/* Enqueue the chunked prefill.  workspace: device memory of at least
- * gdn_prefill_workspace_bytes(layer, N, T_total) bytes, 256-byte aligned,
- * not shared with a concurrently running call. */
+/* Enqueue the chunked prefill.  workspace: device memory, 256-byte aligned,
+ * not shared with a concurrently running call, of
+ * gdn_prefill_workspace_bytes(layer, N, T_total) bytes; a smaller workspace
+ * is accepted down to the fixed parts plus one chunk slot of operand blocks
+ * and runs with correspondingly smaller windows (same results, more kernel
+ * launches).  GDN_ERR_WORKSPACE below that. */
 gdn_status gdn_prefill(const gdn_layer* layer, const gdn_prefill_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of kernels gdn_prefill enqueues, in order: plan (chunk table),
- * prep (chunk-parallel operands), scan (sequential state passing), epi
- * (gated RMSNorm). */
-#define GDN_PREFILL_KERNELS 4
+/* Number of kernels gdn_prefill enqueues for these sizes and this
+ * workspace size, in order: plan (chunk table), then per window prep
+ * (chunk-parallel operands) and scan (sequential state passing), then epi
+ * (gated RMSNorm): 2 + 2 * windows.  -1 on an invalid layer, sizes or a
+ * too small workspace (detail in gdn_last_error()). */
+int64_t gdn_prefill_launches(const gdn_layer* layer, int32_t N,
+                             int64_t T_total, size_t workspace_bytes);
 
 /* gdn_prefill that also records caller-created timing events (hipEvent_t
- * handles) on `stream`: events[i] just before kernel i and
- * events[GDN_PREFILL_KERNELS] after the last, so event pairs bracket each
- * kernel.  n_events must be GDN_PREFILL_KERNELS + 1.  Same results as
- * gdn_prefill; meant for per-kernel timing. */
+ * handles) on `stream`: events[0] before the first kernel and events[i]
+ * after kernel i-1 (numbering as in gdn_prefill_launches), so consecutive
+ * events bracket each kernel.  n_events must be gdn_prefill_launches() + 1.
+ * Same results as gdn_prefill; meant for per-kernel timing. */
 gdn_status gdn_prefill_timed(const gdn_layer* layer, const gdn_prefill_io* io,
                              void* workspace, size_t workspace_bytes,
                              void* stream, void* const* events, int n_events);

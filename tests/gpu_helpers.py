@@ -44,7 +44,28 @@ def dims(sh):
     return oracle.Dims(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, sh.scale, sh.eps_l2, sh.eps_rms)
 
 
-def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=False):
+def chunk_slot_bytes(Hv, dk, dv, C):
+    """Operand-block bytes of one chunk slot (all value heads): -W, Q_G,
+    K_d^T, P and U~ as split bf16 / fp32 fragments."""
+    CK = max(C, 32)
+    return Hv * (4 * C * dk * 2 + 4 * dk * CK + 4 * C * CK + 4 * C * dv)
+
+
+def workspace_for_window(layer, N, T, window_slots):
+    """Workspace bytes that make gdn_prefill run windows of window_slots
+    chunk slots (the default window is ~144 MiB of operand blocks for one
+    sequence, up to 4 GiB for several)."""
+    slot = chunk_slot_bytes(layer.Hv, layer.dk, layer.dv, layer.chunk)
+    full = gdn.prefill_workspace_bytes(layer, N, T)
+    target = (144 << 20) if N == 1 else (4 << 30)
+    default = min(max(1, target // slot), max((T + N * (layer.chunk - 1)) // layer.chunk, 1))
+    return full - (default - min(window_slots, default)) * slot
+
+
+def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=False,
+                window_slots=None):
+    """window_slots: run with a workspace that holds only this many chunk
+    slots of operand blocks (more, smaller windows); None = default."""
     sh = case.shape
     ad = act_dtype(sh)
     layer = make_layer(sh, case.params, out_dtype)
@@ -52,9 +73,14 @@ def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=Fal
     cu = to_dev(case.cu_seqlens)
     S0 = None if case.initial_state is None else to_dev(case.initial_state)
     C0 = None if case.conv_state is None else to_dev(case.conv_state, ad)
+    ws = None
+    if window_slots is not None:
+        N, T = len(case.cu_seqlens) - 1, int(case.cu_seqlens[-1])
+        ws = torch.empty(workspace_for_window(layer, N, T, window_slots), dtype=torch.uint8,
+                         device="cuda")
     res = gdn.prefill(layer, x["q"], x["k"], x["v"], x["z"], x["a"], x["b"], cu,
                       initial_state=S0, conv_state_in=C0, want_core=want_core,
-                      in_place=in_place)
+                      in_place=in_place, workspace=ws)
     torch.cuda.synchronize()
     return res
 

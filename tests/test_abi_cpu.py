@@ -190,10 +190,17 @@ def test_binding_marshals_to_the_abi_and_raises():
         gdn.prefill_raw(lay, workspace=None, **kw)
     assert ei.value.status == gdn.GDN_ERR_WORKSPACE
     with pytest.raises(gdn.GdnError) as ei:
-        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16), events=[_FakeEvent()] * 5, **kw)
-    assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT      # NULL event handles
+        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16), **kw)
+    assert ei.value.status == gdn.GDN_ERR_WORKSPACE              # too small
+    nb = gdn.prefill_workspace_bytes(lay, 1, 64)
+    ws = _FakeTensor(FAKE, numel=nb)
+    n_ev = len(gdn.prefill_launches(lay, 1, 64, nb)) + 1
     with pytest.raises(gdn.GdnError) as ei:
-        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16), events=[_FakeEvent()] * 3, **kw)
+        gdn.prefill_raw(lay, workspace=ws, events=[_FakeEvent()] * n_ev, **kw)
+    assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT      # NULL event handles
+    assert b"is NULL" in gdn.lib().gdn_last_error()
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.prefill_raw(lay, workspace=ws, events=[_FakeEvent()] * (n_ev - 1), **kw)
     assert b"timing events" in gdn.lib().gdn_last_error()
     with pytest.raises(gdn.GdnError):
         gdn.decode_raw(lay, B=2, q=t, k=t, v=_FakeTensor(FAKE, 32 * 128),
@@ -203,3 +210,32 @@ def test_binding_marshals_to_the_abi_and_raises():
                        conv_state_in=None, conv_state_out=_FakeTensor(FAKE),
                        stream=_FakeStream())
     assert gdn.prefill_workspace_bytes(lay, 1, 4096) > 0
+
+
+def test_prefill_windows_follow_the_workspace():
+    """The prefill runs window by window over the chunk slots: the default
+    workspace gives ~144 MiB windows at the 35B-A3B shape, a smaller one more
+    windows, down to one chunk slot; below that the call is refused."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    slot = 32 * (4 * 64 * 128 * 2 + 4 * 128 * 64 + 4 * 64 * 64 + 4 * 64 * 128)
+    T = 4096
+    nb = gdn.prefill_workspace_bytes(lay, 1, T)
+    names = gdn.prefill_launches(lay, 1, T, nb)
+    assert names[0] == "plan" and names[-1] == "epi"
+    assert names[1:-1] == ["prep", "scan"] * ((len(names) - 2) // 2)
+    win = (144 << 20) // slot                     # chunk slots per window
+    n_chunks = (T + 63) // 64                     # the bound the library plans for
+    assert len(names) == 2 + 2 * -(-n_chunks // win)
+    # workspace size independent of T beyond the pre-norm output
+    nb_long = gdn.prefill_workspace_bytes(lay, 1, 131072)
+    assert nb_long - nb == (131072 - T) * 32 * 128 * 4 + 4 * (131072 - T) // 64 * 32
+    # half the window: about twice the windows
+    half = len(gdn.prefill_launches(lay, 1, T, nb - (win - win // 2) * slot))
+    assert half == 2 + 2 * -(-n_chunks // (win // 2))
+    # the smallest workspace holds one slot: a window per chunk slot
+    floor = nb - (win - 1) * slot
+    assert len(gdn.prefill_launches(lay, 1, T, floor)) == 2 + 2 * n_chunks
+    with pytest.raises(gdn.GdnError):
+        gdn.prefill_launches(lay, 1, T, floor - 256)

@@ -44,6 +44,26 @@ def test_prefill_tiny_varlen_states():
     check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="tiny-varlen")
 
 
+@pytest.mark.parametrize("window_slots", [1, 2, 3])
+def test_prefill_windows_bitwise(window_slots):
+    """A workspace of 1-3 chunk slots makes the prefill run in many windows,
+    with the recurrent state crossing each window boundary through the carry
+    slots (here sequences of 3 chunks straddle two boundaries); results are
+    bit-identical to the default single window, and in-place states work
+    across windows."""
+    case = synth.prefill_case(synth.TINY, [37, 0, 27, 1, 16, 3, 2], seed=5,
+                              with_state=True, with_conv_state=True,
+                              norm_w_jitter=True)
+    ref = gpu_prefill(case)
+    got = gpu_prefill(case, window_slots=window_slots)
+    for key in ("out", "core_out", "final_state", "conv_state_out"):
+        assert torch.equal(ref[key], got[key]), key
+    inplace = gpu_prefill(case, window_slots=window_slots, in_place=True)
+    for key in ("out", "final_state", "conv_state_out"):
+        assert torch.equal(ref[key], inplace[key]), key
+    check_prefill(case, got, oracle_prefill(case), label=f"windows-{window_slots}")
+
+
 def test_prefill_dk_ne_dv():
     """dk = 32, dv = 64: a transposed state would not match."""
     sh = synth.LayerShape(Hk=2, Hv=4, dk=32, dv=64, chunk=16, act_dtype="bf16")
