@@ -24,9 +24,10 @@
 //                 K_d^T, P, U~ in matrix-core fragment order (split bf16
 //                 hi/lo); see gdn_prep.hpp
 //   scan_kernel   sequential over the chunks of one (sequence, value head,
-//                 dv slice): U, O and H' on split-bf16 matrix-core products,
-//                 H kept in fp32 accumulators for the whole sequence; also
-//                 writes the final state and the conv state tail
+//                 dv slice of 16 or 32 columns): U, O and H' on split-bf16
+//                 matrix-core products, H kept in fp32 accumulators for the
+//                 whole sequence; also writes the final state and the conv
+//                 state tail
 //   epi_kernel    token-parallel SiLU(z)-gated RMSNorm of o.
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
@@ -508,7 +509,26 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int C, int DVS, bool BF16>
+// Compute units of the current device (cached per device).
+static int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// The scan runs one work-group per compute unit (its registers admit one),
+// so it uses the narrow slice DVS when the (sequence, head, slice) groups
+// fit in one round over the compute units, else the wide one DVSW (less
+// operand traffic per column).  Each output column's arithmetic does not
+// depend on the slicing, so results are the same bits either way.
+template <int DK, int DV, int C, int DVS, int DVSW, bool BF16>
 static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
                                    hipEvent_t const* ev) {
     hipError_t e = hipSuccess;
@@ -536,8 +556,12 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
         mark(ev_i++);
         if (pairs > 0) {
             const int groups = (pairs + 7) / 8;
-            hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
-                               dim3(256), 0, s, q);
+            if (static_cast<int64_t>(groups) * 8 * (DV / DVS) <= compute_units())
+                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
+                                   dim3(256), 0, s, q);
+            else
+                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVSW, BF16>), dim3(groups * 8 * (DV / DVSW)),
+                                   dim3(256), 0, s, q);
         }
         mark(ev_i++);
     }
@@ -560,13 +584,13 @@ bool prefill_shape_supported(int DK, int DV, int C) {
 hipError_t launch_prefill(int DK, int DV, int C, bool bf16, const PrefillParams& p,
                           hipStream_t s, bool* supported, hipEvent_t const* events) {
     *supported = true;
-#define GDN_PF(dk, dv, c, dvs)                                                            \
+#define GDN_PF(dk, dv, c, dvs, dvsw)                                                      \
     if (DK == dk && DV == dv && C == c)                                                   \
-        return bf16 ? launch_prefill_t<dk, dv, c, dvs, true>(p, s, events)                \
-                    : launch_prefill_t<dk, dv, c, dvs, false>(p, s, events);
-    GDN_PF(128, 128, 64, 32)
-    GDN_PF(32, 32, 16, 32)
-    GDN_PF(32, 64, 16, 32)
+        return bf16 ? launch_prefill_t<dk, dv, c, dvs, dvsw, true>(p, s, events)          \
+                    : launch_prefill_t<dk, dv, c, dvs, dvsw, false>(p, s, events);
+    GDN_PF(128, 128, 64, 16, 32)
+    GDN_PF(32, 32, 16, 16, 32)
+    GDN_PF(32, 64, 16, 16, 32)
 #undef GDN_PF
     *supported = false;
     return hipSuccess;

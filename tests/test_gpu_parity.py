@@ -64,6 +64,28 @@ def test_prefill_windows_bitwise(window_slots):
     check_prefill(case, got, oracle_prefill(case), label=f"windows-{window_slots}")
 
 
+def test_prefill_wide_batch_bitwise_vs_alone():
+    """40 short sequences: the batch has more (sequence, head, slice) groups
+    than there are compute units, so its scan runs 32-column slices, while
+    a sequence alone runs 16-column ones; the bits must not change."""
+    lens = [int(v) for v in np.random.default_rng(41).integers(1, 50, 40)]
+    case = synth.prefill_case(synth.TINY, lens, seed=42, with_state=True,
+                              with_conv_state=True)
+    packed = gpu_prefill(case)
+    cu = case.cu_seqlens
+    for n in (0, 17, 39):
+        a, b = int(cu[n]), int(cu[n + 1])
+        alone = synth.PrefillCase(case.shape, np.array([0, b - a], dtype=np.int32),
+                                  {k: v[a:b] for k, v in case.inputs.items()}, case.params,
+                                  case.initial_state[n:n + 1], case.conv_state[n:n + 1])
+        r = gpu_prefill(alone)
+        for key in ("out", "core_out"):
+            assert torch.equal(r[key], packed[key][a:b]), (n, key)
+        assert torch.equal(r["final_state"][0], packed["final_state"][n]), n
+        assert torch.equal(r["conv_state_out"][0], packed["conv_state_out"][n]), n
+    check_prefill(case, packed, oracle_prefill(case), label="wide-batch")
+
+
 def test_prefill_dk_ne_dv():
     """dk = 32, dv = 64: a transposed state would not match."""
     sh = synth.LayerShape(Hk=2, Hv=4, dk=32, dv=64, chunk=16, act_dtype="bf16")
