@@ -48,6 +48,18 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The same for a pair (a in the low half-words, b in the high ones): one
+// packed conversion per word, six instructions per pair.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const f32x2 v = {a, b};
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - h, bf16x2));
+}
+
 // e^x for x <= 0 through the hardware 2^x (v_exp_f32); relative error about
 // |x| * 2^-24 + 2 ulp, used for in-chunk decay factors only.
 __device__ __forceinline__ float exp_neg(float x) {
@@ -119,11 +131,8 @@ __device__ __forceinline__ f32x4 mfma3_k16(uint2 ahi, uint2 alo, uint2 bhi, uint
 // Split four floats into packed bf16 hi and lo words (element e in bits
 // 16*(e%2) of word e/2).
 __device__ __forceinline__ void split4(f32x4 x, uint2& hi, uint2& lo) {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) split_bf16(x[e], h[e], l[e]);
-    hi = make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
-    lo = make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
 }
 
 // Pack 8 bf16 bit patterns (e = 0..7) into one 16-byte fragment register.

@@ -178,14 +178,11 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
             if (!ALL_H && mth >= MTH) continue;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                uint16_t hi[4], lo[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) split_bf16(hacc[qh][nt][i], hi[i], lo[i]);
+                uint2 hi, lo;
+                split4(hacc[qh][nt], hi, lo);
                 const int off = (nt * 16 + l16) * HS + mth * 16 + lq * 4;
-                *reinterpret_cast<uint2*>(&HThi[off]) =
-                    make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
-                *reinterpret_cast<uint2*>(&HTlo[off]) =
-                    make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
+                *reinterpret_cast<uint2*>(&HThi[off]) = hi;
+                *reinterpret_cast<uint2*>(&HTlo[off]) = lo;
             }
         }
     };
@@ -303,14 +300,11 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
             // (2) U^T into LDS (split).
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                uint16_t hi[4], lo[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) split_bf16(accu[nt][i], hi[i], lo[i]);
+                uint2 hi, lo;
+                split4(accu[nt], hi, lo);
                 const int off = (nt * 16 + l16) * US + mt * 16 + lq * 4;
-                *reinterpret_cast<uint2*>(&UThi[off]) =
-                    make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
-                *reinterpret_cast<uint2*>(&UTlo[off]) =
-                    make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
+                *reinterpret_cast<uint2*>(&UThi[off]) = hi;
+                *reinterpret_cast<uint2*>(&UTlo[off]) = lo;
             }
         }
         __syncthreads();

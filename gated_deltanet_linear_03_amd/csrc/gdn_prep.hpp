@@ -133,8 +133,15 @@ __device__ __forceinline__ void conv_rows(const RawRows<BF16>& raw, const f32x4*
             acc = fmaf(w[e][1], x[t + 1][e], acc);
             acc = fmaf(w[e][2], x[t + 2][e], acc);
             acc = fmaf(w[e][3], x[t + 3][e], acc);
-            y[t][e] = (r0 + t < valid) ? silu_fast(acc) : 0.f;
+            y[t][e] = silu_fast(acc);
         }
+    }
+    if (r0 + 4 > valid) {       // only the group that straddles the chunk's end
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (r0 + t >= valid) y[t][e] = 0.f;
     }
 }
 
@@ -149,11 +156,13 @@ __device__ __forceinline__ void unpack8(u32x4 hi, u32x4 lo, float* x) {
 }
 
 __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
-    uint16_t h[8], l[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(x[e], h[e], l[e]);
-    hi = pack8(h);
-    lo = pack8(l);
+    for (int e = 0; e < 4; ++e) {
+        uint32_t h, l;
+        split2(x[2 * e], x[2 * e + 1], h, l);
+        hi[e] = h;
+        lo[e] = l;
+    }
 }
 
 __device__ __forceinline__ void store_frag(uint8_t* tile, int lane, u32x4 hi, u32x4 lo) {
@@ -266,8 +275,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         } else if (kind < 3) {
             load_rows<BF16>(p, n, start, t0, r0, Lc, src, rs, col, c0, Cc, raw);
         }
-            __syncthreads();
-            if (kind < 3) {
+        __syncthreads();
+        if (kind < 3) {
             f32x4 w[8];
             const int wb = (kind == 0 ? 0 : (kind == 1 ? DK : 2 * DK)) + grp * 8;
 #pragma unroll
@@ -320,46 +329,40 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         }
     }
     __syncthreads();
-        // ---- 2. Gram matrices on the matrix cores (lower tiles), scaled on the
+
+    // ---- 2. Gram matrices on the matrix cores (lower tiles), scaled on the
     //         way out: A = strict_tril(beta_r e^{gamma_r - gamma_s} K^K^T) and
-    //         P = tril_incl(e^{gamma_r - gamma_s} Q^K^T).  Wave 0 takes the
-    //         diagonal tiles of K^K^T and goes straight on to the 16x16
-    //         diagonal blocks T_bb of Tm = (I + A)^{-1} (its own LDS writes
-    //         are visible to it in program order); the other waves take the
+    //         P = tril_incl(e^{gamma_r - gamma_s} Q^K^T).  Wave b < NB takes
+    //         diagonal tile b of K^K^T and goes straight on to the 16x16
+    //         diagonal block T_bb of Tm = (I + A)^{-1} (its own LDS writes are
+    //         visible to it in program order); the other waves take the
     //         remaining tiles, then the Q_G fragments. ----
-    if (wave == 0) {
+    static_assert(NB < NW, "a wave per diagonal block and some to spare");
+    if (wave < NB) {
         __builtin_amdgcn_s_setprio(2);
-        {   // the NB diagonal tiles of K K^T (A and B fragments coincide)
-            f32x4 acc[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int b0 = wave * 16;
+        {   // diagonal tile of K K^T (its A and B fragments coincide)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < DK / 32; ++kt) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int o = (b * 16 + l16) * SQ + kt * 32 + lq * 8;
-                    const u32x4 ah = lds16(sKh + o), al = lds16(sKl + o);
-                    acc[b] = mfma3(ah, al, ah, al, acc[b]);
-                }
+                const int o = (b0 + l16) * SQ + kt * 32 + lq * 8;
+                const u32x4 ah = lds16(sKh + o), al = lds16(sKl + o);
+                acc = mfma3(ah, al, ah, al, acc);
             }
+            const int s = b0 + l16;
+            const float gs = sgam[s];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int s = b * 16 + l16;
-                const float gs = sgam[s];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = b * 16 + lq * 4 + i;
-                    sAd[r * SD + l16] = (s < r) ? sbeta[r] * exp_neg(sgam[r] - gs) * acc[b][i] : 0.f;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int r = b0 + lq * 4 + i;
+                sAd[r * SD + l16] = (s < r) ? sbeta[r] * exp_neg(sgam[r] - gs) * acc[i] : 0.f;
             }
         }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lq < NB) {
-            // lane (block lq, column l16): x_r = delta_rc - sum_{s<r} A_rs x_s;
-            // row r+1 of the block is read while row r is computed
-            const int b0 = lq * 16;
+        if (lq == 0) {
+            // lane l16 (column): x_r = delta_rc - sum_{s<r} A_rs x_s; row r+1
+            // of the block is read while row r is computed
             float x[16];
             f32x4 arow[4], anext[4];
 #pragma unroll
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     } else {
         constexpr int NOFF = NB * (NB - 1) / 2;            // K K^T tiles below the diagonal
         constexpr int NTI = NB * (NB + 1) / 2;             // Q K^T lower tiles
-        for (int job = wave - 1; job < NOFF + NTI; job += NW - 1) {
+        for (int job = wave - NB; job < NOFF + NTI; job += NW - NB) {
             const bool isq = job >= NOFF;
             int idx = isq ? job - NOFF : job, mt, nt;
             if (isq) {
@@ -426,8 +429,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 }
             }
         }
-        const int t1 = tid - kWave;
-        constexpr int NT1 = NT - kWave;
+        const int t1 = tid - NB * kWave;
+        constexpr int NT1 = NT - NB * kWave;
         for (int sl = t1; sl < C * DK / 8; sl += NT1) {           // Q_G [C][DK]
             const int tile = sl / 64, ln = sl % 64;
             const int mt = tile / (DK / 32), kt = tile % (DK / 32);
@@ -443,7 +446,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         }
     }
     __syncthreads();
-        // ---- 3. [W | U~] = Tm [diag(beta e^gamma) K^ | diag(beta) V^] by block
+
+    // ---- 3. [W | U~] = Tm [diag(beta e^gamma) K^ | diag(beta) V^] by block
     //         forward substitution over the 16-token blocks,
     //             X_i = T_ii (B_i - sum_{j<i} A_ij X_j),
     //         one 16-column tile per wave on split-bf16 k = 16 matrix-core
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             }
         }
     }
-        for (int sl = tid; sl < C * CK / 8; sl += NT) {               // P [C][CK]
+    for (int sl = tid; sl < C * CK / 8; sl += NT) {               // P [C][CK]
         const int tile = sl / 64, ln = sl % 64;
         const int mt = tile / (CK / 32), kt = tile % (CK / 32);
         const int r = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         split8(x, hi, lo);
         store_frag(blk + L::P + tile * 2048, ln, hi, lo);
     }
-        for (int sl = tid; sl < DK * CK / 8; sl += NT) {              // K_d^T [DK][CK]
+    for (int sl = tid; sl < DK * CK / 8; sl += NT) {              // K_d^T [DK][CK]
         const int tile = sl / 64, ln = sl % 64;
         const int mt = tile / (CK / 32), kt = tile % (CK / 32);
         const int i = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
@@ -532,7 +536,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         store_frag(blk + L::KdT + tile * 2048, ln, hi, lo);
     }
     __syncthreads();
-        // ---- 4. -W out as A fragments ----
+
+    // ---- 4. -W out as A fragments ----
     for (int sl = tid; sl < C * DK / 8; sl += NT) {
         const int tile = sl / 64, ln = sl % 64;
         const int mt = tile / (DK / 32), kt = tile % (DK / 32);
