@@ -30,7 +30,8 @@ GDN_DTYPE_FP32 = 0
 GDN_DTYPE_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
-           "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_status_string",
+           "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
+           "gdn_status_string",
            "gdn_last_error", "gdn_selftest_mfma")
 PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
 
@@ -99,6 +100,9 @@ def lib():
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_decode_multi.restype = ctypes.c_int
+        L.gdn_decode_multi.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CDecodeIO),
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.gdn_prefill_launches.restype = ctypes.c_int64
         L.gdn_prefill_launches.argtypes = [ctypes.POINTER(CLayer), ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_size_t]
@@ -267,6 +271,51 @@ def decode_raw(layer: Layer, *, B, q, k, v, z, a, b, out, state_in, state_out,
                    _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
                    _ptr(core_out))
     _check(lib().gdn_decode(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
+
+
+MAX_VERIFY_TOKENS = 16
+
+
+def decode_multi_raw(layer: Layer, *, B, tokens, q, k, v, z, a, b, out, state_in, state_out,
+                     conv_state_in, conv_state_out, core_out=None, state_snapshots=None,
+                     stream=None):
+    """Call ``gdn_decode_multi``: `tokens` tokens for each of B sequences
+    (token tensors with B * tokens rows, sequence-major)."""
+    cl = layer.c()
+    io = CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
+                   _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
+                   _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
+                   _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
+                   _ptr(core_out))
+    _check(lib().gdn_decode_multi(ctypes.byref(cl), ctypes.byref(io), int(tokens),
+                                  _ptr(state_snapshots), _stream(stream)))
+
+
+def decode_multi(layer: Layer, q, k, v, z, a, b, state, conv_state, tokens, in_place=True,
+                 want_core=False, want_snapshots=False, stream=None):
+    """Multi-token verify: q, k [B*tokens, Hk, dk]; v, z [B*tokens, Hv, dv];
+    a, b [B*tokens, Hv]; state [B, Hv, dk, dv]; conv_state [B, 3, Cc].
+    Returns out (and core_out, per-token state snapshots [B, tokens, Hv, dk,
+    dv] if asked) plus the final states."""
+    import torch
+    dev = q.device
+    B = int(state.shape[0])
+    odt = torch.bfloat16 if layer.out_dtype == GDN_DTYPE_BF16 else torch.float32
+    out = torch.empty((B * tokens, layer.Hv, layer.dv), dtype=odt, device=dev)
+    core = torch.empty((B * tokens, layer.Hv, layer.dv), dtype=torch.float32, device=dev) if want_core else None
+    snap = (torch.empty((B, tokens, layer.Hv, layer.dk, layer.dv), dtype=torch.float32, device=dev)
+            if want_snapshots else None)
+    st_out = state if in_place else torch.empty_like(state)
+    cs_out = conv_state if in_place else torch.empty_like(conv_state)
+    decode_multi_raw(layer, B=B, tokens=tokens, q=q, k=k, v=v, z=z, a=a, b=b, out=out,
+                     state_in=state, state_out=st_out, conv_state_in=conv_state,
+                     conv_state_out=cs_out, core_out=core, state_snapshots=snap, stream=stream)
+    res = {"out": out, "final_state": st_out, "conv_state_out": cs_out}
+    if want_core:
+        res["core_out"] = core
+    if want_snapshots:
+        res["state_snapshots"] = snap
+    return res
 
 
 def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,

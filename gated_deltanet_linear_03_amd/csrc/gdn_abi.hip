@@ -269,8 +269,15 @@ gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void*
     return prefill_impl(L, io, ws, ws_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
-gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream) {
-    g_err[0] = 0;
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Ts = 0: one token per sequence (gdn_decode); Ts >= 1: the multi-token kernel.
+static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32_t Ts, float* snap,
+                              void* stream) {
     gdn_status st = check_layer(L, false);
     if (st != GDN_OK) return st;
     if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
@@ -303,8 +310,15 @@ gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream)
         return fail(GDN_ERR_INVALID_ARGUMENT, "state_out partially overlaps state_in");
     if (bad_alias(io->conv_state_in, conv_bytes, io->conv_state_out, conv_bytes))
         return fail(GDN_ERR_INVALID_ARGUMENT, "conv_state_out partially overlaps conv_state_in");
-    if (static_cast<int64_t>(B) * Hk >= (int64_t(1) << 31))
-        return fail(GDN_ERR_INVALID_ARGUMENT, "B * Hk too large");
+    if (static_cast<int64_t>(B) * Hk >= (int64_t(1) << 31) || static_cast<int64_t>(B) * Ts >= (int64_t(1) << 31))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "B * Hk or B * tokens too large");
+    if (snap) {
+        const size_t snap_bytes = size_t(B) * Ts * Hv * dk * dv * 4;
+        if (!aligned(snap, 16)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_snapshots must be 16-byte aligned");
+        if (overlaps(snap, snap_bytes, io->state_in, state_bytes) ||
+            overlaps(snap, snap_bytes, io->state_out, state_bytes))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "state_snapshots overlaps a state");
+    }
 
     gdn::DecodeParams p{};
     p.B = B; p.Hk = Hk; p.Hv = Hv; p.G = Hv / Hk;
@@ -315,12 +329,26 @@ gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream)
     p.state_in = io->state_in; p.state_out = io->state_out;
     p.conv_in = io->conv_state_in; p.conv_out = io->conv_state_out;
     p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16; p.core_out = io->core_out;
+    p.Ts = Ts; p.snap = snap;     // Ts = 0: the one-token kernel
     bool supported = false;
     hipError_t e = gdn::launch_decode(dk, dv, L->act_dtype == GDN_DTYPE_BF16, p,
                                       static_cast<hipStream_t>(stream), &supported);
     if (!supported) return fail(GDN_ERR_UNSUPPORTED, "decode shape not compiled");
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
+}
+
+gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream) {
+    g_err[0] = 0;
+    return decode_impl(L, io, 0, nullptr, stream);
+}
+
+gdn_status gdn_decode_multi(const gdn_layer* L, const gdn_decode_io* io, int32_t tokens,
+                            float* state_snapshots, void* stream) {
+    g_err[0] = 0;
+    if (tokens < 1 || tokens > gdn::kMaxVerifyTokens)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "tokens (%d) must be in [1, %d]", tokens, gdn::kMaxVerifyTokens);
+    return decode_impl(L, io, tokens, state_snapshots, stream);
 }
 
 gdn_status gdn_selftest_mfma(const float* A, const float* B, float* C, void* stream) {

@@ -20,6 +20,12 @@
 //
 // The work-group has 512 threads: each half streams one value head of the
 // group, so the two heads' state loads, arithmetic and stores overlap.
+//
+// The same kernel applies up to kMaxVerifyTokens tokens per sequence in one
+// launch (multi-token verify of speculative decoding): the state is read
+// once, updated token by token in registers with the one-token arithmetic,
+// optionally written after every token (snapshots for rollback) and written
+// once at the end.
 // Thread layout over H: DV/4 column groups (one float4 each) x RG row groups;
 // thread (rg, cg) holds a block of DK/RG consecutive rows.  Loads of one
 // instruction cover whole 512-byte rows, so the stream is fully coalesced.  Column sums over the row
@@ -266,10 +272,250 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-token verify: p.Ts <= TSM tokens per sequence.  The same work-group
+// layout and the same per-token arithmetic as the one-token kernel above, in
+// the same order, with the state held in registers between tokens, so the
+// result equals p.Ts single decode steps bit for bit.  The state is written
+// after every token to p.snap when given, and after the last one to
+// state_out.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool BF16, int TSM = kMaxVerifyTokens>
+__global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams p) {
+    using A = Act<BF16>;
+    using T = typename A::T;
+    constexpr int NT = kDecodeHalf;
+    constexpr int CG = DV / 4;          // float4 column groups
+    constexpr int RG = NT / CG;         // row groups
+    constexpr int RPT = DK / RG;        // rows per thread
+    static_assert(CG <= 64 && NT % CG == 0 && DK % RG == 0 && RPT >= 1, "shape");
+    static_assert(2 * DK <= kDecodeThreads, "one thread per q/k channel");
+
+    __shared__ float sq[TSM][DK], sk[TSM][DK], sv[2][TSM][DV], sz[2][TSM][DV];
+    __shared__ f32x4 red_k[2][RG][CG], red_q[2][RG][CG];
+    __shared__ float s_r[2][TSM], s_kq[TSM], s_eg[2][TSM], s_beta[2][TSM];
+
+    const int Ts = p.Ts;
+    const int b = blockIdx.x / p.Hk;
+    const int hk = blockIdx.x % p.Hk;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    // value head slot (uniform per wave, so the state base lives in SGPRs)
+    const int half = __builtin_amdgcn_readfirstlane(tid / NT);
+    const int t = tid % NT;
+    const int Cc = 2 * p.Hk * DK + p.Hv * DV;
+    const T* cin = static_cast<const T*>(p.conv_in);
+    T* cout = static_cast<T*>(p.conv_out);
+    const size_t crow = static_cast<size_t>(b) * 3 * Cc;
+    const int64_t row0 = static_cast<int64_t>(b) * Ts;   // the sequence's first token row
+
+    // thread (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 of columns 4cg..4cg+3;
+    // one load instruction still covers whole 512-byte rows.  The first pair
+    // of heads' state stream is issued before anything else so its latency
+    // overlaps the conv and the norms.
+    const int cg = t % CG, rg = t / CG;
+    const uint32_t toff = static_cast<uint32_t>(rg * RPT * DV + 4 * cg);
+    f32x4 H[RPT];
+    auto load_state = [&](int g0) {
+        const int g = g0 + half;
+        if (g < p.G && p.state_in) {
+            const float* sb = p.state_in + (static_cast<size_t>(b) * p.Hv + hk * p.G + g) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < RPT; ++m)
+                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sb + toff + m * DV));
+        } else {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    load_state(0);
+
+    // conv1d(K=4) + SiLU of channel c over the sequence's tokens: the window
+    // (w0, w1, w2) holds the three previous raw inputs (the conv state for the
+    // first token) and slides by one per token; the last window is the new
+    // conv state.  All of the channel's loads are issued before arithmetic.
+    auto conv_channel = [&](int c, const T* src, int64_t rs, float* y, int ystride) {
+        T xs[TSM];
+#pragma unroll
+        for (int s = 0; s < TSM; ++s)
+            if (s < Ts) xs[s] = src[(row0 + s) * rs];
+        T w0 = cin ? cin[crow + c] : T(0);
+        T w1 = cin ? cin[crow + Cc + c] : T(0);
+        T w2 = cin ? cin[crow + 2 * Cc + c] : T(0);
+        const f32x4 w = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c) * 4);
+#pragma unroll
+        for (int s = 0; s < TSM; ++s) {
+            if (s < Ts) {
+                float acc = w[0] * A::load(&w0);
+                acc = fmaf(w[1], A::load(&w1), acc);
+                acc = fmaf(w[2], A::load(&w2), acc);
+                acc = fmaf(w[3], A::load(&xs[s]), acc);
+                y[s * ystride] = silu(acc);
+                w0 = w1;
+                w1 = w2;
+                w2 = xs[s];
+            }
+        }
+        cout[crow + c] = w0;
+        cout[crow + Cc + c] = w1;
+        cout[crow + 2 * Cc + c] = w2;
+    };
+    // z and the gates of value head h (slot `slot`) for every token
+    auto head_inputs = [&](int h, int slot, int j, bool gate) {
+#pragma unroll
+        for (int s = 0; s < TSM; ++s)
+            if (s < Ts) sz[slot][s][j] = A::load(static_cast<const T*>(p.z) + (row0 + s) * p.zs + h * DV + j);
+        if (gate) {
+            float av[TSM], bv[TSM];
+#pragma unroll
+            for (int s = 0; s < TSM; ++s) {
+                if (s < Ts) {
+                    av[s] = A::load(static_cast<const T*>(p.a) + (row0 + s) * p.as + h);
+                    bv[s] = A::load(static_cast<const T*>(p.b) + (row0 + s) * p.bs + h);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < TSM; ++s) {
+                if (s < Ts) {
+                    const float gg = -expf(p.A_log[h]) * softplus(av[s] + p.dt_bias[h]);
+                    s_eg[slot][s] = expf(gg);
+                    s_beta[slot][s] = sigmoid(bv[s]);
+                }
+            }
+        }
+    };
+
+    // q and k: one conv channel per thread, threads [0, 2 DK)
+    if (tid < 2 * DK) {
+        const int isk = tid >= DK;
+        const int i = tid - isk * DK;
+        conv_channel(isk * p.Hk * DK + hk * DK + i,
+                     (isk ? static_cast<const T*>(p.k) : static_cast<const T*>(p.q)) + hk * DK + i,
+                     isk ? p.ks : p.qs, (isk ? &sk[0][0] : &sq[0][0]) + i, DK);
+    }
+    __syncthreads();
+    if (wave < 2) {
+        for (int s = 0; s < Ts; ++s) {
+            const float* src = wave == 0 ? sq[s] : sk[s];
+            float ss = 0.f;
+            for (int i = lane; i < DK; i += kWave) ss = fmaf(src[i], src[i], ss);
+            ss = wave_sum(ss);
+            if (lane == 0) s_r[wave][s] = (wave == 0 ? p.scale : 1.0f) / sqrtf(ss + p.eps_l2);
+        }
+    }
+    __syncthreads();
+    if (tid < 2 * DK) {
+        for (int s = 0; s < Ts; ++s) {
+            if (tid < DK) sq[s][tid] *= s_r[0][s];
+            else sk[s][tid - DK] *= s_r[1][s];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        for (int s = 0; s < Ts; ++s) {
+            float d = 0.f;
+            for (int i = lane; i < DK; i += kWave) d = fmaf(sk[s][i], sq[s][i], d);
+            d = wave_sum(d);
+            if (lane == 0) s_kq[s] = d;
+        }
+    }
+
+    for (int g0 = 0; g0 < p.G; g0 += 2) {
+        const int g = g0 + half;
+        const bool active = g < p.G;
+        const int h = hk * p.G + g;
+        const size_t hbase = (static_cast<size_t>(b) * p.Hv + h) * DK * DV;
+        if (g0 > 0) load_state(g0);
+        // conv + SiLU of this head's v channels, z and gates
+        if (active) {
+            for (int j = t; j < DV; j += NT) {
+                conv_channel(2 * p.Hk * DK + h * DV + j, static_cast<const T*>(p.v) + h * DV + j, p.vs,
+                             &sv[half][0][j], DV);
+                head_inputs(h, half, j, j == 0);
+            }
+        }
+        for (int s = 0; s < Ts; ++s) {
+            f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int i = rg * RPT + m;
+                const float kk = sk[s][i], qq = sq[s][i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    rk[e] = fmaf(H[m][e], kk, rk[e]);
+                    rq[e] = fmaf(H[m][e], qq, rq[e]);
+                }
+            }
+            red_k[half][rg][cg] = rk;
+            red_q[half][rg][cg] = rq;
+            __syncthreads();
+            if (active) {
+                f32x4 RK = red_k[half][0][cg], RQ = red_q[half][0][cg];
+#pragma unroll
+                for (int r = 1; r < RG; ++r) {
+                    f32x4 a = red_k[half][r][cg], c = red_q[half][r][cg];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { RK[e] += a[e]; RQ[e] += c[e]; }
+                }
+                const float eg = s_eg[half][s], beta = s_beta[half][s], kq = s_kq[s];
+                f32x4 u, o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    u[e] = beta * (sv[half][s][4 * cg + e] - eg * RK[e]);
+                    o[e] = fmaf(eg, RQ[e], kq * u[e]);
+                }
+                // H' = e^g H + k u^T: the last token's goes to state_out, each
+                // token's to its snapshot when asked for
+                float* so = (s == Ts - 1) ? p.state_out + hbase : nullptr;
+                float* sn = p.snap ? p.snap + ((row0 + s) * p.Hv + h) * DK * DV : nullptr;
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float kk = sk[s][rg * RPT + m];
+                    f32x4 hn;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hn[e] = fmaf(eg, H[m][e], kk * u[e]);
+                    if (s + 1 < Ts) H[m] = hn;       // (dead after the last token)
+                    if (so) __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(so + toff + m * DV));
+                    if (sn) __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(sn + toff + m * DV));
+                }
+                // z-gated RMSNorm over dv: row group 0 = lanes 0..CG-1 of the
+                // half's first wave.
+                if (t < kWave) {
+                    float ps = 0.f;
+                    if (t < CG) ps = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+                    ps = wave_sum(ps);
+                    if (t < CG) {
+                        const float r = 1.0f / sqrtf(ps / DV + p.eps_rms);
+                        const size_t obase = (static_cast<size_t>(row0 + s) * p.Hv + h) * DV + 4 * cg;
+                        float y[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            y[e] = p.norm_w[4 * cg + e] * (o[e] * r) * silu(sz[half][s][4 * cg + e]);
+                        if (p.out_bf16) {
+                            uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
+                        } else {
+                            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) =
+                                f32x4{y[0], y[1], y[2], y[3]};
+                        }
+                        if (p.core_out)
+                            *reinterpret_cast<f32x4*>(p.core_out + obase) = o;
+                    }
+                }
+            }
+            __syncthreads();   // red_* reused by the next token, sv/sz by the next pair
+        }
+    }
+}
+
 template <int DK, int DV, bool BF16>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.Hk));
-    hipLaunchKernelGGL((decode_kernel<DK, DV, BF16>), grid, dim3(kDecodeThreads), 0, s, p);
+    if (p.Ts == 0)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, BF16>), grid, dim3(kDecodeThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((verify_kernel<DK, DV, BF16>), grid, dim3(kDecodeThreads), 0, s, p);
     return hipGetLastError();
 }
 

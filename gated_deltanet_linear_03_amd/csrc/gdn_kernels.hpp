@@ -22,7 +22,11 @@ struct DecodeParams {
     void* out;
     int out_bf16;
     float* core_out;
+    int Ts;                              // 0: one token (decode); else tokens per sequence (rows b*Ts ..)
+    float* snap;                         // [B][Ts][Hv][dk][dv] state after each token, or NULL
 };
+
+constexpr int kMaxVerifyTokens = 16;     // tokens per sequence of one multi-token decode
 
 struct PrefillParams {
     int N, Hk, Hv, G;

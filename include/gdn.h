@@ -175,6 +175,28 @@ gdn_status gdn_prefill_timed(const gdn_layer* layer, const gdn_prefill_io* io,
 gdn_status gdn_decode(const gdn_layer* layer, const gdn_decode_io* io,
                       void* stream);
 
+/* Most tokens per sequence gdn_decode_multi takes. */
+#define GDN_MAX_VERIFY_TOKENS 16
+
+/* Several tokens per sequence against carried state, in order -- the
+ * multi-token verify step of speculative decoding (the pages' drafters
+ * propose short blocks: llmxabe README, the speculative-decoding notes).
+ * io is read as for gdn_decode except that the token tensors q, k, v, z,
+ * a, b and out / core_out hold B * tokens rows, sequence b's tokens at rows
+ * b * tokens .. b * tokens + tokens - 1 (token strides as in gdn_decode);
+ * the conv state advances by all the tokens.  The state is read once and
+ * updated token by token with the arithmetic of gdn_decode, so every output
+ * and state is bit-identical to `tokens` successive gdn_decode calls.
+ * state_snapshots: NULL, or device fp32 [B][tokens][Hv][dk][dv] receiving
+ * the state after each token (the last equals state_out), for rolling back
+ * to any accepted prefix; it must not overlap state_in or state_out.  (The
+ * conv state after an accepted prefix of k tokens is the last K-1 raw
+ * inputs of the old conv state followed by those k tokens, which the caller
+ * already holds.)  tokens in [1, GDN_MAX_VERIFY_TOKENS], else
+ * GDN_ERR_INVALID_ARGUMENT. */
+gdn_status gdn_decode_multi(const gdn_layer* layer, const gdn_decode_io* io,
+                            int32_t tokens, float* state_snapshots, void* stream);
+
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status status);
 

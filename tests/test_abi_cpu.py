@@ -239,3 +239,25 @@ def test_prefill_windows_follow_the_workspace():
     assert len(gdn.prefill_launches(lay, 1, T, floor)) == 2 + 2 * n_chunks
     with pytest.raises(gdn.GdnError):
         gdn.prefill_launches(lay, 1, T, floor - 256)
+
+
+def test_decode_multi_rejects_token_counts():
+    """gdn_decode_multi takes 1..GDN_MAX_VERIFY_TOKENS tokens per sequence and
+    refuses snapshot buffers that overlap a state (host-side checks)."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    t = _FakeTensor(FAKE, 16 * 128)
+    kw = dict(B=2, q=t, k=t, v=_FakeTensor(FAKE, 32 * 128), z=_FakeTensor(FAKE, 32 * 128),
+              a=_FakeTensor(FAKE, 32), b=_FakeTensor(FAKE, 32), out=_FakeTensor(FAKE + 4096),
+              state_in=_FakeTensor(FAKE + (1 << 24)), state_out=_FakeTensor(FAKE + (1 << 24)),
+              conv_state_in=None, conv_state_out=_FakeTensor(FAKE + (1 << 26)),
+              stream=_FakeStream())
+    for bad in (0, gdn.MAX_VERIFY_TOKENS + 1):
+        with pytest.raises(gdn.GdnError) as ei:
+            gdn.decode_multi_raw(lay, tokens=bad, **kw)
+        assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT
+        assert b"tokens" in gdn.lib().gdn_last_error()
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.decode_multi_raw(lay, tokens=4, state_snapshots=_FakeTensor(FAKE + (1 << 24) + 4096), **kw)
+    assert b"snapshots" in gdn.lib().gdn_last_error()
