@@ -339,10 +339,69 @@ def main():
                                          "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
                                          "traffic": measured_traffic("decode_b64/decode") if B == 64 else None,
                                          "bytes_per_launch": B * per_seq}}
-            log(f"decode B={B}: {ms:.3f} ms/step, state {state_gbs:.1f} GB/s, "
+            # the same 30-layer step replayed from a HIP graph (launch gaps
+            # removed; the states keep advancing exactly as eager steps do)
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                dstep()                       # warm the capture stream
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=cap):
+                    dstep()
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            g0, g1 = new_events(2)
+            g0.record(stream)
+            for i in range(K):
+                g.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            gms = g0.elapsed_time(g1) / K
+            dec[f"B{B}"]["graph_ms_per_step"] = gms
+            dec[f"B{B}"]["graph_state_GBps"] = L * B * state_per_seq / (gms * 1e-3) / 1e9
+            del g
+            log(f"decode B={B}: {ms:.3f} ms/step ({gms:.3f} from a graph), state {state_gbs:.1f} GB/s, "
                 f"kernel {kms * 1e3:.1f} us = {kern_gbs:.1f} GB/s")
         result["decode"] = dec
-        del layers, states, convs, toks
+
+        # multi-token verify: VB sequences x VT draft tokens x the same layers
+        VB, VT = 8, 4
+        vt = []
+        for l in range(L):
+            gen.manual_seed(2000 + l)
+            vt.append(gpu_inputs(VB * VT, gen))
+        vouts = [torch.empty((VB * VT, sh.Hv, sh.dv), dtype=torch.float32, device=dev) for _ in range(L)]
+
+        def vstep(events=None):
+            for l in range(L):
+                t = vt[l]
+                if events is not None:
+                    events[l][0].record(stream)
+                gdn.decode_multi_raw(layers[l], B=VB, tokens=VT, q=t["q"], k=t["k"], v=t["v"],
+                                     z=t["z"], a=t["a"], b=t["b"], out=vouts[l],
+                                     state_in=states[l][:VB], state_out=states[l][:VB],
+                                     conv_state_in=convs[l][:VB], conv_state_out=convs[l][:VB])
+                if events is not None:
+                    events[l][1].record(stream)
+        for _ in range(W):
+            vstep()
+        torch.cuda.synchronize()
+        vevs = [[new_events(2) for _ in range(L)] for _ in range(K)]
+        v0, v1 = new_events(2)
+        v0.record(stream)
+        for i in range(K):
+            vstep(vevs[i])
+        v1.record(stream)
+        torch.cuda.synchronize()
+        vms = v0.elapsed_time(v1) / K
+        vkms = sum(vevs[i][l][0].elapsed_time(vevs[i][l][1]) for i in range(K) for l in range(L)) / (K * L)
+        result["verify"] = {"B": VB, "tokens": VT, "layers": L, "ms_per_step": vms,
+                            "tokens_per_s": VB * VT / (vms * 1e-3),
+                            "kernel_avg_ms": vkms,
+                            "state_GBps": L * VB * state_per_seq / (vms * 1e-3) / 1e9}
+        log(f"verify B={VB} x {VT} tokens: {vms:.3f} ms/step, kernel {vkms * 1e3:.1f} us")
+        del layers, states, convs, toks, vt, vouts
         torch.cuda.empty_cache()
 
     # ---------------- long prefill, 1 x 131072 from a random state ----------------
