@@ -31,7 +31,7 @@ GDN_DTYPE_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
-           "gdn_status_string",
+           "gdn_step", "gdn_status_string",
            "gdn_last_error", "gdn_selftest_mfma")
 PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
 
@@ -69,7 +69,8 @@ class CPrefillIO(ctypes.Structure):
                  ("final_state", ctypes.c_void_p),
                  ("conv_state_in", ctypes.c_void_p),
                  ("conv_state_out", ctypes.c_void_p),
-                 ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p)])
+                 ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p),
+                 ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32)])
 
 
 class CDecodeIO(ctypes.Structure):
@@ -77,7 +78,8 @@ class CDecodeIO(ctypes.Structure):
                 [("state_in", ctypes.c_void_p), ("state_out", ctypes.c_void_p),
                  ("conv_state_in", ctypes.c_void_p),
                  ("conv_state_out", ctypes.c_void_p),
-                 ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p)])
+                 ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p),
+                 ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32)])
 
 
 _lib = None
@@ -100,6 +102,10 @@ def lib():
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_step.restype = ctypes.c_int
+        L.gdn_step.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
+                               ctypes.POINTER(CDecodeIO), ctypes.c_void_p, ctypes.c_size_t,
+                               ctypes.c_void_p]
         L.gdn_decode_multi.restype = ctypes.c_int
         L.gdn_decode_multi.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CDecodeIO),
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
@@ -196,21 +202,38 @@ def prefill_launches(layer: Layer, N: int, T_total: int, workspace_bytes: int | 
     return ["plan"] + ["prep", "scan"] * ((n - 2) // 2) + ["epi"]
 
 
+def _prefill_io(N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
+                final_state, conv_state_in, conv_state_out, state_slots, num_slots):
+    return CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
+                      _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
+                      _tok_stride(q), _tok_stride(k), _tok_stride(v),
+                      _tok_stride(z), _tok_stride(a), _tok_stride(b),
+                      _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
+                      _ptr(conv_state_out), _ptr(out), _ptr(core_out), _ptr(state_slots),
+                      int(num_slots))
+
+
+def _decode_io(B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
+               conv_state_out, state_slots, num_slots):
+    return CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
+                     _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
+                     _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
+                     _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
+                     _ptr(core_out), _ptr(state_slots), int(num_slots))
+
+
 def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
                 out, core_out=None, initial_state=None, final_state=None,
                 conv_state_in=None, conv_state_out=None, workspace=None,
-                workspace_bytes=None, stream=None, events=None):
+                workspace_bytes=None, stream=None, events=None, state_slots=None,
+                num_slots=0):
     """Call ``gdn_prefill`` on caller-provided buffers (no allocation).
     events: optional list of len(prefill_launches(...)) + 1 recorded
     torch.cuda.Event(enable_timing=True) objects; the call then goes through
     ``gdn_prefill_timed`` and consecutive events bracket each kernel."""
     cl = layer.c()
-    io = CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
-                    _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
-                    _tok_stride(q), _tok_stride(k), _tok_stride(v),
-                    _tok_stride(z), _tok_stride(a), _tok_stride(b),
-                    _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
-                    _ptr(conv_state_out), _ptr(out), _ptr(core_out))
+    io = _prefill_io(N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
+                     final_state, conv_state_in, conv_state_out, state_slots, num_slots)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if events is None:
@@ -262,15 +285,41 @@ def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,
 
 
 def decode_raw(layer: Layer, *, B, q, k, v, z, a, b, out, state_in, state_out,
-               conv_state_in, conv_state_out, core_out=None, stream=None):
-    """Call ``gdn_decode`` on caller-provided buffers (no allocation)."""
+               conv_state_in, conv_state_out, core_out=None, stream=None, state_slots=None,
+               num_slots=0):
+    """Call ``gdn_decode`` on caller-provided buffers (no allocation).  With
+    state_slots (device int32 [B]) the states are pools of num_slots entries."""
     cl = layer.c()
-    io = CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
-                   _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
-                   _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
-                   _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
-                   _ptr(core_out))
+    io = _decode_io(B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
+                    conv_state_out, state_slots, num_slots)
     _check(lib().gdn_decode(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
+
+
+def step_raw(layer: Layer, *, prefill=None, decode=None, workspace=None, workspace_bytes=None,
+             stream=None):
+    """Call ``gdn_step``: prefill and decode are dicts of the keyword
+    arguments prefill_raw / decode_raw take (buffers only), or None."""
+    cl = layer.c()
+    pio = dio = None
+    if prefill is not None:
+        f = dict(core_out=None, initial_state=None, final_state=None, conv_state_in=None,
+                 conv_state_out=None, state_slots=None, num_slots=0)
+        f.update(prefill)
+        pio = _prefill_io(f["N"], f["T_total"], f["cu_seqlens"], f["q"], f["k"], f["v"], f["z"],
+                          f["a"], f["b"], f["out"], f["core_out"], f["initial_state"],
+                          f["final_state"], f["conv_state_in"], f["conv_state_out"],
+                          f["state_slots"], f["num_slots"])
+    if decode is not None:
+        f = dict(core_out=None, state_slots=None, num_slots=0)
+        f.update(decode)
+        dio = _decode_io(f["B"], f["q"], f["k"], f["v"], f["z"], f["a"], f["b"], f["out"],
+                         f["core_out"], f["state_in"], f["state_out"], f["conv_state_in"],
+                         f["conv_state_out"], f["state_slots"], f["num_slots"])
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_step(ctypes.byref(cl), ctypes.byref(pio) if pio is not None else None,
+                          ctypes.byref(dio) if dio is not None else None, _ptr(workspace),
+                          int(workspace_bytes), _stream(stream)))
 
 
 MAX_VERIFY_TOKENS = 16
@@ -282,11 +331,8 @@ def decode_multi_raw(layer: Layer, *, B, tokens, q, k, v, z, a, b, out, state_in
     """Call ``gdn_decode_multi``: `tokens` tokens for each of B sequences
     (token tensors with B * tokens rows, sequence-major)."""
     cl = layer.c()
-    io = CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
-                   _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
-                   _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
-                   _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
-                   _ptr(core_out))
+    io = _decode_io(B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
+                    conv_state_out, None, 0)
     _check(lib().gdn_decode_multi(ctypes.byref(cl), ctypes.byref(io), int(tokens),
                                   _ptr(state_snapshots), _stream(stream)))
 

@@ -150,7 +150,8 @@ static gdn_status fit_workspace(const gdn_layer* L, int32_t N, int64_t T, bool n
 }
 
 static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, void* ws,
-                               size_t ws_bytes, void* stream, hipEvent_t const* events) {
+                               size_t ws_bytes, void* stream, hipEvent_t const* events,
+                               bool launch = true) {
     g_err[0] = 0;
     gdn_status st = check_layer(L, true);
     if (st != GDN_OK) return st;
@@ -182,9 +183,12 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
         return fail(GDN_ERR_INVALID_ARGUMENT, "a token stride is smaller than one token's row");
     if (qs % 8 || ks % 8 || vs % 8 || zs % 8)
         return fail(GDN_ERR_INVALID_ARGUMENT, "q/k/v/z strides must be multiples of 8 elements");
-    const size_t state_bytes = size_t(N) * Hv * dk * dv * 4;
+    if (io->state_slots && io->num_slots < N)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots (%d) < N (%d) with state_slots", io->num_slots, N);
+    const int64_t entries = io->state_slots ? io->num_slots : N;    // state pool size
+    const size_t state_bytes = size_t(entries) * Hv * dk * dv * 4;
     const int64_t Cc = 2ll * Hk * dk + int64_t(Hv) * dv;
-    const size_t conv_bytes = size_t(N) * 3 * Cc * es;
+    const size_t conv_bytes = size_t(entries) * 3 * Cc * es;
     if ((io->initial_state && !aligned(io->initial_state, 16)) || (io->final_state && !aligned(io->final_state, 16)))
         return fail(GDN_ERR_INVALID_ARGUMENT, "states must be 16-byte aligned");
     if ((io->conv_state_in && !aligned(io->conv_state_in, 16)) ||
@@ -218,12 +222,14 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
     p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16;
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.core = io->core_out ? io->core_out : reinterpret_cast<float*>(base + w.off_core);
+    p.slots = io->state_slots;
     p.chunk_off = reinterpret_cast<int32_t*>(base + w.off_chunk);
     p.decay = reinterpret_cast<float*>(base + w.off_decay);
     p.sink = reinterpret_cast<float*>(base + w.off_sink);
     p.carry = reinterpret_cast<float*>(base + w.off_carry);
     p.vch = base + w.off_vch;
     p.win_slots = static_cast<int>(w.win_slots);
+    if (!launch) return GDN_OK;
 
     bool supported = false;
     hipError_t e = gdn::launch_prefill(dk, dv, L->chunk, L->act_dtype == GDN_DTYPE_BF16, p,
@@ -277,7 +283,7 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 // Ts = 0: one token per sequence (gdn_decode); Ts >= 1: the multi-token kernel.
 static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32_t Ts, float* snap,
-                              void* stream) {
+                              void* stream, bool launch = true) {
     gdn_status st = check_layer(L, false);
     if (st != GDN_OK) return st;
     if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
@@ -303,9 +309,12 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
     if (qs < int64_t(Hk) * dk || ks < int64_t(Hk) * dk || vs < int64_t(Hv) * dv || zs < int64_t(Hv) * dv ||
         as < Hv || bs < Hv)
         return fail(GDN_ERR_INVALID_ARGUMENT, "a token stride is smaller than one token's row");
-    const size_t state_bytes = size_t(B) * Hv * dk * dv * 4;
+    if (io->state_slots && io->num_slots < B)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots (%d) < B (%d) with state_slots", io->num_slots, B);
+    const int64_t entries = io->state_slots ? io->num_slots : B;    // state pool size
+    const size_t state_bytes = size_t(entries) * Hv * dk * dv * 4;
     const int64_t Cc = 2ll * Hk * dk + int64_t(Hv) * dv;
-    const size_t conv_bytes = size_t(B) * 3 * Cc * es;
+    const size_t conv_bytes = size_t(entries) * 3 * Cc * es;
     if (bad_alias(io->state_in, state_bytes, io->state_out, state_bytes))
         return fail(GDN_ERR_INVALID_ARGUMENT, "state_out partially overlaps state_in");
     if (bad_alias(io->conv_state_in, conv_bytes, io->conv_state_out, conv_bytes))
@@ -330,6 +339,8 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
     p.conv_in = io->conv_state_in; p.conv_out = io->conv_state_out;
     p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16; p.core_out = io->core_out;
     p.Ts = Ts; p.snap = snap;     // Ts = 0: the one-token kernel
+    p.slots = io->state_slots;
+    if (!launch) return GDN_OK;
     bool supported = false;
     hipError_t e = gdn::launch_decode(dk, dv, L->act_dtype == GDN_DTYPE_BF16, p,
                                       static_cast<hipStream_t>(stream), &supported);
@@ -341,6 +352,19 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
 gdn_status gdn_decode(const gdn_layer* L, const gdn_decode_io* io, void* stream) {
     g_err[0] = 0;
     return decode_impl(L, io, 0, nullptr, stream);
+}
+
+gdn_status gdn_step(const gdn_layer* L, const gdn_prefill_io* prefill, const gdn_decode_io* decode,
+                    void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    const bool has_d = decode && decode->B > 0;
+    const bool has_p = prefill && (prefill->N > 0 || prefill->T_total > 0);
+    gdn_status st = GDN_OK;
+    if (has_d && (st = decode_impl(L, decode, 0, nullptr, stream, false)) != GDN_OK) return st;
+    if (has_p && (st = prefill_impl(L, prefill, ws, ws_bytes, stream, nullptr, false)) != GDN_OK) return st;
+    if (has_d && (st = decode_impl(L, decode, 0, nullptr, stream)) != GDN_OK) return st;
+    if (has_p && (st = prefill_impl(L, prefill, ws, ws_bytes, stream, nullptr)) != GDN_OK) return st;
+    return GDN_OK;
 }
 
 gdn_status gdn_decode_multi(const gdn_layer* L, const gdn_decode_io* io, int32_t tokens,

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
     const int Cc = 2 * p.Hk * DK + p.Hv * DV;
     const T* cin = static_cast<const T*>(p.conv_in);
     T* cout = static_cast<T*>(p.conv_out);
-    const size_t crow = static_cast<size_t>(b) * 3 * Cc;
+    const int sb = state_slot(p.slots, b);                // pool entry of the states
+    const size_t crow = static_cast<size_t>(sb) * 3 * Cc;
 
     // thread (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 of columns 4cg..4cg+3;
     // one load instruction still covers whole 512-byte rows.  The first pair
@@ -77,10 +78,10 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
     auto load_state = [&](int g0) {
         const int g = g0 + half;
         if (g < p.G && p.state_in) {
-            const float* sb = p.state_in + (static_cast<size_t>(b) * p.Hv + hk * p.G + g) * DK * DV;
+            const float* src = p.state_in + (static_cast<size_t>(sb) * p.Hv + hk * p.G + g) * DK * DV;
 #pragma unroll
             for (int m = 0; m < RPT; ++m)
-                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sb + toff + m * DV));
+                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + toff + m * DV));
         } else {
 #pragma unroll
             for (int m = 0; m < RPT; ++m) H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
         const int g = g0 + half;
         const bool active = g < p.G;
         const int h = hk * p.G + g;
-        const size_t hbase = (static_cast<size_t>(b) * p.Hv + h) * DK * DV;
+        const size_t hbase = (static_cast<size_t>(sb) * p.Hv + h) * DK * DV;
         if (g0 > 0) load_state(g0);
         // conv + SiLU of this head's v channels, gate inputs (the first pair
         // was done in the prologue).
@@ -306,7 +307,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
     const int Cc = 2 * p.Hk * DK + p.Hv * DV;
     const T* cin = static_cast<const T*>(p.conv_in);
     T* cout = static_cast<T*>(p.conv_out);
-    const size_t crow = static_cast<size_t>(b) * 3 * Cc;
+    const int sb = state_slot(p.slots, b);                // pool entry of the states
+    const size_t crow = static_cast<size_t>(sb) * 3 * Cc;
     const int64_t row0 = static_cast<int64_t>(b) * Ts;   // the sequence's first token row
 
     // thread (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 of columns 4cg..4cg+3;
@@ -319,10 +321,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
     auto load_state = [&](int g0) {
         const int g = g0 + half;
         if (g < p.G && p.state_in) {
-            const float* sb = p.state_in + (static_cast<size_t>(b) * p.Hv + hk * p.G + g) * DK * DV;
+            const float* src = p.state_in + (static_cast<size_t>(sb) * p.Hv + hk * p.G + g) * DK * DV;
 #pragma unroll
             for (int m = 0; m < RPT; ++m)
-                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sb + toff + m * DV));
+                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + toff + m * DV));
         } else {
 #pragma unroll
             for (int m = 0; m < RPT; ++m) H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
         const int g = g0 + half;
         const bool active = g < p.G;
         const int h = hk * p.G + g;
-        const size_t hbase = (static_cast<size_t>(b) * p.Hv + h) * DK * DV;
+        const size_t hbase = (static_cast<size_t>(sb) * p.Hv + h) * DK * DV;
         if (g0 > 0) load_state(g0);
         // conv + SiLU of this head's v channels, z and gates
         if (active) {

@@ -24,9 +24,13 @@ struct DecodeParams {
     float* core_out;
     int Ts;                              // 0: one token (decode); else tokens per sequence (rows b*Ts ..)
     float* snap;                         // [B][Ts][Hv][dk][dv] state after each token, or NULL
+    const int32_t* slots;                // [B] pool entry of each sequence's states, or NULL (entry b)
 };
 
 constexpr int kMaxVerifyTokens = 16;     // tokens per sequence of one multi-token decode
+
+// Pool entry holding sequence n's recurrent and conv state.
+__device__ __forceinline__ int state_slot(const int32_t* slots, int n) { return slots ? slots[n] : n; }
 
 struct PrefillParams {
     int N, Hk, Hv, G;
@@ -47,6 +51,7 @@ struct PrefillParams {
     void* out;
     int out_bf16;
     float* core;                          // o before the gated norm (user or workspace)
+    const int32_t* slots;                 // [N] pool entry of each sequence's states, or NULL (entry n)
     // workspace views
     int32_t* chunk_off;                   // [N+1] first chunk of each sequence
     float* decay;                         // [max_chunks][Hv] exp(gamma_last)

@@ -148,7 +148,8 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     // entering state: the caller's initial state where the sequence starts,
     // else what the previous window left in the carry slot of its parity
     f32x4 hacc[QH][NTL];
-    const size_t sbase = (static_cast<size_t>(n) * p.Hv + h) * DK * DV;
+    const int sn = state_slot(p.slots, n);                 // pool entry of the states
+    const size_t sbase = (static_cast<size_t>(sn) * p.Hv + h) * DK * DV;
     const size_t cbase = static_cast<size_t>(h) * DK * DV;
     const size_t cslot = static_cast<size_t>(p.Hv) * DK * DV;
     const float* hin = seq_first ? (p.state_in ? p.state_in + sbase : nullptr)
@@ -435,12 +436,12 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
                     v = base[src_off];
                 } else if (cin) {
                     const int64_t rr = 3 + (pos - start);
-                    v = cin[(static_cast<int64_t>(n) * 3 + rr) * Cc + cch];
+                    v = cin[(static_cast<int64_t>(sn) * 3 + rr) * Cc + cch];
                 }
                 vals[r] = v;
             }
 #pragma unroll
-            for (int r = 0; r < 3; ++r) cout[(static_cast<int64_t>(n) * 3 + r) * Cc + cch] = vals[r];
+            for (int r = 0; r < 3; ++r) cout[(static_cast<int64_t>(sn) * 3 + r) * Cc + cch] = vals[r];
         }
     }
 }

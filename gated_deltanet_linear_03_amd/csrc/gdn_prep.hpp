@@ -71,14 +71,15 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float* x) {
 
 // Raw input rows of one conv item: 8 channels [c0, c0+8) for the 7 token
 // positions r0-3 .. r0+3 of a chunk (chunk rows at or past `valid` and
-// history before the first conv-state row read as zeros).
+// history before the first conv-state row read as zeros); history before the
+// sequence start comes from conv-state entry `slot`.
 template <bool BF16>
 struct RawRows {
     u32x4 r[7][BF16 ? 1 : 2];
 };
 
 template <bool BF16>
-__device__ __forceinline__ void load_rows(const PrefillParams& p, int n, int64_t start, int64_t t0,
+__device__ __forceinline__ void load_rows(const PrefillParams& p, int slot, int64_t start, int64_t t0,
                                           int r0, int valid, const void* src, int64_t rs, int col,
                                           int c0, int Cc, RawRows<BF16>& raw) {
     using T = typename Act<BF16>::T;
@@ -93,7 +94,7 @@ __device__ __forceinline__ void load_rows(const PrefillParams& p, int n, int64_t
             q = reinterpret_cast<const u32x4*>(row + j * rs);
         } else if (rr < valid && p.conv_in && rr + hist >= -3) {
             q = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.conv_in) +
-                                               (static_cast<int64_t>(n) * 3 + 3 + rr + hist) * Cc + c0);
+                                               (static_cast<int64_t>(slot) * 3 + 3 + rr + hist) * Cc + c0);
         }
 #pragma unroll
         for (int w = 0; w < W; ++w) raw.r[j][w] = q ? q[w] : u32x4{0u, 0u, 0u, 0u};
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 if (i < NCW) sCw[i] = wst[u];
             }
         } else if (kind < 3) {
-            load_rows<BF16>(p, n, start, t0, r0, Lc, src, rs, col, c0, Cc, raw);
+            load_rows<BF16>(p, state_slot(p.slots, n), start, t0, r0, Lc, src, rs, col, c0, Cc, raw);
         }
         __syncthreads();
         if (kind < 3) {

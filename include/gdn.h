@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -112,6 +112,13 @@ typedef struct {
     void* conv_state_out;
     void* out;                     /* out_dtype */
     float* core_out;               /* optional */
+    /* optional state pool: device int32 [N], distinct entries in
+     * [0, num_slots); sequence n's recurrent and conv states are then entry
+     * state_slots[n] of initial_state / final_state ([num_slots][Hv][dk][dv])
+     * and of conv_state_in / conv_state_out ([num_slots][K-1][Cc]).  NULL:
+     * entry n, as without a pool (num_slots ignored). */
+    const int32_t* state_slots;
+    int32_t num_slots;
 } gdn_prefill_io;
 
 /* One token for each of B sequences.  state_out may equal state_in and
@@ -127,6 +134,8 @@ typedef struct {
     void* conv_state_out;                /* required */
     void* out;                           /* [B][Hv][dv], out_dtype */
     float* core_out;                     /* optional [B][Hv][dv] fp32 */
+    const int32_t* state_slots;          /* optional pool entries, as in gdn_prefill_io */
+    int32_t num_slots;
 } gdn_decode_io;
 
 /* Version of this header's structs and layouts. */
@@ -174,6 +183,17 @@ gdn_status gdn_prefill_timed(const gdn_layer* layer, const gdn_prefill_io* io,
 /* Enqueue one decode step (no workspace needed). */
 gdn_status gdn_decode(const gdn_layer* layer, const gdn_decode_io* io,
                       void* stream);
+
+/* One serving step of a layer over a state pool: the decode batch (one
+ * token per sequence; NULL or B = 0 for none) and the prefill batch (NULL or
+ * N = 0 for none), each as its own call describes, enqueued on `stream`
+ * decode first.  The two batches' sequences must use distinct pool entries
+ * (state_slots) when they share pools.  Both are validated before anything
+ * is enqueued.  workspace as for gdn_prefill (may be NULL without a prefill
+ * batch). */
+gdn_status gdn_step(const gdn_layer* layer, const gdn_prefill_io* prefill,
+                    const gdn_decode_io* decode, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Most tokens per sequence gdn_decode_multi takes. */
 #define GDN_MAX_VERIFY_TOKENS 16

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 2
+    assert L.gdn_abi_version() == 3
 
 
 def test_status_strings():
@@ -261,3 +261,36 @@ def test_decode_multi_rejects_token_counts():
     with pytest.raises(gdn.GdnError) as ei:
         gdn.decode_multi_raw(lay, tokens=4, state_snapshots=_FakeTensor(FAKE + (1 << 24) + 4096), **kw)
     assert b"snapshots" in gdn.lib().gdn_last_error()
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes structs have the sizes and field offsets a C compiler gives
+    the header's structs (a tiny C program compiled against include/gdn.h)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    checks = {"gdn_layer": (gdn.CLayer, ["Hk", "chunk", "scale", "conv_w", "norm_w"]),
+              "gdn_prefill_io": (gdn.CPrefillIO, ["N", "T_total", "cu_seqlens", "b_stride",
+                                                  "initial_state", "core_out", "state_slots",
+                                                  "num_slots"]),
+              "gdn_decode_io": (gdn.CDecodeIO, ["B", "q", "b_stride", "state_in", "core_out",
+                                                "state_slots", "num_slots"])}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gdn.h"', "int main(void) {"]
+    for name, (_, fields) in checks.items():
+        lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
+        for f in fields:
+            lines.append(f'  printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for name, (cls, fields) in checks.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for f in fields:
+            assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, (name, f)
