@@ -95,25 +95,37 @@ struct VchLayout {
 namespace gdn {
 
 // ---------------------------------------------------------------------------
-// scan: one work-group per (sequence, value head, dv slice of DVS columns).
+// scan: one work-group per (sequence, value head, dv slice of DVS columns),
+// eight waves in two roles around the slice's state, shared through LDS:
+//   state waves 0..3   U = U~ - W H for chunk-row tile `wave`, then
+//                      H' = e^{gamma_last} H + K_d^T U for the H row tiles
+//                      wave, wave + 4, ...  (registers, fp32)
+//   output waves 4..7  O = Q_G H + P U for chunk-row tile `wave - 4`
+// Per chunk:  [state: U -> LDS | output: Q_G H]  barrier
+//             [state: H' -> LDS | output: + P U, store O]  barrier.
+// Only the state waves are on the chunk-to-chunk chain; the output products,
+// their stores and their operand loads run beside it on the other wave of
+// each SIMD.
 // ---------------------------------------------------------------------------
+constexpr int kScanThreads = 512;
+
 template <int DK, int DV, int C, int DVS, bool BF16>
-__global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     using L = VchLayout<DK, DV, C>;
     constexpr int CK = L::CK;
-    constexpr int NW = 4;
+    constexpr int NW = 4;                 // waves per role
     constexpr int NS = DV / DVS;          // slices per head
     constexpr int NTL = DVS / 16;         // n tiles per slice
-    constexpr int MT = C / 16;            // U/O m tiles
-    constexpr int MTH = DK / 16;          // H m tiles
+    constexpr int MT = C / 16;            // U/O row tiles
+    constexpr int MTH = DK / 16;          // H row tiles
     constexpr int KTH = DK / 32;          // k steps over dk
     constexpr int KTC = CK / 32;          // k steps over the chunk
-    constexpr int QU = (MT + NW - 1) / NW;
     constexpr int QH = (MTH + NW - 1) / NW;
     constexpr int HS = DK + 8;            // LDS row stride (bf16) of H^T
     constexpr int US = CK + 8;            // LDS row stride (bf16) of U^T
-    constexpr bool ALL_H = (MTH % NW) == 0;   // every wave owns QH H row tiles
+    constexpr bool ALL_H = (MTH % NW) == 0;   // every state wave owns QH H row tiles
     static_assert(DV % DVS == 0 && DVS % 16 == 0 && DK % 32 == 0 && C % 16 == 0, "shape");
+    static_assert(MT <= NW, "one chunk-row tile per wave");
 
     __shared__ __align__(16) uint16_t HThi[DVS * HS], HTlo[DVS * HS];
     __shared__ __align__(16) uint16_t UThi[DVS * US], UTlo[DVS * US];
@@ -137,17 +149,19 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
     const bool seq_last = no_chunks || c_end == ce;      // ... and ends in it
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
     const int col0 = sl * DVS;
+    const bool out_role = wave >= NW;
+    const int mt = wave % NW;                 // chunk-row tile (U or O), if < MT
+    const bool has_row = (MT >= NW) || mt < MT;
 
     // zero U^T (including the padded chunk rows C..CK-1, never written later)
-    for (int i = tid; i < DVS * US; i += 256) { UThi[i] = 0; UTlo[i] = 0; }
+    for (int i = tid; i < DVS * US; i += kScanThreads) { UThi[i] = 0; UTlo[i] = 0; }
 
-    // H slice in accumulator fragments: tile (mth = wave + NW*qh, nt).
     // entering state: the caller's initial state where the sequence starts,
     // else what the previous window left in the carry slot of its parity
-    f32x4 hacc[QH][NTL];
     const int sn = state_slot(p.slots, n);                 // pool entry of the states
     const size_t sbase = (static_cast<size_t>(sn) * p.Hv + h) * DK * DV;
     const size_t cbase = static_cast<size_t>(h) * DK * DV;
@@ -156,22 +170,10 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
                                  : p.carry + ((p.win_idx - 1) & 1) * cslot + cbase;
     float* hout = seq_last ? (p.state_out ? p.state_out + sbase : nullptr)
                            : p.carry + (p.win_idx & 1) * cslot + cbase;
-#pragma unroll
-    for (int qh = 0; qh < QH; ++qh) {
-        const int mth = wave + NW * qh;
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (mth < MTH && hin) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = mth * 16 + lq * 4 + i;
-                    v[i] = hin[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16];
-                }
-            }
-            hacc[qh][nt] = v;
-        }
-    }
+
+    // H slice in accumulator fragments of the state waves: tile
+    // (mth = wave + NW*qh, nt)
+    f32x4 hacc[QH][NTL];
     auto store_H_lds = [&]() {
 #pragma unroll
         for (int qh = 0; qh < QH; ++qh) {
@@ -187,129 +189,41 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
             }
         }
     };
-    store_H_lds();
+    if (!out_role) {
+#pragma unroll
+        for (int qh = 0; qh < QH; ++qh) {
+            const int mth = wave + NW * qh;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (mth < MTH && hin) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = mth * 16 + lq * 4 + i;
+                        v[i] = hin[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16];
+                    }
+                }
+                hacc[qh][nt] = v;
+            }
+        }
+        store_H_lds();
+    }
     __syncthreads();
 
     const int64_t start = p.cu[n], end = p.cu[n + 1];
-    static_assert(QU == 1, "one U/O row tile per wave");
-    const int mt = wave;                     // this wave's chunk-row tile (if < MT)
-    // when every wave has a row tile / its H tiles, the role tests fold away
-    const bool has_u = (MT >= NW) || mt < MT;
-
-    // Software pipeline with two operand sets in registers (ping-pong): while
-    // chunk c computes from one set, chunk c+1's fragments load into the
-    // other, in four groups issued between chunk c's first matrix-core ops,
-    // so load issue overlaps arithmetic instead of stalling a phase.
-    struct Ops {
-        u32x4 w_h[KTH], w_l[KTH], q_h[KTH], q_l[KTH];
-        f32x4 ut[NTL];
-        u32x4 p_h[KTC], p_l[KTC], k_h[QH][KTC], k_l[QH][KTC];
-        float dec;
+    auto block_of = [&](int c) {
+        return p.vch + (static_cast<int64_t>(c - p.win_lo) * p.Hv + h) * L::bytes;
     };
-    auto load_group = [&](Ops& o, int c, int grp) {
-        const uint8_t* blk = p.vch + (static_cast<int64_t>(c - p.win_lo) * p.Hv + h) * L::bytes;
-        if (grp == 0) {
-            o.dec = p.decay[static_cast<int64_t>(c) * p.Hv + h];
-            if (has_u) {
-#pragma unroll
-                for (int kt = 0; kt < KTH; ++kt) {
-                    const uint8_t* tw = blk + L::negW + (mt * KTH + kt) * 2048;
-                    o.w_h[kt] = *reinterpret_cast<const u32x4*>(tw + lane * 16);
-                    o.w_l[kt] = *reinterpret_cast<const u32x4*>(tw + 1024 + lane * 16);
-                }
-            }
-        } else if (grp == 1) {
-            if (has_u) {
-#pragma unroll
-                for (int kt = 0; kt < KTH; ++kt) {
-                    const uint8_t* tq = blk + L::QG + (mt * KTH + kt) * 2048;
-                    o.q_h[kt] = *reinterpret_cast<const u32x4*>(tq + lane * 16);
-                    o.q_l[kt] = *reinterpret_cast<const u32x4*>(tq + 1024 + lane * 16);
-                }
-            }
-        } else if (grp == 2) {
-            if (has_u) {
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    const int tile = mt * (DV / 16) + sl * NTL + nt;
-                    o.ut[nt] = *reinterpret_cast<const f32x4*>(blk + L::Ut + tile * 1024 + lane * 16);
-                }
-#pragma unroll
-                for (int kt = 0; kt < KTC; ++kt) {
-                    const uint8_t* tp = blk + L::P + (mt * KTC + kt) * 2048;
-                    o.p_h[kt] = *reinterpret_cast<const u32x4*>(tp + lane * 16);
-                    o.p_l[kt] = *reinterpret_cast<const u32x4*>(tp + 1024 + lane * 16);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int qh = 0; qh < QH; ++qh) {
-                const int mth = wave + NW * qh;
-                if (!ALL_H && mth >= MTH) continue;
-#pragma unroll
-                for (int kt = 0; kt < KTC; ++kt) {
-                    const uint8_t* tk = blk + L::KdT + (mth * KTC + kt) * 2048;
-                    o.k_h[qh][kt] = *reinterpret_cast<const u32x4*>(tk + lane * 16);
-                    o.k_l[qh][kt] = *reinterpret_cast<const u32x4*>(tk + 1024 + lane * 16);
-                }
-            }
-        }
-    };
-
-    auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
-        const int64_t t0 = start + static_cast<int64_t>(c - cb) * C;
-        const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
-        f32x4 accu[NTL], acco[NTL];
-        // (1) U = U~ - W H and O = Q_G H for this wave's chunk rows; the
-        // three split terms go term-major over the independent accumulators
-        // so dependent matrix-core ops are not back to back.
+    // B fragments of H^T (k over dk) and of U^T (k over the chunk) from LDS
+    auto read_H = [&](int kt, u32x4* bh, u32x4* bl) {
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
-            accu[nt] = cur.ut[nt];
-            acco[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int off = (nt * 16 + l16) * HS + kt * 32 + lq * 8;
+            bh[nt] = *reinterpret_cast<const u32x4*>(&HThi[off]);
+            bl[nt] = *reinterpret_cast<const u32x4*>(&HTlo[off]);
         }
-#pragma unroll
-        for (int kt = 0; kt < KTH; ++kt) {
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp)
-                if (grp * KTH / 4 == kt) load_group(nxt, cn, grp);
-            if (!has_u) continue;
-            u32x4 bh[NTL], bl[NTL];
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                const int off = (nt * 16 + l16) * HS + kt * 32 + lq * 8;
-                bh[nt] = *reinterpret_cast<const u32x4*>(&HThi[off]);
-                bl[nt] = *reinterpret_cast<const u32x4*>(&HTlo[off]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                accu[nt] = mfma(cur.w_l[kt], bh[nt], accu[nt]);
-                acco[nt] = mfma(cur.q_l[kt], bh[nt], acco[nt]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                accu[nt] = mfma(cur.w_h[kt], bl[nt], accu[nt]);
-                acco[nt] = mfma(cur.q_h[kt], bl[nt], acco[nt]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                accu[nt] = mfma(cur.w_h[kt], bh[nt], accu[nt]);
-                acco[nt] = mfma(cur.q_h[kt], bh[nt], acco[nt]);
-            }
-        }
-        if (has_u) {
-            // (2) U^T into LDS (split).
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                uint2 hi, lo;
-                split4(accu[nt], hi, lo);
-                const int off = (nt * 16 + l16) * US + mt * 16 + lq * 4;
-                *reinterpret_cast<uint2*>(&UThi[off]) = hi;
-                *reinterpret_cast<uint2*>(&UTlo[off]) = lo;
-            }
-        }
-        __syncthreads();
-        u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
+    };
+    auto read_U = [&](u32x4 (*ubh)[NTL], u32x4 (*ubl)[NTL]) {
 #pragma unroll
         for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
@@ -318,94 +232,245 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
                 ubh[kt][nt] = *reinterpret_cast<const u32x4*>(&UThi[off]);
                 ubl[kt][nt] = *reinterpret_cast<const u32x4*>(&UTlo[off]);
             }
-        // (4) H' = e^{gamma_last} H + K_d^T U  (first: it is on the chain)
-#pragma unroll
-        for (int qh = 0; qh < QH; ++qh) {
-            if (!ALL_H && wave + NW * qh >= MTH) continue;
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hacc[qh][nt][i] *= cur.dec;
-        }
-#pragma unroll
-        for (int kt = 0; kt < KTC; ++kt) {
-#pragma unroll
-            for (int term = 0; term < 3; ++term) {
-#pragma unroll
-                for (int qh = 0; qh < QH; ++qh) {
-                    if (!ALL_H && wave + NW * qh >= MTH) continue;
+    };
+    auto frag = [&](const uint8_t* tile, u32x4& hi, u32x4& lo) {
+        hi = *reinterpret_cast<const u32x4*>(tile + lane * 16);
+        lo = *reinterpret_cast<const u32x4*>(tile + 1024 + lane * 16);
+    };
+
+    if (!out_role) {
+        // ---------------- state waves ----------------
+        // Two operand sets in registers (ping-pong): chunk c+1's fragments
+        // load while chunk c computes, W's per k step between the products,
+        // K_d^T's after the state update.
+        struct Ops {
+            u32x4 w_h[KTH], w_l[KTH];
+            f32x4 ut[NTL];
+            u32x4 k_h[QH][KTC], k_l[QH][KTC];
+            float dec;
+        };
+        auto load_w = [&](Ops& o, int c, int kt) {
+            const uint8_t* blk = block_of(c);
+            if (kt == 0) {
+                o.dec = p.decay[static_cast<int64_t>(c) * p.Hv + h];
+                if (has_row) {
 #pragma unroll
                     for (int nt = 0; nt < NTL; ++nt) {
-                        const u32x4 a = term == 1 ? cur.k_h[qh][kt] : (term == 0 ? cur.k_l[qh][kt] : cur.k_h[qh][kt]);
-                        const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
-                        hacc[qh][nt] = mfma(a, b, hacc[qh][nt]);
+                        const int tile = mt * (DV / 16) + sl * NTL + nt;
+                        o.ut[nt] = *reinterpret_cast<const f32x4*>(blk + L::Ut + tile * 1024 + lane * 16);
                     }
                 }
             }
-        }
-        // (5) H into LDS for the next chunk (all waves finished reading H in (1)).
-        store_H_lds();
-        if (has_u) {
-            // (3) O += P U, store valid rows.
+            if (has_row) frag(blk + L::negW + (mt * KTH + kt) * 2048, o.w_h[kt], o.w_l[kt]);
+        };
+        auto load_k = [&](Ops& o, int c) {
+            const uint8_t* blk = block_of(c);
+#pragma unroll
+            for (int qh = 0; qh < QH; ++qh) {
+                const int mth = wave + NW * qh;
+                if (!ALL_H && mth >= MTH) continue;
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt)
+                    frag(blk + L::KdT + (mth * KTC + kt) * 2048, o.k_h[qh][kt], o.k_l[qh][kt]);
+            }
+        };
+        auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
+            // (1) U = U~ - W H for this wave's chunk rows; even and odd k
+            // steps accumulate separately (two independent chains), the three
+            // split terms term-major within each
+            f32x4 a0[NTL], a1[NTL];
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                a0[nt] = cur.ut[nt];
+                a1[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int kt = 0; kt < KTH; ++kt) {
+                load_w(nxt, cn, kt);
+                if (!has_row) continue;
+                u32x4 bh[NTL], bl[NTL];
+                read_H(kt, bh, bl);
+                f32x4* a = (kt & 1) ? a1 : a0;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.w_l[kt], bh[nt], a[nt]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.w_h[kt], bl[nt], a[nt]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.w_h[kt], bh[nt], a[nt]);
+            }
+            if (has_row) {
+                // (2) U^T into LDS (split)
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    f32x4 u;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) u[i] = a0[nt][i] + a1[nt][i];
+                    uint2 hi, lo;
+                    split4(u, hi, lo);
+                    const int off = (nt * 16 + l16) * US + mt * 16 + lq * 4;
+                    *reinterpret_cast<uint2*>(&UThi[off]) = hi;
+                    *reinterpret_cast<uint2*>(&UTlo[off]) = lo;
+                }
+            }
+            __syncthreads();
+            // (3) H' = e^{gamma_last} H + K_d^T U
+            u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
+            read_U(ubh, ubl);
+#pragma unroll
+            for (int qh = 0; qh < QH; ++qh) {
+                if (!ALL_H && wave + NW * qh >= MTH) continue;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hacc[qh][nt][i] *= cur.dec;
+            }
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
 #pragma unroll
                 for (int term = 0; term < 3; ++term) {
 #pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) {
-                        const u32x4 a = term == 1 ? cur.p_h[kt] : (term == 0 ? cur.p_l[kt] : cur.p_h[kt]);
-                        const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
-                        acco[nt] = mfma(a, b, acco[nt]);
+                    for (int qh = 0; qh < QH; ++qh) {
+                        if (!ALL_H && wave + NW * qh >= MTH) continue;
+#pragma unroll
+                        for (int nt = 0; nt < NTL; ++nt) {
+                            const u32x4 a = term == 1 ? cur.k_h[qh][kt] : (term == 0 ? cur.k_l[qh][kt] : cur.k_h[qh][kt]);
+                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
+                            hacc[qh][nt] = mfma(a, b, hacc[qh][nt]);
+                        }
                     }
                 }
             }
-            // rows past the sequence end go to a sink, so that every lane
-            // issues the same stores (the memory counter the next chunk's
-            // operand waits rely on then counts them exactly)
+            // (4) H' into LDS for the next chunk (every wave read H in (1))
+            store_H_lds();
+            load_k(nxt, cn);
+            __syncthreads();
+        };
+
+        Ops opA, opB;
+        if (c_begin < c_end) {
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
+            for (int kt = 0; kt < KTH; ++kt) load_w(opA, c_begin, kt);
+            load_k(opA, c_begin);
+        }
+        // drain the memory counter once before the loop, so the loop's waits
+        // are set by its own steady-state load/store order
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
+            step(opA, opB, c, c + 1);
+            step(opB, opA, c + 1, (c + 2 < c_end) ? c + 2 : c + 1);
+        }
+        if (c < c_end) step(opA, opB, c, c);
+
+        // leaving state
+        if (hout) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = mt * 16 + lq * 4 + i;
-                    float* dst = r < Lc ? p.core + ((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16
-                                        : p.sink + lane;
-                    *dst = acco[nt][i];
-                }
+            for (int qh = 0; qh < QH; ++qh) {
+                const int mth = wave + NW * qh;
+                if (mth >= MTH) continue;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = mth * 16 + lq * 4 + i;
+                        hout[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16] = hacc[qh][nt][i];
+                    }
             }
         }
-        __syncthreads();
-    };
-
-    Ops opA, opB;
-    if (c_begin < c_end) {
+    } else {
+        // ---------------- output waves ----------------
+        struct Ops {
+            u32x4 q_h[KTH], q_l[KTH];
+            u32x4 p_h[KTC], p_l[KTC];
+        };
+        auto load_q = [&](Ops& o, int c, int kt) {
+            if (has_row) frag(block_of(c) + L::QG + (mt * KTH + kt) * 2048, o.q_h[kt], o.q_l[kt]);
+        };
+        auto load_p = [&](Ops& o, int c) {
+            if (!has_row) return;
+            const uint8_t* blk = block_of(c);
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) load_group(opA, c_begin, grp);
-    }
-    // drain the memory counter once before the loop, so the loop's waits are
-    // set by its own steady-state load/store order (s_waitcnt vmcnt(0))
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    int c = c_begin;
-    for (; c + 1 < c_end; c += 2) {
-        step(opA, opB, c, c + 1);
-        step(opB, opA, c + 1, (c + 2 < c_end) ? c + 2 : c + 1);
-    }
-    if (c < c_end) step(opA, opB, c, c);
-
-    // leaving state
-    if (hout) {
+            for (int kt = 0; kt < KTC; ++kt) frag(blk + L::P + (mt * KTC + kt) * 2048, o.p_h[kt], o.p_l[kt]);
+        };
+        auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
+            const int64_t t0 = start + static_cast<int64_t>(c - cb) * C;
+            const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
+            // (1) O = Q_G H (even / odd k steps apart, as for U)
+            f32x4 a0[NTL], a1[NTL];
 #pragma unroll
-        for (int qh = 0; qh < QH; ++qh) {
-            const int mth = wave + NW * qh;
-            if (mth >= MTH) continue;
+            for (int nt = 0; nt < NTL; ++nt) {
+                a0[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                a1[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
+            for (int kt = 0; kt < KTH; ++kt) {
+                load_q(nxt, cn, kt);
+                if (!has_row) continue;
+                u32x4 bh[NTL], bl[NTL];
+                read_H(kt, bh, bl);
+                f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = mth * 16 + lq * 4 + i;
-                    hout[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16] = hacc[qh][nt][i];
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.q_l[kt], bh[nt], a[nt]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.q_h[kt], bl[nt], a[nt]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.q_h[kt], bh[nt], a[nt]);
+            }
+            __syncthreads();
+            if (has_row) {
+                // (2) O += P U, store the valid rows
+                u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
+                read_U(ubh, ubl);
+                load_p(nxt, cn);
+                f32x4 acco[NTL];
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acco[nt][i] = a0[nt][i] + a1[nt][i];
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) {
+#pragma unroll
+                    for (int term = 0; term < 3; ++term) {
+#pragma unroll
+                        for (int nt = 0; nt < NTL; ++nt) {
+                            const u32x4 a = term == 1 ? cur.p_h[kt] : (term == 0 ? cur.p_l[kt] : cur.p_h[kt]);
+                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
+                            acco[nt] = mfma(a, b, acco[nt]);
+                        }
+                    }
                 }
+                // rows past the sequence end go to a sink, so that every lane
+                // issues the same stores (the memory counter the next chunk's
+                // operand waits rely on then counts them exactly)
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = mt * 16 + lq * 4 + i;
+                        float* dst = r < Lc ? p.core + ((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16
+                                            : p.sink + lane;
+                        *dst = acco[nt][i];
+                    }
+                }
+            }
+            __syncthreads();
+        };
+
+        Ops opA, opB;
+        if (c_begin < c_end) {
+#pragma unroll
+            for (int kt = 0; kt < KTH; ++kt) load_q(opA, c_begin, kt);
+            load_p(opA, c_begin);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
+            step(opA, opB, c, c + 1);
+            step(opB, opA, c + 1, (c + 2 < c_end) ? c + 2 : c + 1);
+        }
+        if (c < c_end) step(opA, opB, c, c);
     }
+
     // conv state tail: the last K-1 raw rows of (old conv state ++ inputs).
     // Slice 0 of each value head owns its v channels, and head h % G == 0
     // also owns its key head's q and k channels; one thread per channel reads
@@ -419,7 +484,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillParams p) {
         const int nch = DV + ((h % p.G == 0) ? 2 * DK : 0);
         T* cout = static_cast<T*>(p.conv_out);
         const T* cin = static_cast<const T*>(p.conv_in);
-        for (int e = tid; e < nch; e += 256) {
+        for (int e = tid; e < nch; e += kScanThreads) {
             int cch, src_kind, src_off;   // 0 q, 1 k, 2 v
             if (e < DV) { cch = 2 * qk + h * DV + e; src_kind = 2; src_off = h * DV + e; }
             else if (e < DV + DK) { cch = hk * DK + (e - DV); src_kind = 0; src_off = hk * DK + (e - DV); }
@@ -553,10 +618,10 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
             const int groups = (pairs + 7) / 8;
             if (static_cast<int64_t>(groups) * 8 * (DV / DVS) <= compute_units())
                 hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
-                                   dim3(256), 0, s, q);
+                                   dim3(kScanThreads), 0, s, q);
             else
                 hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVSW, BF16>), dim3(groups * 8 * (DV / DVSW)),
-                                   dim3(256), 0, s, q);
+                                   dim3(kScanThreads), 0, s, q);
         }
         mark(ev_i++);
     }
