@@ -1,22 +1,27 @@
 // gdn_device.hpp -- device helpers shared by the gfx950 Gated DeltaNet kernels.
 //
 // Matrix-core fragments (one wave of 64 lanes):
-//   v_mfma_f32_16x16x32_bf16
+//   v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x32_f16
 //     A operand, 16 rows x 32 k:  lane l holds row (l % 16), k = 8*(l/16) + e,
-//                                 e = 0..7 (eight bf16, 16 bytes)
+//                                 e = 0..7 (eight 16-bit values, 16 bytes)
 //     B operand, 32 k x 16 cols:  lane l holds col (l % 16), k = 8*(l/16) + e
 //   v_mfma_f32_16x16x16_bf16: the same with k = 4*(l/16) + e, e = 0..3
 //     (four bf16, 8 bytes), so its B operand is laid out like C/D below
 //   C/D,        16 x 16 fp32:     lane l holds col (l % 16), rows 4*(l/16) + i,
 //                                 i = 0..3
-// gdn_selftest_mfma checks both layouts on the device.
+// gdn_selftest_mfma checks these layouts on the device.
 //
-// Products run in split-bf16 form: x = hi + lo with hi = bf16(x) and
-// lo = bf16(x - hi), and a*b ~= a_hi*b_hi + a_hi*b_lo + a_lo*b_hi with fp32
-// accumulation (Henry, Tang, Heinecke, "Leveraging the bfloat16 Artificial
-// Intelligence Datatype For Higher-Precision Computations", ARITH 2019).  The
-// dropped a_lo*b_lo term and the rounding of lo leave ~2^-16 relative error
-// per product, against 2^-8 for a single bf16 rounding.
+// Two product precisions, both with fp32 accumulation:
+//  * split bf16 (inside a chunk): x = hi + lo with hi = bf16(x) and
+//    lo = bf16(x - hi), and a*b ~= a_hi*b_hi + a_hi*b_lo + a_lo*b_hi (Henry,
+//    Tang, Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype
+//    For Higher-Precision Computations", ARITH 2019).  The dropped a_lo*b_lo
+//    term and the rounding of lo leave ~2^-16 relative error per product,
+//    against 2^-8 for a single bf16 rounding.
+//  * single fp16 (between chunks, in the scan): both operands rounded once to
+//    fp16 (2^-11 relative), one product.  The rounding does not compound
+//    along the sequence: the state itself stays in fp32 accumulators and
+//    only its operand copy is rounded, afresh at every chunk.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,6 +32,8 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -58,6 +65,22 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
     hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
     const f32x2 h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u)};
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - h, bf16x2));
+}
+
+// Two floats to packed fp16, round to nearest even (v_cvt_pk_f16_f32); a in
+// the low half-word.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+__device__ __forceinline__ uint2 pack4_f16(f32x4 x) {
+    return uint2{pack_f16(x[0], x[1]), pack_f16(x[2], x[3])};
+}
+
+__device__ __forceinline__ u32x4 pack8_f16(const float* x) {
+    return u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]),
+                 pack_f16(x[6], x[7])};
 }
 
 // e^x for x <= 0 through the hardware 2^x (v_exp_f32); relative error about
@@ -106,6 +129,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+}
+
+// acc += a * b on fp16 fragments (eight fp16 per 16-byte register).
+__device__ __forceinline__ f32x4 mfma_h(u32x4 a, u32x4 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
 }
 
 // acc += (a_hi + a_lo) * (b_hi + b_lo) without the lo*lo term.

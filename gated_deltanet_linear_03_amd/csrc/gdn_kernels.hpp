@@ -64,14 +64,15 @@ struct PrefillParams {
     int win_slots, win_lo, win_hi, win_idx;
 };
 
-// Bytes of the per-(chunk, value head) operand block for a compiled shape.
+// Bytes of the per-(chunk, value head) operand block for a compiled shape:
+// the scan's matrix-core operands as fp16 fragments, U~ as fp32 fragments.
 __host__ __device__ constexpr int ck_pad(int C) { return C < 32 ? 32 : C; }
 __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
-    return 4ll * C * DK        // -W   (A fragments, hi+lo bf16)
-         + 4ll * C * DK        // Q_G  (A fragments)
-         + 4ll * DK * ck_pad(C)  // K_d^T (A fragments)
-         + 4ll * C * ck_pad(C)   // P    (A fragments)
-         + 4ll * C * DV;       // U~   (fp32 accumulator fragments)
+    return 2ll * C * DK          // -W    (A fragments)
+         + 2ll * C * DK          // Q_G   (A fragments)
+         + 2ll * DK * ck_pad(C)  // K_d^T (A fragments)
+         + 2ll * C * ck_pad(C)   // P     (A fragments)
+         + 4ll * C * DV;         // U~    (fp32 accumulator fragments)
 }
 
 // Target size of one window's operand blocks.  One sequence: small enough
@@ -82,12 +83,15 @@ __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
 constexpr int64_t kPrefillWindowBytes = 144ll << 20;
 constexpr int64_t kPrefillBatchWindowBytes = 4ll << 30;
 
-// Chunk slots per window for a layer.
+// Chunk slots per window for a layer: as many as the target size allows,
+// then evened out over the windows that takes.
 inline int64_t prefill_window_slots(int DK, int DV, int C, int Hv, int N, int64_t max_chunks) {
     const int64_t slot = static_cast<int64_t>(Hv) * vch_bytes(DK, DV, C);
     int64_t w = (N > 1 ? kPrefillBatchWindowBytes : kPrefillWindowBytes) / slot;
     const int64_t cap = max_chunks > 1 ? max_chunks : 1;
-    return w < 1 ? 1 : (w > cap ? cap : w);
+    w = w < 1 ? 1 : (w > cap ? cap : w);
+    const int64_t nwin = (cap + w - 1) / w;
+    return (cap + nwin - 1) / nwin;
 }
 
 // Kernel launches of one prefill: plan, (prep, scan) per window, epi.

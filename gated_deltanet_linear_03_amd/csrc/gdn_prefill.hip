@@ -76,14 +76,17 @@ __device__ __forceinline__ int seq_of_chunk(const int32_t* chunk_off, int N, int
 }
 
 // Byte offsets of the operand arrays inside one (chunk, value head) block.
+// -W, Q_G, K_d^T and P are fp16 A fragments, 1 KiB per 16 x 32 tile (tile
+// (m, k) at (m * ktiles + k) KiB); U~ is fp32 C/D fragments, 1 KiB per 16 x 16
+// tile.
 template <int DK, int DV, int C>
 struct VchLayout {
     static constexpr int CK = ck_pad(C);
     static constexpr int64_t negW = 0;
-    static constexpr int64_t QG = negW + 4ll * C * DK;
-    static constexpr int64_t KdT = QG + 4ll * C * DK;
-    static constexpr int64_t P = KdT + 4ll * DK * CK;
-    static constexpr int64_t Ut = P + 4ll * C * CK;
+    static constexpr int64_t QG = negW + 2ll * C * DK;
+    static constexpr int64_t KdT = QG + 2ll * C * DK;
+    static constexpr int64_t P = KdT + 2ll * DK * CK;
+    static constexpr int64_t Ut = P + 2ll * C * CK;
     static constexpr int64_t bytes = Ut + 4ll * C * DV;
     static_assert(bytes == vch_bytes(DK, DV, C), "layout");
 };
@@ -121,14 +124,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     constexpr int KTH = DK / 32;          // k steps over dk
     constexpr int KTC = CK / 32;          // k steps over the chunk
     constexpr int QH = (MTH + NW - 1) / NW;
-    constexpr int HS = DK + 8;            // LDS row stride (bf16) of H^T
-    constexpr int US = CK + 8;            // LDS row stride (bf16) of U^T
+    constexpr int HS = DK + 8;            // LDS row stride (fp16) of H^T
+    constexpr int US = CK + 8;            // LDS row stride (fp16) of U^T
     constexpr bool ALL_H = (MTH % NW) == 0;   // every state wave owns QH H row tiles
     static_assert(DV % DVS == 0 && DVS % 16 == 0 && DK % 32 == 0 && C % 16 == 0, "shape");
     static_assert(MT <= NW, "one chunk-row tile per wave");
 
-    __shared__ __align__(16) uint16_t HThi[DVS * HS], HTlo[DVS * HS];
-    __shared__ __align__(16) uint16_t UThi[DVS * US], UTlo[DVS * US];
+    // the matrix-core copies of H^T and U^T (fp16; the state itself stays in
+    // fp32 accumulators)
+    __shared__ __align__(16) uint16_t HT[DVS * HS];
+    __shared__ __align__(16) uint16_t UT[DVS * US];
 
     // XCD-aware order: the NS slices of one head land on the same XCD
     // (consecutive work-groups are dealt round-robin over the 8 XCDs), so the
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     const bool has_row = (MT >= NW) || mt < MT;
 
     // zero U^T (including the padded chunk rows C..CK-1, never written later)
-    for (int i = tid; i < DVS * US; i += kScanThreads) { UThi[i] = 0; UTlo[i] = 0; }
+    for (int i = tid; i < DVS * US; i += kScanThreads) UT[i] = 0;
 
     // entering state: the caller's initial state where the sequence starts,
     // else what the previous window left in the carry slot of its parity
@@ -181,11 +186,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             if (!ALL_H && mth >= MTH) continue;
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
-                uint2 hi, lo;
-                split4(hacc[qh][nt], hi, lo);
                 const int off = (nt * 16 + l16) * HS + mth * 16 + lq * 4;
-                *reinterpret_cast<uint2*>(&HThi[off]) = hi;
-                *reinterpret_cast<uint2*>(&HTlo[off]) = lo;
+                *reinterpret_cast<uint2*>(&HT[off]) = pack4_f16(hacc[qh][nt]);
             }
         }
     };
@@ -215,28 +217,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
         return p.vch + (static_cast<int64_t>(c - p.win_lo) * p.Hv + h) * L::bytes;
     };
     // B fragments of H^T (k over dk) and of U^T (k over the chunk) from LDS
-    auto read_H = [&](int kt, u32x4* bh, u32x4* bl) {
+    auto read_H = [&](int kt, u32x4* b) {
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-            const int off = (nt * 16 + l16) * HS + kt * 32 + lq * 8;
-            bh[nt] = *reinterpret_cast<const u32x4*>(&HThi[off]);
-            bl[nt] = *reinterpret_cast<const u32x4*>(&HTlo[off]);
-        }
+        for (int nt = 0; nt < NTL; ++nt)
+            b[nt] = *reinterpret_cast<const u32x4*>(&HT[(nt * 16 + l16) * HS + kt * 32 + lq * 8]);
     };
-    auto read_U = [&](u32x4 (*ubh)[NTL], u32x4 (*ubl)[NTL]) {
+    auto read_U = [&](u32x4 (*ub)[NTL]) {
 #pragma unroll
         for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                const int off = (nt * 16 + l16) * US + kt * 32 + lq * 8;
-                ubh[kt][nt] = *reinterpret_cast<const u32x4*>(&UThi[off]);
-                ubl[kt][nt] = *reinterpret_cast<const u32x4*>(&UTlo[off]);
-            }
+            for (int nt = 0; nt < NTL; ++nt)
+                ub[kt][nt] = *reinterpret_cast<const u32x4*>(&UT[(nt * 16 + l16) * US + kt * 32 + lq * 8]);
     };
-    auto frag = [&](const uint8_t* tile, u32x4& hi, u32x4& lo) {
-        hi = *reinterpret_cast<const u32x4*>(tile + lane * 16);
-        lo = *reinterpret_cast<const u32x4*>(tile + 1024 + lane * 16);
-    };
+    // one lane's 16 bytes of a 1 KiB fp16 fragment tile
+    auto frag = [&](const uint8_t* tile) { return *reinterpret_cast<const u32x4*>(tile + lane * 16); };
 
     if (!out_role) {
         // ---------------- state waves ----------------
@@ -244,9 +238,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
         // load while chunk c computes, W's per k step between the products,
         // K_d^T's after the state update.
         struct Ops {
-            u32x4 w_h[KTH], w_l[KTH];
+            u32x4 w[KTH];
             f32x4 ut[NTL];
-            u32x4 k_h[QH][KTC], k_l[QH][KTC];
+            u32x4 k[QH][KTC];
             float dec;
         };
         auto load_w = [&](Ops& o, int c, int kt) {
@@ -261,7 +255,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                     }
                 }
             }
-            if (has_row) frag(blk + L::negW + (mt * KTH + kt) * 2048, o.w_h[kt], o.w_l[kt]);
+            if (has_row) o.w[kt] = frag(blk + L::negW + (mt * KTH + kt) * 1024);
         };
         auto load_k = [&](Ops& o, int c) {
             const uint8_t* blk = block_of(c);
@@ -271,13 +265,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 if (!ALL_H && mth >= MTH) continue;
 #pragma unroll
                 for (int kt = 0; kt < KTC; ++kt)
-                    frag(blk + L::KdT + (mth * KTC + kt) * 2048, o.k_h[qh][kt], o.k_l[qh][kt]);
+                    o.k[qh][kt] = frag(blk + L::KdT + (mth * KTC + kt) * 1024);
             }
         };
         auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
             // (1) U = U~ - W H for this wave's chunk rows; even and odd k
-            // steps accumulate separately (two independent chains), the three
-            // split terms term-major within each
+            // steps accumulate separately (two independent chains)
             f32x4 a0[NTL], a1[NTL];
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
@@ -288,34 +281,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             for (int kt = 0; kt < KTH; ++kt) {
                 load_w(nxt, cn, kt);
                 if (!has_row) continue;
-                u32x4 bh[NTL], bl[NTL];
-                read_H(kt, bh, bl);
+                u32x4 b[NTL];
+                read_H(kt, b);
                 f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.w_l[kt], bh[nt], a[nt]);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.w_h[kt], bl[nt], a[nt]);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.w_h[kt], bh[nt], a[nt]);
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h(cur.w[kt], b[nt], a[nt]);
             }
             if (has_row) {
-                // (2) U^T into LDS (split)
+                // (2) U^T into LDS
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) {
                     f32x4 u;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) u[i] = a0[nt][i] + a1[nt][i];
-                    uint2 hi, lo;
-                    split4(u, hi, lo);
-                    const int off = (nt * 16 + l16) * US + mt * 16 + lq * 4;
-                    *reinterpret_cast<uint2*>(&UThi[off]) = hi;
-                    *reinterpret_cast<uint2*>(&UTlo[off]) = lo;
+                    *reinterpret_cast<uint2*>(&UT[(nt * 16 + l16) * US + mt * 16 + lq * 4]) = pack4_f16(u);
                 }
             }
             __syncthreads();
             // (3) H' = e^{gamma_last} H + K_d^T U
-            u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
-            read_U(ubh, ubl);
+            u32x4 ub[KTC][NTL];
+            read_U(ub);
 #pragma unroll
             for (int qh = 0; qh < QH; ++qh) {
                 if (!ALL_H && wave + NW * qh >= MTH) continue;
@@ -327,17 +312,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
 #pragma unroll
-                for (int term = 0; term < 3; ++term) {
+                for (int qh = 0; qh < QH; ++qh) {
+                    if (!ALL_H && wave + NW * qh >= MTH) continue;
 #pragma unroll
-                    for (int qh = 0; qh < QH; ++qh) {
-                        if (!ALL_H && wave + NW * qh >= MTH) continue;
-#pragma unroll
-                        for (int nt = 0; nt < NTL; ++nt) {
-                            const u32x4 a = term == 1 ? cur.k_h[qh][kt] : (term == 0 ? cur.k_l[qh][kt] : cur.k_h[qh][kt]);
-                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
-                            hacc[qh][nt] = mfma(a, b, hacc[qh][nt]);
-                        }
-                    }
+                    for (int nt = 0; nt < NTL; ++nt) hacc[qh][nt] = mfma_h(cur.k[qh][kt], ub[kt][nt], hacc[qh][nt]);
                 }
             }
             // (4) H' into LDS for the next chunk (every wave read H in (1))
@@ -380,17 +358,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     } else {
         // ---------------- output waves ----------------
         struct Ops {
-            u32x4 q_h[KTH], q_l[KTH];
-            u32x4 p_h[KTC], p_l[KTC];
+            u32x4 q[KTH];
+            u32x4 p[KTC];
         };
         auto load_q = [&](Ops& o, int c, int kt) {
-            if (has_row) frag(block_of(c) + L::QG + (mt * KTH + kt) * 2048, o.q_h[kt], o.q_l[kt]);
+            if (has_row) o.q[kt] = frag(block_of(c) + L::QG + (mt * KTH + kt) * 1024);
         };
         auto load_p = [&](Ops& o, int c) {
             if (!has_row) return;
             const uint8_t* blk = block_of(c);
 #pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) frag(blk + L::P + (mt * KTC + kt) * 2048, o.p_h[kt], o.p_l[kt]);
+            for (int kt = 0; kt < KTC; ++kt) o.p[kt] = frag(blk + L::P + (mt * KTC + kt) * 1024);
         };
         auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
             const int64_t t0 = start + static_cast<int64_t>(c - cb) * C;
@@ -406,21 +384,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             for (int kt = 0; kt < KTH; ++kt) {
                 load_q(nxt, cn, kt);
                 if (!has_row) continue;
-                u32x4 bh[NTL], bl[NTL];
-                read_H(kt, bh, bl);
+                u32x4 b[NTL];
+                read_H(kt, b);
                 f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.q_l[kt], bh[nt], a[nt]);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.q_h[kt], bl[nt], a[nt]);
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma(cur.q_h[kt], bh[nt], a[nt]);
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h(cur.q[kt], b[nt], a[nt]);
             }
             __syncthreads();
             if (has_row) {
                 // (2) O += P U, store the valid rows
-                u32x4 ubh[KTC][NTL], ubl[KTC][NTL];
-                read_U(ubh, ubl);
+                u32x4 ub[KTC][NTL];
+                read_U(ub);
                 load_p(nxt, cn);
                 f32x4 acco[NTL];
 #pragma unroll
@@ -428,17 +402,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acco[nt][i] = a0[nt][i] + a1[nt][i];
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt) {
+                for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-                    for (int term = 0; term < 3; ++term) {
-#pragma unroll
-                        for (int nt = 0; nt < NTL; ++nt) {
-                            const u32x4 a = term == 1 ? cur.p_h[kt] : (term == 0 ? cur.p_l[kt] : cur.p_h[kt]);
-                            const u32x4 b = term == 1 ? ubl[kt][nt] : ubh[kt][nt];
-                            acco[nt] = mfma(a, b, acco[nt]);
-                        }
-                    }
-                }
+                    for (int nt = 0; nt < NTL; ++nt) acco[nt] = mfma_h(cur.p[kt], ub[kt][nt], acco[nt]);
                 // rows past the sequence end go to a sink, so that every lane
                 // issues the same stores (the memory counter the next chunk's
                 // operand waits rely on then counts them exactly)
@@ -691,6 +657,17 @@ __global__ __launch_bounds__(64) void selftest_mfma_kernel(const float* A, const
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) Cm[256 + (4 * (l / 16) + i) * 16 + (l % 16)] = acc2[i];
+    // A and B rounded once to fp16, one v_mfma_f32_16x16x32_f16
+    float a8[8], b8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int k = 8 * (l / 16) + e;
+        a8[e] = A[(l % 16) * 32 + k];
+        b8[e] = B[k * 16 + (l % 16)];
+    }
+    const f32x4 acc3 = mfma_h(pack8_f16(a8), pack8_f16(b8), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Cm[512 + (4 * (l / 16) + i) * 16 + (l % 16)] = acc3[i];
 }
 
 hipError_t launch_selftest_mfma(const float* A, const float* B, float* Cm, hipStream_t s) {

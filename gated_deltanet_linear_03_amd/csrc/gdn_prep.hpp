@@ -14,8 +14,8 @@
 //           substitution X_i = T_ii (B_i - sum_{j<i} A_ij X_j) over the
 //           16-token blocks, split-bf16 MFMA
 // and writes the scan's operands in MFMA fragment order: -W, Q_G =
-// diag(e^gamma) Q^, K_d^T = (diag(e^{gamma_last - gamma}) K^)^T, P and U~,
-// plus e^{gamma_last}.  (Chunk form of Yang, Kautz, Hatamizadeh, "Gated Delta
+// diag(e^gamma) Q^, K_d^T = (diag(e^{gamma_last - gamma}) K^)^T and P as
+// fp16, U~ as fp32, plus e^{gamma_last}.  (Chunk form of Yang, Kautz, Hatamizadeh, "Gated Delta
 // Networks", ICLR 2025, on the UT transform of Yang et al., NeurIPS 2024.)
 #pragma once
 #include "gdn_device.hpp"
@@ -166,11 +166,6 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
     }
 }
 
-__device__ __forceinline__ void store_frag(uint8_t* tile, int lane, u32x4 hi, u32x4 lo) {
-    *reinterpret_cast<u32x4*>(tile + lane * 16) = hi;
-    *reinterpret_cast<u32x4*>(tile + 1024 + lane * 16) = lo;
-}
-
 // bf16 element of a split pair back to fp32
 __device__ __forceinline__ float hl(const uint16_t* h, const uint16_t* l, int i) {
     return bf16_bits_to_f32(h[i]) + bf16_bits_to_f32(l[i]);
@@ -191,8 +186,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     __shared__ __align__(16) uint8_t smem[S::total];
     uint16_t* sQh = reinterpret_cast<uint16_t*>(smem + S::oQ);
     uint16_t* sQl = sQh + C * SQ;
-    uint16_t* sWh = sQh;                 // -W staging over Q^
-    uint16_t* sWl = sQl;
+    uint16_t* sW = sQh;                  // -W staging (fp16) over Q^
     uint16_t* sKh = reinterpret_cast<uint16_t*>(smem + S::oK);
     uint16_t* sKl = sKh + C * SQ;
     uint16_t* sVh = reinterpret_cast<uint16_t*>(smem + S::oV);
@@ -441,9 +435,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             const float e = sE[r];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] *= e;
-            u32x4 hi, lo;
-            split8(x, hi, lo);
-            store_frag(blk + L::QG + tile * 2048, ln, hi, lo);
+            *reinterpret_cast<u32x4*>(blk + L::QG + tile * 1024 + ln * 16) = pack8_f16(x);
         }
     }
     __syncthreads();
@@ -454,7 +446,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     //         one 16-column tile per wave on split-bf16 k = 16 matrix-core
     //         products: their accumulator layout is their B-operand layout,
     //         so X_j stays in registers and the waves never wait for each
-    //         other.  U~ goes out directly, -W is staged over Q^ (dead).
+    //         other.  U~ goes out directly, -W is staged (fp16) over Q^
+    //         (dead).
     //         Then the P and K_d^T fragments. ----
     constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU;
     static_assert(NTT <= NW, "one column tile per wave");
@@ -493,11 +486,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             for (int i = 0; i < NB; ++i) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    uint16_t hi, lo;
-                    split_bf16(-X[i][r], hi, lo);
-                    const int off = (16 * i + 4 * lq + r) * SQ + wave * 16 + l16;
-                    sWh[off] = hi;
-                    sWl[off] = lo;
+                    sW[(16 * i + 4 * lq + r) * SQ + wave * 16 + l16] =
+                        __builtin_bit_cast(uint16_t, static_cast<_Float16>(-X[i][r]));
                 }
             }
         } else {
@@ -518,9 +508,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             const int s = s0 + e;
             x[e] = (s / 16 <= r / 16 && s < C) ? sP[r * SG + s] : 0.f;
         }
-        u32x4 hi, lo;
-        split8(x, hi, lo);
-        store_frag(blk + L::P + tile * 2048, ln, hi, lo);
+        *reinterpret_cast<u32x4*>(blk + L::P + tile * 1024 + ln * 16) = pack8_f16(x);
     }
     for (int sl = tid; sl < DK * CK / 8; sl += NT) {              // K_d^T [DK][CK]
         const int tile = sl / 64, ln = sl % 64;
@@ -532,9 +520,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             const int s = s0 + e;
             x[e] = s < C ? sD[s] * hl(sKh, sKl, s * SQ + i) : 0.f;
         }
-        u32x4 hi, lo;
-        split8(x, hi, lo);
-        store_frag(blk + L::KdT + tile * 2048, ln, hi, lo);
+        *reinterpret_cast<u32x4*>(blk + L::KdT + tile * 1024 + ln * 16) = pack8_f16(x);
     }
     __syncthreads();
 
@@ -543,7 +529,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         const int tile = sl / 64, ln = sl % 64;
         const int mt = tile / (DK / 32), kt = tile % (DK / 32);
         const int r = mt * 16 + ln % 16, c0 = kt * 32 + 8 * (ln / 16);
-        store_frag(blk + L::negW + tile * 2048, ln, lds16(sWh + r * SQ + c0), lds16(sWl + r * SQ + c0));
+        *reinterpret_cast<u32x4*>(blk + L::negW + tile * 1024 + ln * 16) = lds16(sW + r * SQ + c0);
     }
 }
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -224,10 +224,11 @@ const char* gdn_status_string(gdn_status status);
 const char* gdn_last_error(void);
 
 /* Library self-test of the matrix-core fragment layouts the kernels rely on:
- * computes C = A[16][32] * B[32][16] twice through bf16 hi/lo split
- * products, into C[0][16][16] on v_mfma_f32_16x16x32_bf16 and into
- * C[1][16][16] on v_mfma_f32_16x16x16_bf16 (two k halves); row-major fp32
- * in/out, device pointers (C holds 512 floats).  Synchronises the stream.
+ * computes C = A[16][32] * B[32][16] through bf16 hi/lo split products into
+ * C[0][16][16] on v_mfma_f32_16x16x32_bf16 and into C[1][16][16] on
+ * v_mfma_f32_16x16x16_bf16 (two k halves), and with A and B rounded to fp16
+ * into C[2][16][16] on v_mfma_f32_16x16x32_f16; row-major fp32 in/out,
+ * device pointers (C holds 768 floats).  Synchronises the stream.
  * Returns GDN_OK or GDN_ERR_HIP. */
 gdn_status gdn_selftest_mfma(const float* A, const float* B, float* C,
                              void* stream);

@@ -46,19 +46,29 @@ def dims(sh):
 
 def chunk_slot_bytes(Hv, dk, dv, C):
     """Operand-block bytes of one chunk slot (all value heads): -W, Q_G,
-    K_d^T, P and U~ as split bf16 / fp32 fragments."""
+    K_d^T and P as fp16 fragments, U~ as fp32 fragments."""
     CK = max(C, 32)
-    return Hv * (4 * C * dk * 2 + 4 * dk * CK + 4 * C * CK + 4 * C * dv)
+    return Hv * (2 * C * dk * 2 + 2 * dk * CK + 2 * C * CK + 4 * C * dv)
+
+
+def default_window_slots(layer, N, T):
+    """Chunk slots per window gdn_prefill uses with a full workspace: as many
+    as ~144 MiB of operand blocks hold for one sequence (4 GiB for several),
+    evened out over the windows that takes."""
+    slot = chunk_slot_bytes(layer.Hv, layer.dk, layer.dv, layer.chunk)
+    target = (144 << 20) if N == 1 else (4 << 30)
+    mc = max((T + N * (layer.chunk - 1)) // layer.chunk, 1)
+    w = min(max(1, target // slot), mc)
+    nwin = -(-mc // w)
+    return -(-mc // nwin)
 
 
 def workspace_for_window(layer, N, T, window_slots):
     """Workspace bytes that make gdn_prefill run windows of window_slots
-    chunk slots (the default window is ~144 MiB of operand blocks for one
-    sequence, up to 4 GiB for several)."""
+    chunk slots (fewer, if that is more than the default)."""
     slot = chunk_slot_bytes(layer.Hv, layer.dk, layer.dv, layer.chunk)
     full = gdn.prefill_workspace_bytes(layer, N, T)
-    target = (144 << 20) if N == 1 else (4 << 30)
-    default = min(max(1, target // slot), max((T + N * (layer.chunk - 1)) // layer.chunk, 1))
+    default = default_window_slots(layer, N, T)
     return full - (default - min(window_slots, default)) * slot
 
 

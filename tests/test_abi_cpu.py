@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 3
+    assert L.gdn_abi_version() == 4
 
 
 def test_status_strings():
@@ -214,24 +214,32 @@ def test_binding_marshals_to_the_abi_and_raises():
 
 def test_prefill_windows_follow_the_workspace():
     """The prefill runs window by window over the chunk slots: the default
-    workspace gives ~144 MiB windows at the 35B-A3B shape, a smaller one more
-    windows, down to one chunk slot; below that the call is refused."""
+    workspace gives windows of up to ~144 MiB of operand blocks at the 35B-A3B
+    shape (evened out over the windows), a smaller one more windows, down to
+    one chunk slot; below that the call is refused."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
                     conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
                     dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
-    slot = 32 * (4 * 64 * 128 * 2 + 4 * 128 * 64 + 4 * 64 * 64 + 4 * 64 * 128)
+    # -W, Q_G, K_d^T, P as fp16 fragments and U~ as fp32, for 32 value heads
+    slot = 32 * (2 * 64 * 128 * 2 + 2 * 128 * 64 + 2 * 64 * 64 + 4 * 64 * 128)
+
+    def window(n_chunks):
+        w = min((144 << 20) // slot, n_chunks)
+        return -(-n_chunks // -(-n_chunks // w))
+
     T = 4096
     nb = gdn.prefill_workspace_bytes(lay, 1, T)
     names = gdn.prefill_launches(lay, 1, T, nb)
     assert names[0] == "plan" and names[-1] == "epi"
     assert names[1:-1] == ["prep", "scan"] * ((len(names) - 2) // 2)
-    win = (144 << 20) // slot                     # chunk slots per window
     n_chunks = (T + 63) // 64                     # the bound the library plans for
-    assert len(names) == 2 + 2 * -(-n_chunks // win)
-    # workspace size independent of T beyond the pre-norm output
+    win = window(n_chunks)                        # chunk slots per window
+    assert win == 32 and len(names) == 2 + 2 * 2
+    # beyond the pre-norm output and the decay table, only the window grows
     nb_long = gdn.prefill_workspace_bytes(lay, 1, 131072)
-    assert nb_long - nb == (131072 - T) * 32 * 128 * 4 + 4 * (131072 - T) // 64 * 32
-    # half the window: about twice the windows
+    assert nb_long - nb == ((131072 - T) * 32 * 128 * 4 + 4 * (131072 - T) // 64 * 32
+                            + (window(131072 // 64) - win) * slot)
+    # half the window: twice the windows
     half = len(gdn.prefill_launches(lay, 1, T, nb - (win - win // 2) * slot))
     assert half == 2 + 2 * -(-n_chunks // (win // 2))
     # the smallest workspace holds one slot: a window per chunk slot

@@ -20,13 +20,18 @@ def test_mfma_fragment_layout():
     r = np.random.default_rng(0)
     A = r.standard_normal((16, 32)).astype(np.float32)
     B = r.standard_normal((32, 16)).astype(np.float32)
-    C = torch.empty((2, 16, 16), dtype=torch.float32, device="cuda")
+    C = torch.empty((3, 16, 16), dtype=torch.float32, device="cuda")
     gdn.selftest_mfma(to_dev(A), to_dev(B), C)
     ref = A.astype(np.float64) @ B.astype(np.float64)
     for i, shape in enumerate(("16x16x32", "16x16x16")):
         err = np.abs(C[i].cpu().numpy() - ref).max() / np.abs(ref).max()
         print(f"mfma {shape} split-bf16 product rel err", err)
         assert err < 1e-4, shape
+    # single fp16 product: exact up to fp32 accumulation once A, B are rounded
+    ref16 = A.astype(np.float16).astype(np.float64) @ B.astype(np.float16).astype(np.float64)
+    err = np.abs(C[2].cpu().numpy() - ref16).max() / np.abs(ref16).max()
+    print("mfma 16x16x32 fp16 product rel err", err)
+    assert err < 1e-5
 
 
 def test_prefill_tiny():
