@@ -28,7 +28,7 @@ struct PrepSmem {
     static constexpr int CK = ck_pad(C);
     static constexpr int NB = C / 16;
     static constexpr int SQ = DK + 8;    // bf16 row stride of Q^, K^ and the W staging [C][SQ]
-    static constexpr int SV = DV + 8;    // bf16 row stride of V^ [C][SV]
+    static constexpr int SV = DV + 8;    // fp32 row stride of V^ [C][SV]
     static constexpr int SG = C + 4;     // fp32 row stride of P [C][SG]
     static constexpr int SA = C + 8;     // bf16 row stride of -A below the diagonal blocks [C][SA]
     static constexpr int SD = 20;        // fp32 row stride of A's diagonal blocks [NB][16][SD]
@@ -189,8 +189,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     uint16_t* sW = sQh;                  // -W staging (fp16) over Q^
     uint16_t* sKh = reinterpret_cast<uint16_t*>(smem + S::oK);
     uint16_t* sKl = sKh + C * SQ;
-    uint16_t* sVh = reinterpret_cast<uint16_t*>(smem + S::oV);
-    uint16_t* sVl = sVh + C * SV;
+    float* sV = reinterpret_cast<float*>(smem + S::oV);     // V^ (fp32: only a B-operand source)
     f32x4* sCw = reinterpret_cast<f32x4*>(smem + S::oG);
     float* sAd = reinterpret_cast<float*>(smem + S::oG);
     uint16_t* sAh = reinterpret_cast<uint16_t*>(smem + S::oG + S::ad_bytes);
@@ -278,11 +277,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             for (int e = 0; e < 8; ++e) w[e] = sCw[wb + e];
             float y[4][8];
             conv_rows<BF16>(raw, w, r0, Lc, y);
-            uint16_t* dh = kind == 0 ? sQh : (kind == 1 ? sKh : sVh);
-            uint16_t* dl = kind == 0 ? sQl : (kind == 1 ? sKl : sVl);
-            const int stride = kind == 2 ? SV : SQ;
+            uint16_t* dh = kind == 0 ? sQh : sKh;
+            uint16_t* dl = kind == 0 ? sQl : sKl;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
+                if (kind == 2) {
+                    float* dv = sV + (r0 + t) * SV + grp * 8;
+                    *reinterpret_cast<f32x4*>(dv) = f32x4{y[t][0], y[t][1], y[t][2], y[t][3]};
+                    *reinterpret_cast<f32x4*>(dv + 4) = f32x4{y[t][4], y[t][5], y[t][6], y[t][7]};
+                    continue;
+                }
                 if (kind < 2) {
                     float ss = 0.f;
 #pragma unroll
@@ -295,8 +299,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 }
                 u32x4 hi, lo;
                 split8(y[t], hi, lo);
-                *reinterpret_cast<u32x4*>(dh + (r0 + t) * stride + grp * 8) = hi;
-                *reinterpret_cast<u32x4*>(dl + (r0 + t) * stride + grp * 8) = lo;
+                *reinterpret_cast<u32x4*>(dh + (r0 + t) * SQ + grp * 8) = hi;
+                *reinterpret_cast<u32x4*>(dl + (r0 + t) * SQ + grp * 8) = lo;
             }
         }
         if (wave == 0) {
@@ -454,9 +458,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     if (wave < NTT) {
         const bool isw = wave < NTW;
         const int ch = (isw ? wave : wave - NTW) * 16 + l16;
-        const uint16_t* bh = (isw ? sKh : sVh) + ch;
-        const uint16_t* bl = (isw ? sKl : sVl) + ch;
-        const int bs = isw ? SQ : SV;
         f32x4 X[NB];
         uint2 xh[NB], xl[NB];
 #pragma unroll
@@ -465,9 +466,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             const f32x4 be = *reinterpret_cast<const f32x4*>(sbeta + s0);
             const f32x4 ee = *reinterpret_cast<const f32x4*>(sE + s0);
             f32x4 acc;
+            if (isw) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[e] = hl(bh, bl, (s0 + e) * bs) * (isw ? be[e] * ee[e] : be[e]);
+                for (int e = 0; e < 4; ++e) acc[e] = hl(sKh + ch, sKl + ch, (s0 + e) * SQ) * (be[e] * ee[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = sV[(s0 + e) * SV + ch] * be[e];
+            }
 #pragma unroll
             for (int j = 0; j < i; ++j) {
                 const int ao = (16 * i + l16) * SA + 16 * j + 4 * lq;
