@@ -217,6 +217,8 @@ def main():
 
     scan_f, prep_f = prefill_flops_per_token(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.chunk)
     epi_bytes = sh.Hv * sh.dv * (4 + 2 + 4)
+    path_bytes = (T * ((2 * sh.Hk * sh.dk + 2 * sh.Hv * sh.dv + 2 * sh.Hv) * 2 + sh.Hv * sh.dv * 4)
+                  + sh.Hv * sh.dk * sh.dv * 4)
     rl = {}
     for name, ms in kern_ms.items():
         if name == "scan":
@@ -255,6 +257,12 @@ def main():
         "ms_per_step_one_input_set": warm_ms,
         "prefill_kernel_roofline": {k: dict(v, frac=v["achieved"] / v["peak"]) for k, v in rl.items()},
         "prefill_alg_tflops": (scan_f + prep_f) * T / (ms_step * 1e-3) / 1e12,
+        # the whole path against HBM: compulsory bytes (q, k, v, z, a, b in,
+        # out, the final state) over the step time
+        "prefill_path_roofline": {
+            "bound": "hbm", "bytes_per_step": path_bytes,
+            "achieved": path_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": path_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
 
     # ---------------- context: measured device-copy bandwidth ----------------
