@@ -57,7 +57,7 @@ def parse():
     return ap.parse_args()
 
 
-# ---- algorithmic work per token / per sequence (definitions in the design doc) --
+# ---- algorithmic work per token / per sequence ---------------------------------
 
 def prefill_flops_per_token(Hk, Hv, dk, dv, C):
     """Matrix products of the chunked form, counted once (triangles at
