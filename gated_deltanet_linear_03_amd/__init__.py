@@ -31,8 +31,10 @@ GDN_DTYPE_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
-           "gdn_step", "gdn_status_string",
-           "gdn_last_error", "gdn_selftest_mfma")
+           "gdn_step", "gdn_snapshot_bytes", "gdn_snapshot_save", "gdn_snapshot_inspect",
+           "gdn_snapshot_restore", "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
+SNAPSHOT_MAGIC = 0x50534E47
+SNAPSHOT_VERSION = 1
 PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
 
 
@@ -41,6 +43,15 @@ class GdnError(RuntimeError):
         super().__init__(f"gdn status {status}: {detail}")
         self.status = status
         self.detail = detail
+
+
+class CSnapshotHeader(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+                ("Hk", ctypes.c_int32), ("Hv", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("conv_K", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("state_bytes", ctypes.c_uint64), ("conv_bytes", ctypes.c_uint64),
+                ("checksum", ctypes.c_uint64), ("reserved", ctypes.c_uint64)]
 
 
 class CLayer(ctypes.Structure):
@@ -125,6 +136,19 @@ def lib():
         L.gdn_last_error.argtypes = []
         L.gdn_selftest_mfma.restype = ctypes.c_int
         L.gdn_selftest_mfma.argtypes = [ctypes.c_void_p] * 4
+        L.gdn_snapshot_bytes.restype = ctypes.c_size_t
+        L.gdn_snapshot_bytes.argtypes = [ctypes.POINTER(CLayer)]
+        L.gdn_snapshot_save.restype = ctypes.c_int
+        L.gdn_snapshot_save.argtypes = [ctypes.POINTER(CLayer), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_snapshot_inspect.restype = ctypes.c_int
+        L.gdn_snapshot_inspect.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.POINTER(CSnapshotHeader)]
+        L.gdn_snapshot_restore.restype = ctypes.c_int
+        L.gdn_snapshot_restore.argtypes = [ctypes.POINTER(CLayer), ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -383,6 +407,53 @@ def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
     if want_core:
         res["core_out"] = core
     return res
+
+
+def snapshot_bytes(layer: Layer) -> int:
+    cl = layer.c()
+    n = lib().gdn_snapshot_bytes(ctypes.byref(cl))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return int(n)
+
+
+def snapshot_save(layer: Layer, state, conv_state, slot: int = 0, num_slots=None, stream=None):
+    """Park pool entry `slot` of state [num_slots, Hv, dk, dv] and conv_state
+    [num_slots, K-1, Cc] (device tensors) into a new host buffer (a numpy
+    uint8 array holding the header and the payload).  Synchronises the
+    stream."""
+    import numpy as np
+    if num_slots is None:
+        num_slots = int(state.shape[0])
+    buf = np.zeros(snapshot_bytes(layer), dtype=np.uint8)
+    cl = layer.c()
+    _check(lib().gdn_snapshot_save(ctypes.byref(cl), _ptr(state), _ptr(conv_state), int(slot),
+                                   int(num_slots), buf.ctypes.data, buf.nbytes, _stream(stream)))
+    return buf
+
+
+def snapshot_inspect(buf) -> dict:
+    """Validate a snapshot held in a host bytes-like object; return its header."""
+    import numpy as np
+    arr = np.frombuffer(buf, dtype=np.uint8)
+    hd = CSnapshotHeader()
+    _check(lib().gdn_snapshot_inspect(arr.ctypes.data if arr.size else None, arr.nbytes,
+                                      ctypes.byref(hd)))
+    return {name: getattr(hd, name) for name, _ in CSnapshotHeader._fields_}
+
+
+def snapshot_restore(layer: Layer, buf, state, conv_state, slot: int = 0, num_slots=None,
+                     stream=None):
+    """Write a snapshot back into pool entry `slot` of state / conv_state
+    after checking it belongs to this layer.  Synchronises the stream."""
+    import numpy as np
+    if num_slots is None:
+        num_slots = int(state.shape[0])
+    arr = np.frombuffer(buf, dtype=np.uint8)
+    cl = layer.c()
+    _check(lib().gdn_snapshot_restore(ctypes.byref(cl), arr.ctypes.data if arr.size else None,
+                                      arr.nbytes, _ptr(state), _ptr(conv_state), int(slot),
+                                      int(num_slots), _stream(stream)))
 
 
 def selftest_mfma(A, B, C, stream=None):

@@ -1,6 +1,7 @@
 // gdn_abi.hip -- C-ABI front end: argument validation, workspace carving and
 // dispatch to the compiled kernel instantiations.  No allocation, no host
-// synchronisation (except the self-test), no exceptions across the ABI.
+// synchronisation (except the self-test and the snapshot calls), no exceptions
+// across the ABI.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -373,6 +374,134 @@ gdn_status gdn_decode_multi(const gdn_layer* L, const gdn_decode_io* io, int32_t
     if (tokens < 1 || tokens > gdn::kMaxVerifyTokens)
         return fail(GDN_ERR_INVALID_ARGUMENT, "tokens (%d) must be in [1, %d]", tokens, gdn::kMaxVerifyTokens);
     return decode_impl(L, io, tokens, state_snapshots, stream);
+}
+
+// ---- session snapshots ------------------------------------------------------
+
+static_assert(sizeof(gdn_snapshot_header) == 64, "snapshot header is 64 bytes");
+
+static uint64_t fnv1a64(const uint8_t* p, size_t n) {
+    uint64_t h = 14695981039346656037ull;    // FNV-1a 64 offset basis
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 1099511628211ull;                   // FNV 64 prime
+    }
+    return h;
+}
+
+static void snapshot_sizes(const gdn_layer* L, uint64_t* sb, uint64_t* cb) {
+    const int64_t Cc = 2ll * L->Hk * L->dk + static_cast<int64_t>(L->Hv) * L->dv;
+    *sb = static_cast<uint64_t>(L->Hv) * L->dk * L->dv * 4;
+    *cb = static_cast<uint64_t>(L->conv_K - 1) * Cc * act_size(L->act_dtype);
+}
+
+static gdn_status snapshot_args(const gdn_layer* L, const void* state, const void* conv, int32_t slot,
+                                int32_t num_slots, const void* host, size_t host_bytes) {
+    gdn_status st = check_layer(L, false);
+    if (st != GDN_OK) return st;
+    if (!state || !conv || !host) return fail(GDN_ERR_INVALID_ARGUMENT, "NULL state, conv state or host buffer");
+    if (num_slots <= 0 || slot < 0 || slot >= num_slots)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "slot %d outside [0, num_slots=%d)", slot, num_slots);
+    uint64_t sb, cb;
+    snapshot_sizes(L, &sb, &cb);
+    if (host_bytes < sizeof(gdn_snapshot_header) + sb + cb)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "host buffer of %zu bytes, a snapshot needs %llu", host_bytes,
+                    static_cast<unsigned long long>(sizeof(gdn_snapshot_header) + sb + cb));
+    return GDN_OK;
+}
+
+size_t gdn_snapshot_bytes(const gdn_layer* L) {
+    g_err[0] = 0;
+    if (check_layer(L, false) != GDN_OK) return 0;
+    uint64_t sb, cb;
+    snapshot_sizes(L, &sb, &cb);
+    return sizeof(gdn_snapshot_header) + sb + cb;
+}
+
+gdn_status gdn_snapshot_save(const gdn_layer* L, const float* state, const void* conv, int32_t slot,
+                             int32_t num_slots, void* host, size_t host_bytes, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = snapshot_args(L, state, conv, slot, num_slots, host, host_bytes);
+    if (st != GDN_OK) return st;
+    uint64_t sb, cb;
+    snapshot_sizes(L, &sb, &cb);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* payload = static_cast<uint8_t*>(host) + sizeof(gdn_snapshot_header);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(payload, reinterpret_cast<const uint8_t*>(state) + sb * slot, sb,
+                           hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(payload + sb, static_cast<const uint8_t*>(conv) + cb * slot, cb,
+                           hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "snapshot copy failed: %s", hipGetErrorString(e));
+    gdn_snapshot_header hd{};
+    hd.magic = GDN_SNAPSHOT_MAGIC;
+    hd.version = GDN_SNAPSHOT_VERSION;
+    hd.Hk = L->Hk; hd.Hv = L->Hv; hd.dk = L->dk; hd.dv = L->dv;
+    hd.conv_K = L->conv_K;
+    hd.act_dtype = L->act_dtype;
+    hd.state_bytes = sb;
+    hd.conv_bytes = cb;
+    hd.checksum = fnv1a64(payload, sb + cb);
+    hd.reserved = 0;
+    memcpy(host, &hd, sizeof hd);
+    return GDN_OK;
+}
+
+gdn_status gdn_snapshot_inspect(const void* host, size_t host_bytes, gdn_snapshot_header* out) {
+    g_err[0] = 0;
+    if (!host) return fail(GDN_ERR_INVALID_ARGUMENT, "NULL snapshot buffer");
+    if (host_bytes < sizeof(gdn_snapshot_header))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "buffer of %zu bytes is shorter than a snapshot header", host_bytes);
+    gdn_snapshot_header hd;
+    memcpy(&hd, host, sizeof hd);
+    if (hd.magic != GDN_SNAPSHOT_MAGIC) return fail(GDN_ERR_INVALID_ARGUMENT, "not a snapshot (bad magic)");
+    if (hd.version != GDN_SNAPSHOT_VERSION)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot version %u, this library reads %u", hd.version,
+                    static_cast<unsigned>(GDN_SNAPSHOT_VERSION));
+    if (hd.Hk <= 0 || hd.Hv <= 0 || hd.dk <= 0 || hd.dv <= 0 || hd.conv_K < 1 ||
+        (hd.act_dtype != GDN_DTYPE_FP32 && hd.act_dtype != GDN_DTYPE_BF16))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot header has an invalid geometry or dtype");
+    const uint64_t Cc = 2ull * hd.Hk * hd.dk + static_cast<uint64_t>(hd.Hv) * hd.dv;
+    if (hd.state_bytes != static_cast<uint64_t>(hd.Hv) * hd.dk * hd.dv * 4 ||
+        hd.conv_bytes != static_cast<uint64_t>(hd.conv_K - 1) * Cc * act_size(hd.act_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot payload sizes do not match its geometry");
+    if (host_bytes - sizeof hd < hd.state_bytes + hd.conv_bytes)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot truncated: %zu payload bytes, header says %llu",
+                    host_bytes - sizeof hd, static_cast<unsigned long long>(hd.state_bytes + hd.conv_bytes));
+    const uint8_t* payload = static_cast<const uint8_t*>(host) + sizeof hd;
+    if (fnv1a64(payload, hd.state_bytes + hd.conv_bytes) != hd.checksum)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot checksum mismatch (corrupted payload)");
+    if (out) *out = hd;
+    return GDN_OK;
+}
+
+gdn_status gdn_snapshot_restore(const gdn_layer* L, const void* host, size_t host_bytes, float* state,
+                                void* conv, int32_t slot, int32_t num_slots, void* stream) {
+    g_err[0] = 0;
+    gdn_snapshot_header hd;
+    gdn_status st = gdn_snapshot_inspect(host, host_bytes, &hd);
+    if (st != GDN_OK) return st;
+    if ((st = check_layer(L, false)) != GDN_OK) return st;
+    if (hd.Hk != L->Hk || hd.Hv != L->Hv || hd.dk != L->dk || hd.dv != L->dv || hd.conv_K != L->conv_K ||
+        hd.act_dtype != L->act_dtype)
+        return fail(GDN_ERR_INVALID_ARGUMENT,
+                    "snapshot of a layer with Hk=%d Hv=%d dk=%d dv=%d K=%d act_dtype=%d does not fit this "
+                    "layer (Hk=%d Hv=%d dk=%d dv=%d K=%d act_dtype=%d)", hd.Hk, hd.Hv, hd.dk, hd.dv,
+                    hd.conv_K, hd.act_dtype, L->Hk, L->Hv, L->dk, L->dv, L->conv_K, L->act_dtype);
+    if ((st = snapshot_args(L, state, conv, slot, num_slots, host, host_bytes)) != GDN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* payload = static_cast<const uint8_t*>(host) + sizeof hd;
+    hipError_t e = hipMemcpyAsync(reinterpret_cast<uint8_t*>(state) + hd.state_bytes * slot, payload,
+                                  hd.state_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(static_cast<uint8_t*>(conv) + hd.conv_bytes * slot, payload + hd.state_bytes,
+                           hd.conv_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "snapshot restore failed: %s", hipGetErrorString(e));
+    return GDN_OK;
 }
 
 gdn_status gdn_selftest_mfma(const float* A, const float* B, float* C, void* stream) {

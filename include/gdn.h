@@ -27,8 +27,9 @@
  * --------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
  *   allocates nothing, keeps no state besides its code objects, and never
- *   synchronises the host; all work is enqueued on `stream` (a hipStream_t;
- *   NULL = the default stream).  Device-side faults surface at the caller's
+ *   synchronises the host (except gdn_selftest_mfma and the gdn_snapshot_*
+ *   calls); all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *   default stream).  Device-side faults surface at the caller's
  *   next synchronisation.
  * - Layouts are row-major, innermost dimension contiguous:
  *     q, k           [tokens][Hk][dk]    (token stride q_stride/k_stride)
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -199,8 +200,8 @@ gdn_status gdn_step(const gdn_layer* layer, const gdn_prefill_io* prefill,
 #define GDN_MAX_VERIFY_TOKENS 16
 
 /* Several tokens per sequence against carried state, in order -- the
- * multi-token verify step of speculative decoding (the pages' drafters
- * propose short blocks: llmxabe README, the speculative-decoding notes).
+ * multi-token verify step of speculative decoding (the block drafters of
+ * the xwen README's speculative-decoding section propose up to 15 tokens).
  * io is read as for gdn_decode except that the token tensors q, k, v, z,
  * a, b and out / core_out hold B * tokens rows, sequence b's tokens at rows
  * b * tokens .. b * tokens + tokens - 1 (token strides as in gdn_decode);
@@ -216,6 +217,60 @@ gdn_status gdn_step(const gdn_layer* layer, const gdn_prefill_io* prefill,
  * GDN_ERR_INVALID_ARGUMENT. */
 gdn_status gdn_decode_multi(const gdn_layer* layer, const gdn_decode_io* io,
                             int32_t tokens, float* state_snapshots, void* stream);
+
+/* ---- session snapshots ------------------------------------------------
+ * Park one sequence's layer state (recurrent + conv) in host memory and
+ * resume it later, in this process or another -- the session swap of
+ * skindeep.ai "Our own inference runtime" ("Session swap": save, inspect,
+ * restore and delete with compatibility checks; a restart-and-continue must
+ * reproduce the output exactly).  A snapshot is a gdn_snapshot_header
+ * followed by the state [Hv][dk][dv] fp32 and the conv state [K-1][Cc] in
+ * the act dtype, byte for byte as they are in device memory, so a restore
+ * continues bit-identically.  Deleting a snapshot is freeing its buffer.
+ * These calls synchronise `stream` (parking is not on the per-token path). */
+#define GDN_SNAPSHOT_MAGIC 0x50534E47u   /* "GNSP" little-endian */
+#define GDN_SNAPSHOT_VERSION 1
+
+typedef struct {
+    uint32_t magic;            /* GDN_SNAPSHOT_MAGIC */
+    uint32_t version;          /* GDN_SNAPSHOT_VERSION */
+    int32_t Hk, Hv, dk, dv;    /* layer geometry the state belongs to */
+    int32_t conv_K;
+    int32_t act_dtype;         /* dtype of the conv state */
+    uint64_t state_bytes;      /* Hv*dk*dv*4 */
+    uint64_t conv_bytes;       /* (K-1)*Cc*act size */
+    uint64_t checksum;         /* FNV-1a 64 over the payload bytes */
+    uint64_t reserved;         /* 0 */
+} gdn_snapshot_header;         /* 64 bytes; the payload follows it */
+
+/* Bytes of one snapshot for this layer (header + payload), 0 on error. */
+size_t gdn_snapshot_bytes(const gdn_layer* layer);
+
+/* Copy pool entry `slot` of state [num_slots][Hv][dk][dv] and conv_state
+ * [num_slots][K-1][Cc] (device) into `host_buf` (host memory, at least
+ * gdn_snapshot_bytes(layer) bytes) and seal it with the header.  Waits for
+ * the stream first, so the state saved is the one after all work enqueued
+ * before this call.  slot outside [0, num_slots) or a short buffer:
+ * GDN_ERR_INVALID_ARGUMENT; nothing is written then. */
+gdn_status gdn_snapshot_save(const gdn_layer* layer, const float* state,
+                             const void* conv_state, int32_t slot,
+                             int32_t num_slots, void* host_buf,
+                             size_t host_bytes, void* stream);
+
+/* Validate a snapshot in host memory (magic, version, sizes, checksum) and
+ * return its header; touches no device.  GDN_ERR_INVALID_ARGUMENT with the
+ * reason in gdn_last_error() when it is not a whole, intact snapshot. */
+gdn_status gdn_snapshot_inspect(const void* host_buf, size_t host_bytes,
+                                gdn_snapshot_header* header);
+
+/* Validate the snapshot as gdn_snapshot_inspect does, check that it belongs
+ * to this layer's geometry and conv dtype (else GDN_ERR_INVALID_ARGUMENT,
+ * nothing written), then copy it into pool entry `slot` of state and
+ * conv_state (device) and wait for the copy to finish. */
+gdn_status gdn_snapshot_restore(const gdn_layer* layer, const void* host_buf,
+                                size_t host_bytes, float* state,
+                                void* conv_state, int32_t slot,
+                                int32_t num_slots, void* stream);
 
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status status);

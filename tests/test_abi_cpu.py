@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 4
+    assert L.gdn_abi_version() == 5
 
 
 def test_status_strings():
@@ -284,7 +284,10 @@ def test_binding_structs_match_the_header(tmp_path):
                                                   "initial_state", "core_out", "state_slots",
                                                   "num_slots"]),
               "gdn_decode_io": (gdn.CDecodeIO, ["B", "q", "b_stride", "state_in", "core_out",
-                                                "state_slots", "num_slots"])}
+                                                "state_slots", "num_slots"]),
+              "gdn_snapshot_header": (gdn.CSnapshotHeader, ["magic", "version", "Hk", "dv",
+                                                            "act_dtype", "state_bytes",
+                                                            "checksum", "reserved"])}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gdn.h"', "int main(void) {"]
     for name, (_, fields) in checks.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
@@ -302,3 +305,71 @@ def test_binding_structs_match_the_header(tmp_path):
         assert int(got[name]) == ctypes.sizeof(cls), name
         for f in fields:
             assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, (name, f)
+
+
+# ---- session snapshots (host-side checks; no device involved) ---------------
+
+def _fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64-bit, from its published definition (offset basis
+    14695981039346656037, prime 1099511628211)."""
+    h = 14695981039346656037
+    for byte in data:
+        h ^= byte
+        h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def _host_snapshot(Hk=2, Hv=4, dk=32, dv=32, act=gdn.GDN_DTYPE_FP32, seed=0):
+    import numpy as np
+    Cc = 2 * Hk * dk + Hv * dv
+    sb, cb = Hv * dk * dv * 4, 3 * Cc * (2 if act == gdn.GDN_DTYPE_BF16 else 4)
+    payload = np.random.default_rng(seed).integers(0, 256, sb + cb, dtype=np.uint8).tobytes()
+    hd = gdn.CSnapshotHeader(gdn.SNAPSHOT_MAGIC, gdn.SNAPSHOT_VERSION, Hk, Hv, dk, dv, 4, act,
+                             sb, cb, _fnv1a64(payload), 0)
+    return bytes(hd) + payload
+
+
+def test_snapshot_size_and_inspect():
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
+                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    Cc = 2 * 16 * 128 + 32 * 128
+    assert gdn.snapshot_bytes(lay) == 64 + 32 * 128 * 128 * 4 + 3 * Cc * 2
+    buf = _host_snapshot()
+    hd = gdn.snapshot_inspect(buf)
+    assert (hd["Hk"], hd["Hv"], hd["dk"], hd["dv"], hd["conv_K"]) == (2, 4, 32, 32, 4)
+    assert hd["state_bytes"] == 4 * 32 * 32 * 4 and hd["conv_bytes"] == 3 * 256 * 4
+
+
+@pytest.mark.parametrize("damage, msg", [
+    (lambda b: b[:40], "shorter than a snapshot header"),
+    (lambda b: b[:-1], "truncated"),
+    (lambda b: b[:100] + bytes([b[100] ^ 1]) + b[101:], "checksum"),
+    (lambda b: bytes([b[0] ^ 0xFF]) + b[1:], "magic"),
+    (lambda b: b[:4] + (2).to_bytes(4, "little") + b[8:], "version"),
+    (lambda b: b[:32] + (7).to_bytes(8, "little") + b[40:], "sizes"),
+])
+def test_snapshot_inspect_rejects_damage(damage, msg):
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.snapshot_inspect(damage(_host_snapshot()))
+    assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT and msg in ei.value.detail
+
+
+def test_snapshot_restore_rejects_another_layer():
+    """A snapshot taken at one geometry or dtype is refused by a layer of
+    another before any device copy (the pointers here are never touched)."""
+    buf = _host_snapshot(Hk=2, Hv=4, dk=32, dv=32, act=gdn.GDN_DTYPE_FP32)
+    for kw in (dict(Hk=2, Hv=4, dk=32, dv=64), dict(Hk=1, Hv=4, dk=32, dv=32),
+               dict(Hk=2, Hv=4, dk=32, dv=32, act_dtype=gdn.GDN_DTYPE_BF16)):
+        lay = gdn.Layer(chunk=16, conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                        dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE), **kw)
+        with pytest.raises(gdn.GdnError) as ei:
+            gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), _FakeTensor(FAKE), slot=0,
+                                 num_slots=1, stream=_FakeStream())
+        assert "does not fit this layer" in ei.value.detail
+    lay = gdn.Layer(Hk=2, Hv=4, dk=32, dv=32, chunk=16, conv_w=_FakeTensor(FAKE),
+                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE),
+                    act_dtype=gdn.GDN_DTYPE_FP32)
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), _FakeTensor(FAKE), slot=3,
+                             num_slots=3, stream=_FakeStream())
+    assert "outside" in ei.value.detail
