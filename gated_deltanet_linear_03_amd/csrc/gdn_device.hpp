@@ -174,11 +174,33 @@ __device__ __forceinline__ u32x4 pack8(const uint16_t* h) {
     return r;
 }
 
-// Deterministic wave-wide sum (xor butterfly: every lane ends with the same
-// bits because each level adds the same two partial sums).
+// Lane swap of a float inside a row of 16 lanes by a DPP control word.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N = 4, 8 or 16 lanes on DPP lane swaps inside a
+// row of 16 (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror): one VALU op per step instead of an LDS permute.  Every lane
+// of a group ends with the same bits: at each step the two partners add the
+// same two values, and fp32 addition is commutative.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    x += dpp_f32<0xB1>(x);                           // quad_perm [1,0,3,2]
+    x += dpp_f32<0x4E>(x);                           // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x += dpp_f32<0x141>(x);    // row_half_mirror
+    if constexpr (N >= 16) x += dpp_f32<0x140>(x);   // row_mirror
+    return x;
+}
+
+// Deterministic wave-wide sum: rows of 16 on DPP swaps, then the four rows
+// through two xor permutes; every lane ends with the same bits.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+    x = group_sum<16>(x);
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
     return x;
 }
 

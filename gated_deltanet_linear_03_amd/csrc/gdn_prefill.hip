@@ -517,8 +517,13 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
     ss = fmaf(o[1], o[1], ss);
     ss = fmaf(o[2], o[2], ss);
     ss = fmaf(o[3], o[3], ss);
+    if constexpr (G::LPR <= 16) {
+        ss = group_sum<G::LPR>(ss);
+    } else {
+        ss = group_sum<16>(ss);
 #pragma unroll
-    for (int off = G::LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+        for (int off = 16; off < G::LPR; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+    }
     const float r = 1.0f / sqrtf(ss / DV + p.eps_rms);
     float y[4];
 #pragma unroll

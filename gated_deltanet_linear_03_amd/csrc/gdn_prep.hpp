@@ -291,8 +291,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                     float ss = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) ss = fmaf(y[t][e], y[t][e], ss);
-#pragma unroll
-                    for (int off = GPRK / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+                    ss = group_sum<GPRK>(ss);
                     const float f = (kind ? 1.0f : p.scale) * __builtin_amdgcn_rsqf(ss + p.eps_l2);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) y[t][e] *= f;
