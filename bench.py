@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--decode-batches", default="64,3,1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the layer-with-projections line")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -459,6 +461,69 @@ def main():
         r = timed_prefill("varlen prefill 8 seqs", lens, 4, 3)
         r["lengths"] = lens
         result["varlen_prefill"] = r
+
+    # ---------------- the layer with its projections, 1 x 4096 ----------------
+    if not args.no_layer:
+        H = synth.HIDDEN
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(21)
+        P = synth.proj_rows(sh)
+        HD = sh.Hv * sh.dv
+        lay = layer_from(case.params)
+        w_in = (torch.randn((P, H), generator=gen, device=dev) / math.sqrt(H)).to(torch.bfloat16)
+        w_out = (torch.randn((H, HD), generator=gen, device=dev) / math.sqrt(HD)).to(torch.bfloat16)
+        proj = gdn.Proj(hidden=H, w_in=w_in, w_out=w_out)
+        xs = [torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3)]
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        lws = torch.empty(gdn.layer_prefill_workspace_bytes(lay, proj, 1, T), dtype=torch.uint8,
+                          device=dev)
+        lfs = torch.empty((1, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+        lcs = torch.empty((1, 3, sh.Cc), dtype=torch.bfloat16, device=dev)
+
+        def layer_step(xx):
+            gdn.layer_prefill_raw(lay, proj, N=1, T_total=T, cu_seqlens=cu, x=xx, y=y,
+                                  final_state=lfs, conv_state_out=lcs, workspace=lws)
+
+        for i in range(W):
+            layer_step(xs[i % 3])
+        l0, l1 = new_events(2)
+        l0.record(stream)
+        for i in range(K):
+            layer_step(xs[i % 3])
+        l1.record(stream)
+        torch.cuda.synchronize()
+        lms = l0.elapsed_time(l1) / K
+        # the two GEMMs alone, same shapes and buffers
+        pbuf = torch.empty((T, P), dtype=torch.bfloat16, device=dev)
+        gbuf = torch.empty((T, HD), dtype=torch.bfloat16, device=dev)
+
+        def gemm_ms(A, B, C):
+            for _ in range(2):
+                gdn.gemm_bf16(A, B, C)
+            g0, g1 = new_events(2)
+            g0.record(stream)
+            for _ in range(K):
+                gdn.gemm_bf16(A, B, C)
+            g1.record(stream)
+            torch.cuda.synchronize()
+            return g0.elapsed_time(g1) / K
+
+        in_ms = gemm_ms(xs[0], w_in, pbuf)
+        out_ms = gemm_ms(gbuf, w_out, y)
+        in_tf = 2 * T * P * H / (in_ms * 1e-3) / 1e12
+        out_tf = 2 * T * HD * H / (out_ms * 1e-3) / 1e12
+        result["layer_with_projections"] = {
+            "hidden": H, "T": T, "ms_per_step": lms, "tokens_per_s": T / (lms * 1e-3),
+            "in_proj_ms": in_ms, "out_proj_ms": out_ms,
+            "in_proj": {"bound": "mfma", "achieved": in_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": in_tf / PEAK_BF16_TFLOPS, "shape": [T, P, H]},
+            "out_proj": {"bound": "mfma", "achieved": out_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": out_tf / PEAK_BF16_TFLOPS, "shape": [T, H, HD]}}
+        log(f"layer with projections (hidden {H}) 1x{T}: {lms:.3f} ms/step "
+            f"({T / (lms * 1e-3):.4g} tok/s); in_proj {in_ms * 1e3:.1f} us = {in_tf:.0f} TFLOP/s, "
+            f"out_proj {out_ms * 1e3:.1f} us = {out_tf:.0f} TFLOP/s")
+        del xs, y, lws, lfs, lcs, pbuf, gbuf, w_in, w_out
+        torch.cuda.empty_cache()
 
     # ---------------- CPU baseline: the fp64 oracle on the host ----------------
     if not args.no_cpu_baseline:

@@ -32,7 +32,8 @@ GDN_DTYPE_BF16 = 1
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
            "gdn_step", "gdn_snapshot_bytes", "gdn_snapshot_save", "gdn_snapshot_inspect",
-           "gdn_snapshot_restore", "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
+           "gdn_snapshot_restore", "gdn_gemm_bf16", "gdn_layer_prefill_workspace_bytes",
+           "gdn_layer_prefill", "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
 PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
@@ -52,6 +53,19 @@ class CSnapshotHeader(ctypes.Structure):
                 ("conv_K", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("state_bytes", ctypes.c_uint64), ("conv_bytes", ctypes.c_uint64),
                 ("checksum", ctypes.c_uint64), ("reserved", ctypes.c_uint64)]
+
+
+class CProj(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("w_in", ctypes.c_void_p), ("w_out", ctypes.c_void_p)]
+
+
+class CLayerIO(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("T_total", ctypes.c_int64),
+                ("cu_seqlens", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("y_dtype", ctypes.c_int32), ("initial_state", ctypes.c_void_p),
+                ("final_state", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
+                ("conv_state_out", ctypes.c_void_p), ("state_slots", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int32)]
 
 
 class CLayer(ctypes.Structure):
@@ -136,6 +150,17 @@ def lib():
         L.gdn_last_error.argtypes = []
         L.gdn_selftest_mfma.restype = ctypes.c_int
         L.gdn_selftest_mfma.argtypes = [ctypes.c_void_p] * 4
+        L.gdn_gemm_bf16.restype = ctypes.c_int
+        L.gdn_gemm_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        L.gdn_layer_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_layer_prefill_workspace_bytes.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CProj),
+                                                        ctypes.c_int32, ctypes.c_int64]
+        L.gdn_layer_prefill.restype = ctypes.c_int
+        L.gdn_layer_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CProj),
+                                        ctypes.POINTER(CLayerIO), ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
         L.gdn_snapshot_bytes.restype = ctypes.c_size_t
         L.gdn_snapshot_bytes.argtypes = [ctypes.POINTER(CLayer)]
         L.gdn_snapshot_save.restype = ctypes.c_int
@@ -407,6 +432,56 @@ def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
     if want_core:
         res["core_out"] = core
     return res
+
+
+def gemm_bf16(A, B, C, stream=None):
+    """C[M, N] = A[M, K] @ B[N, K]^T on the matrix cores: A, B bf16 device
+    tensors (rows may be strided), C bf16 or fp32."""
+    import torch
+    M, K = int(A.shape[0]), int(A.shape[1])
+    N = int(B.shape[0])
+    cd = GDN_DTYPE_BF16 if C.dtype == torch.bfloat16 else GDN_DTYPE_FP32
+    _check(lib().gdn_gemm_bf16(_ptr(A), int(A.stride(0)), _ptr(B), int(B.stride(0)), _ptr(C),
+                               int(C.stride(0)), cd, M, N, K, _stream(stream)))
+
+
+@dataclass
+class Proj:
+    """The projections either side of the layer: w_in [P, hidden] and w_out
+    [hidden, Hv*dv], bf16 device tensors (P = 2 Hk dk + 2 Hv dv + 2 Hv, rows
+    q | k | v | z | a | b)."""
+    hidden: int
+    w_in: object
+    w_out: object
+
+    def c(self) -> CProj:
+        return CProj(self.hidden, _ptr(self.w_in), _ptr(self.w_out))
+
+
+def layer_prefill_workspace_bytes(layer: Layer, proj: Proj, N: int, T_total: int) -> int:
+    cl, cp = layer.c(), proj.c()
+    n = lib().gdn_layer_prefill_workspace_bytes(ctypes.byref(cl), ctypes.byref(cp), int(N), int(T_total))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return int(n)
+
+
+def layer_prefill_raw(layer: Layer, proj: Proj, *, N, T_total, cu_seqlens, x, y,
+                      initial_state=None, final_state=None, conv_state_in=None,
+                      conv_state_out=None, workspace=None, workspace_bytes=None,
+                      state_slots=None, num_slots=0, stream=None):
+    """Call ``gdn_layer_prefill``: x [T, hidden] bf16 -> y [T, hidden] (bf16
+    or fp32), through in_proj, the layer and out_proj."""
+    import torch
+    cl, cp = layer.c(), proj.c()
+    yd = GDN_DTYPE_BF16 if y is not None and y.dtype == torch.bfloat16 else GDN_DTYPE_FP32
+    io = CLayerIO(int(N), int(T_total), _ptr(cu_seqlens), _ptr(x), _ptr(y), yd,
+                  _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
+                  _ptr(conv_state_out), _ptr(state_slots), int(num_slots))
+    nb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    _check(lib().gdn_layer_prefill(ctypes.byref(cl), ctypes.byref(cp), ctypes.byref(io),
+                                   _ptr(workspace), nb, _stream(stream)))
 
 
 def snapshot_bytes(layer: Layer) -> int:

@@ -376,6 +376,122 @@ gdn_status gdn_decode_multi(const gdn_layer* L, const gdn_decode_io* io, int32_t
     return decode_impl(L, io, tokens, state_snapshots, stream);
 }
 
+// ---- projections and the whole layer ---------------------------------------
+
+gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                         int32_t c_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    g_err[0] = 0;
+    if (M < 0 || N < 0 || K < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "M, N, K must be >= 0");
+    if (c_dtype != GDN_DTYPE_BF16 && c_dtype != GDN_DTYPE_FP32)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "c_dtype %d unknown", c_dtype);
+    if (M == 0 || N == 0) return GDN_OK;
+    if (!A || !B || !C) return fail(GDN_ERR_INVALID_ARGUMENT, "NULL operand");
+    if (K % 8 || lda % 8 || ldb % 8 || !aligned(A, 16) || !aligned(B, 16))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "K, lda and ldb must be multiples of 8 and A, B 16-byte aligned");
+    if (lda < K || ldb < K || ldc < N) return fail(GDN_ERR_INVALID_ARGUMENT, "leading dimension below the row length");
+    if (!aligned(C, c_dtype == GDN_DTYPE_BF16 ? 2 : 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "C misaligned");
+    hipError_t e = gdn::launch_gemm_bf16_nt(A, lda, B, ldb, C, ldc, c_dtype == GDN_DTYPE_BF16, M, N, K,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+namespace {
+
+struct LayerWs {
+    int64_t P = 0, off_proj = 0, off_gated = 0, off_pf = 0, total = 0;
+};
+
+gdn_status layer_ws(const gdn_layer* L, const gdn_proj* pr, int32_t N, int64_t T, LayerWs* w) {
+    gdn_status st = check_layer(L, true);
+    if (st != GDN_OK) return st;
+    if (!pr) return fail(GDN_ERR_INVALID_ARGUMENT, "proj is NULL");
+    if (pr->hidden <= 0 || pr->hidden % 8) return fail(GDN_ERR_INVALID_ARGUMENT, "hidden (%d) must be a positive multiple of 8", pr->hidden);
+    if (L->act_dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_INVALID_ARGUMENT, "the layer path needs act_dtype bf16");
+    if (N < 0 || T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "N and T_total must be >= 0");
+    w->P = 2ll * L->Hk * L->dk + 2ll * L->Hv * L->dv + 2ll * L->Hv;
+    if ((2ll * L->Hk * L->dk) % 8 || (static_cast<int64_t>(L->Hv) * L->dv) % 8 || w->P % 8)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "projection widths must be multiples of 8");
+    int64_t o = 0;
+    w->off_proj = o;
+    o = round_up(o + 2 * T * w->P, 256);
+    w->off_gated = o;
+    o = round_up(o + 2 * T * static_cast<int64_t>(L->Hv) * L->dv, 256);
+    w->off_pf = o;
+    w->total = o + ws_layout(L, N, T, true, 0).total;
+    return GDN_OK;
+}
+
+}  // namespace
+
+size_t gdn_layer_prefill_workspace_bytes(const gdn_layer* L, const gdn_proj* pr, int32_t N, int64_t T) {
+    g_err[0] = 0;
+    LayerWs w;
+    if (layer_ws(L, pr, N, T, &w) != GDN_OK) return 0;
+    return static_cast<size_t>(w.total);
+}
+
+gdn_status gdn_layer_prefill(const gdn_layer* L, const gdn_proj* pr, const gdn_layer_io* io, void* ws,
+                             size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
+    LayerWs w;
+    gdn_status st = layer_ws(L, pr, io->N, io->T_total, &w);
+    if (st != GDN_OK) return st;
+    const int64_t T = io->T_total;
+    const int64_t HD = static_cast<int64_t>(L->Hv) * L->dv;
+    if (T > 0 && (!io->x || !io->y || !pr->w_in || !pr->w_out))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "x, y, w_in and w_out are required");
+    if (io->y_dtype != GDN_DTYPE_BF16 && io->y_dtype != GDN_DTYPE_FP32)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "y_dtype %d unknown", io->y_dtype);
+    if (T > 0 && (!aligned(io->x, 16) || !aligned(pr->w_in, 16) || !aligned(pr->w_out, 16) || !aligned(io->y, 16)))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "x, y, w_in and w_out must be 16-byte aligned");
+    if (!ws || !aligned(ws, 256)) return fail(GDN_ERR_WORKSPACE, "workspace missing or not 256-byte aligned");
+    if (static_cast<int64_t>(ws_bytes) < w.off_pf)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, the layer needs %lld", ws_bytes,
+                    static_cast<long long>(w.total));
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint16_t* proj = reinterpret_cast<uint16_t*>(base + w.off_proj);
+    uint16_t* gated = reinterpret_cast<uint16_t*>(base + w.off_gated);
+    const int64_t qk = static_cast<int64_t>(L->Hk) * L->dk;
+
+    gdn_layer Lg = *L;                  // the gated output feeds out_proj as bf16
+    Lg.out_dtype = GDN_DTYPE_BF16;
+    gdn_prefill_io pio{};
+    pio.N = io->N;
+    pio.T_total = T;
+    pio.cu_seqlens = io->cu_seqlens;
+    pio.q = proj;
+    pio.k = proj + qk;
+    pio.v = proj + 2 * qk;
+    pio.z = proj + 2 * qk + HD;
+    pio.a = proj + 2 * qk + 2 * HD;
+    pio.b = proj + 2 * qk + 2 * HD + L->Hv;
+    pio.q_stride = pio.k_stride = pio.v_stride = pio.z_stride = pio.a_stride = pio.b_stride = w.P;
+    pio.initial_state = io->initial_state;
+    pio.final_state = io->final_state;
+    pio.conv_state_in = io->conv_state_in;
+    pio.conv_state_out = io->conv_state_out;
+    pio.out = gated;
+    pio.core_out = nullptr;
+    pio.state_slots = io->state_slots;
+    pio.num_slots = io->num_slots;
+    // validate the prefill part before enqueueing anything
+    st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr, false);
+    if (st != GDN_OK) return st;
+    if (T == 0) return prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, T, w.P,
+                                            pr->hidden, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
+    st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
+    if (st != GDN_OK) return st;
+    e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, T,
+                                 pr->hidden, HD, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 // ---- session snapshots ------------------------------------------------------
 
 static_assert(sizeof(gdn_snapshot_header) == 64, "snapshot header is 64 bytes");

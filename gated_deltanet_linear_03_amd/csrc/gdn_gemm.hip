@@ -1,0 +1,175 @@
+// gdn_gemm.hip -- the layer's projections as bf16 matrix-core GEMMs.
+//
+// C[M][N] = A[M][K] * B[N][K]^T, bf16 operands with fp32 accumulation, bf16
+// or fp32 output: A is the activations (row-major, k contiguous) and B a
+// weight matrix in the [out][in] layout, so both operands load as 16-byte
+// runs along k, which is the k-contiguous fragment order of
+// v_mfma_f32_16x16x32_bf16 (lane l holds row / column l % 16, k = 8*(l/16)+e).
+//
+// A work-group computes a 256 x 256 tile (256 x 128 when that leaves compute
+// units idle) with 8 waves, two per SIMD; at 256 x 256 each wave owns 128 x
+// 64 (8 x 4 matrix-core tiles of 16 x 16: 12 fragment reads from LDS per 32
+// products).  The k loop runs over BK = 64 slices with two LDS stages: while
+// the waves multiply slice k, slice k+1 comes from global memory into
+// registers and then into the other stage, one barrier per slice.  Rows past
+// M or N and k past K read as zeros; only in-range outputs are stored.
+#include "gdn_device.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kBK = 64;
+constexpr int kGemmThreads = 512;             // 8 waves, two per SIMD
+constexpr int kLS = kBK + 8;                  // LDS row stride (bf16) of both tiles
+
+// BM x BN work-group tile; the 8 waves are WGM x WGN, each owning a
+// (BM/WGM) x (BN/WGN) block of 16 x 16 matrix-core tiles.
+template <int BM, int BN>
+struct GemmGeom {
+    static constexpr int WGM = BN == 256 ? 2 : 4, WGN = 8 / WGM;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int TM = WM / 16, TN = WN / 16;
+    static constexpr int AC = BM * kBK / 8 / kGemmThreads;    // 16-byte loads per thread (A)
+    static constexpr int BC = BN * kBK / 8 / kGemmThreads;    // (B)
+    static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0 && AC >= 1 && BC >= 1, "tile");
+};
+
+template <int BM, int BN, bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_nt_kernel(
+        const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+        void* __restrict__ Cv, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    using G = GemmGeom<BM, BN>;
+    // two LDS stages: slice k is multiplied from one while slice k+1 is
+    // written into the other
+    __shared__ __align__(16) uint16_t As[2][BM * kLS];
+    __shared__ __align__(16) uint16_t Bs[2][BN * kLS];
+
+    // tile order: consecutive work-groups walk down M inside one N column of
+    // tiles, so a B (weight) slice is shared in L2 by the work-groups near it
+    const int64_t mtiles = (M + BM - 1) / BM;
+    const int64_t m0 = (blockIdx.x % mtiles) * BM, n0 = (blockIdx.x / mtiles) * BN;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int l16 = lane % 16, lq = lane / 16;
+    const int wm = wave / G::WGN, wn = wave % G::WGN;
+
+    // global -> register staging: chunk c of a tile is row c / 8, k 8*(c % 8)
+    u32x4 ra[G::AC], rb[G::BC];
+    auto load_tiles = [&](int64_t k0) {
+#pragma unroll
+        for (int u = 0; u < G::AC; ++u) {
+            const int c = tid + u * kGemmThreads;
+            const int64_t r = m0 + c / 8, k = k0 + 8 * (c % 8);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (r < M && k < K) v = *reinterpret_cast<const u32x4*>(A + r * lda + k);
+            ra[u] = v;
+        }
+#pragma unroll
+        for (int u = 0; u < G::BC; ++u) {
+            const int c = tid + u * kGemmThreads;
+            const int64_t r = n0 + c / 8, k = k0 + 8 * (c % 8);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (r < N && k < K) v = *reinterpret_cast<const u32x4*>(B + r * ldb + k);
+            rb[u] = v;
+        }
+    };
+    auto store_tiles = [&](int st) {
+#pragma unroll
+        for (int u = 0; u < G::AC; ++u) {
+            const int c = tid + u * kGemmThreads;
+            *reinterpret_cast<u32x4*>(&As[st][(c / 8) * kLS + 8 * (c % 8)]) = ra[u];
+        }
+#pragma unroll
+        for (int u = 0; u < G::BC; ++u) {
+            const int c = tid + u * kGemmThreads;
+            *reinterpret_cast<u32x4*>(&Bs[st][(c / 8) * kLS + 8 * (c % 8)]) = rb[u];
+        }
+    };
+
+    f32x4 acc[G::TM][G::TN];
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_tiles(0);
+    store_tiles(0);
+    __syncthreads();
+    int st = 0;
+    for (int64_t k0 = 0; k0 < K; k0 += kBK) {
+        const bool more = k0 + kBK < K;
+        if (more) load_tiles(k0 + kBK);            // next slice in flight during the products
+        const uint16_t* as = As[st];
+        const uint16_t* bs = Bs[st];
+#pragma unroll
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            u32x4 fb[G::TN];
+#pragma unroll
+            for (int j = 0; j < G::TN; ++j)
+                fb[j] = *reinterpret_cast<const u32x4*>(&bs[(wn * G::WN + j * 16 + l16) * kLS + ks * 32 + lq * 8]);
+#pragma unroll
+            for (int i = 0; i < G::TM; ++i) {
+                const u32x4 fa = *reinterpret_cast<const u32x4*>(&as[(wm * G::WM + i * 16 + l16) * kLS + ks * 32 + lq * 8]);
+#pragma unroll
+                for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma(fa, fb[j], acc[i][j]);
+            }
+        }
+        if (more) store_tiles(st ^ 1);             // the other stage: nobody reads it now
+        __syncthreads();
+        st ^= 1;
+    }
+
+    // C/D fragment: lane holds column l16 and rows 4*lq + e of each 16 x 16 tile
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) {
+            const int64_t col = n0 + wn * G::WN + j * 16 + l16;
+            if (col >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * G::WM + i * 16 + lq * 4 + e;
+                if (row >= M) continue;
+                if constexpr (OUT_BF16)
+                    static_cast<uint16_t*>(Cv)[row * ldc + col] = f32_to_bf16_bits(acc[i][j][e]);
+                else
+                    static_cast<float*>(Cv)[row * ldc + col] = acc[i][j][e];
+            }
+        }
+    }
+}
+
+template <int BM, int BN>
+hipError_t launch_gemm_t(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, void* C,
+                         int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (out_bf16)
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, true>), dim3(static_cast<unsigned>(tiles)),
+                           dim3(kGemmThreads), 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, false>), dim3(static_cast<unsigned>(tiles)),
+                           dim3(kGemmThreads), 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                               int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K,
+                               hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const auto a = static_cast<const uint16_t*>(A);
+    const auto b = static_cast<const uint16_t*>(B);
+    // 256 x 256 tiles when they still give every compute unit work, else
+    // 256 x 128
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
+    if (wide >= cus) return launch_gemm_t<256, 256>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);
+    return launch_gemm_t<256, 128>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);
+}
+
+}  // namespace gdn

@@ -109,5 +109,9 @@ hipError_t launch_prefill(int DK, int DV, int C, bool bf16, const PrefillParams&
 bool prefill_shape_supported(int DK, int DV, int C);
 bool decode_shape_supported(int DK, int DV);
 hipError_t launch_selftest_mfma(const float* A, const float* B, float* C, hipStream_t s);
+// C[M][N] = A[M][K] B[N][K]^T, bf16 in, fp32 accumulation, bf16 or fp32 out
+hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                               int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K,
+                               hipStream_t s);
 
 }  // namespace gdn

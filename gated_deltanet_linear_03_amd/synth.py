@@ -94,6 +94,30 @@ def layer_params(shape: LayerShape, seed: int, norm_w_jitter: bool = False,
             "norm_w": norm_w}
 
 
+HIDDEN = 2048        # model width of the 35B-A3B shape (see the projection docs)
+
+
+def proj_rows(shape: LayerShape) -> int:
+    """Output rows of in_proj: q | k | v | z | a | b."""
+    return 2 * shape.Hk * shape.dk + 2 * shape.Hv * shape.dv + 2 * shape.Hv
+
+
+def proj_weights(shape: LayerShape, hidden: int, seed: int):
+    """w_in [P, hidden] and w_out [hidden, Hv*dv], N(0, 1/fan_in), rounded to
+    bf16 (values held as fp32 arrays), so projections of N(0, 1) inputs have
+    unit variance like the token inputs."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+    w_in = bf16_round(_normal(rng, (proj_rows(shape), hidden), 1.0 / math.sqrt(hidden)))
+    w_out = bf16_round(_normal(rng, (hidden, shape.Hv * shape.dv), 1.0 / math.sqrt(shape.Hv * shape.dv)))
+    return w_in, w_out
+
+
+def hidden_inputs(T: int, hidden: int, seed: int):
+    """x [T, hidden] ~ N(0, 1), rounded to bf16 (as fp32 values)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    return bf16_round(_normal(rng, (T, hidden)))
+
+
 TOKEN_BLOCK = 4096
 
 

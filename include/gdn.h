@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
     GDN_OK = 0,
@@ -217,6 +217,61 @@ gdn_status gdn_step(const gdn_layer* layer, const gdn_prefill_io* prefill,
  * GDN_ERR_INVALID_ARGUMENT. */
 gdn_status gdn_decode_multi(const gdn_layer* layer, const gdn_decode_io* io,
                             int32_t tokens, float* state_snapshots, void* stream);
+
+/* ---- the projections either side of the layer --------------------------
+ * in_proj maps the model's hidden state to q, k, v, z, a, b and out_proj
+ * maps the gated output back (llmxabe README, model section: the hybrid
+ * stack around these layers; its LM-head figure, 540 MB per token for an
+ * untied 248,320-row head, fits a width of 2048 at 8.5 bits per weight).
+ * Both are bf16 GEMMs on the matrix cores with fp32 accumulation. */
+
+/* C[M][N] = A[M][K] * B[N][K]^T: A, B bf16 (k contiguous, leading dims lda,
+ * ldb in elements), C in c_dtype (GDN_DTYPE_BF16 or GDN_DTYPE_FP32, leading
+ * dim ldc), fp32 accumulation.  K, lda, ldb multiples of 8 and A, B 16-byte
+ * aligned; M, N, K >= 0.  Enqueued on `stream`. */
+gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
+                         void* C, int64_t ldc, int32_t c_dtype, int64_t M,
+                         int64_t N, int64_t K, void* stream);
+
+typedef struct {
+    int32_t hidden;         /* model width; a multiple of 8 */
+    const void* w_in;       /* [P][hidden] bf16, P = 2*Hk*dk + 2*Hv*dv + 2*Hv
+                             * output rows ordered q (head-major) | k | v | z |
+                             * a | b, so the conv channels q|k|v come first */
+    const void* w_out;      /* [hidden][Hv*dv] bf16 */
+} gdn_proj;
+
+/* One sequence batch through the whole layer: x [T][hidden] bf16 in, y
+ * [T][hidden] in y_dtype out; states and cu_seqlens as in gdn_prefill_io. */
+typedef struct {
+    int32_t N;
+    int64_t T_total;
+    const int32_t* cu_seqlens;
+    const void* x;
+    void* y;
+    int32_t y_dtype;               /* GDN_DTYPE_BF16 or GDN_DTYPE_FP32 */
+    const float* initial_state;    /* optional, as in gdn_prefill_io */
+    float* final_state;
+    const void* conv_state_in;
+    void* conv_state_out;
+    const int32_t* state_slots;    /* optional pool entries */
+    int32_t num_slots;
+} gdn_layer_io;
+
+/* Workspace of gdn_layer_prefill: the projection [T][P] bf16, the gated
+ * output [T][Hv*dv] bf16 and gdn_prefill's own workspace. */
+size_t gdn_layer_prefill_workspace_bytes(const gdn_layer* layer,
+                                         const gdn_proj* proj, int32_t N,
+                                         int64_t T_total);
+
+/* in_proj GEMM -> gdn_prefill on views into the projection (token stride
+ * P) -> out_proj GEMM, on `stream`.  The layer's act_dtype must be bf16 (the
+ * projection's dtype); the gated output between the GDN and out_proj is
+ * bf16 whatever the layer's out_dtype.  Same validation and error
+ * behaviour as gdn_prefill, plus the projection's shapes. */
+gdn_status gdn_layer_prefill(const gdn_layer* layer, const gdn_proj* proj,
+                             const gdn_layer_io* io, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---- session snapshots ------------------------------------------------
  * Park one sequence's layer state (recurrent + conv) in host memory and

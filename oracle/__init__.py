@@ -8,7 +8,8 @@ layer's arithmetic.
 
 ``gdn_oracle.c`` is the token-by-token fp64 definition (conv1d + SiLU, L2
 norm, gates, the gated delta rule of Yang, Kautz and Hatamizadeh, "Gated
-Delta Networks", ICLR 2025, and the SiLU(z)-gated RMSNorm).  ``chunked.py``
+Delta Networks", ICLR 2025, and the SiLU(z)-gated RMSNorm).  ``layer_forward``
+adds the projections either side (matrix products in fp64).  ``chunked.py``
 is a second, chunk-parallel fp64 form of the same recurrence that exists only
 to pin the chunk algebra against the sequential definition.
 
@@ -194,3 +195,37 @@ def gdn_forward(dims: Dims, cu_seqlens, q, k, v, z, a, b, conv_w, A_log,
         raise ValueError("oracle_gdn_forward rejected its arguments")
     return {"out": out, "core_out": core, "final_state": fs,
             "conv_state_out": cs}
+
+
+def round_bf16(x):
+    """Round to the nearest bf16 value, ties to even (the dtype the layer's
+    projection and gated output are handed over in), from float64 through
+    float32: fp64 -> fp32 rounds to nearest, then the 16 low bits of the fp32
+    pattern are rounded off to nearest-even."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def layer_forward(dims: Dims, cu_seqlens, x, w_in, w_out, conv_w, A_log, dt_bias,
+                  norm_w, state_in=None, conv_state_in=None, nthreads: int = 0):
+    """The layer with its projections: proj = x w_in^T handed over in bf16,
+    split into q | k | v | z | a | b, the layer above, its gated output handed
+    over in bf16, y = out w_out^T.  x [T, hidden]; w_in [P, hidden]; w_out
+    [hidden, Hv*dv].  Returns gdn_forward's dict plus y (float64)."""
+    x, w_in, w_out = _f64(x), _f64(w_in), _f64(w_out)
+    T = x.shape[0]
+    qk, hd = dims.Hk * dims.dk, dims.Hv * dims.dv
+    proj = round_bf16(x @ w_in.T)
+    q = proj[:, :qk].reshape(T, dims.Hk, dims.dk)
+    k = proj[:, qk:2 * qk].reshape(T, dims.Hk, dims.dk)
+    v = proj[:, 2 * qk:2 * qk + hd].reshape(T, dims.Hv, dims.dv)
+    z = proj[:, 2 * qk + hd:2 * qk + 2 * hd].reshape(T, dims.Hv, dims.dv)
+    a = proj[:, 2 * qk + 2 * hd:2 * qk + 2 * hd + dims.Hv]
+    b = proj[:, 2 * qk + 2 * hd + dims.Hv:]
+    res = gdn_forward(dims, cu_seqlens, q, k, v, z, a, b, conv_w, A_log, dt_bias, norm_w,
+                      state_in=state_in, conv_state_in=conv_state_in, nthreads=nthreads)
+    res["y"] = round_bf16(res["out"]).reshape(T, hd) @ w_out.T
+    res["proj"] = proj
+    return res

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 5
+    assert L.gdn_abi_version() == 6
 
 
 def test_status_strings():
@@ -287,7 +287,11 @@ def test_binding_structs_match_the_header(tmp_path):
                                                 "state_slots", "num_slots"]),
               "gdn_snapshot_header": (gdn.CSnapshotHeader, ["magic", "version", "Hk", "dv",
                                                             "act_dtype", "state_bytes",
-                                                            "checksum", "reserved"])}
+                                                            "checksum", "reserved"]),
+              "gdn_proj": (gdn.CProj, ["hidden", "w_in", "w_out"]),
+              "gdn_layer_io": (gdn.CLayerIO, ["N", "T_total", "cu_seqlens", "x", "y", "y_dtype",
+                                              "initial_state", "conv_state_out", "state_slots",
+                                              "num_slots"])}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gdn.h"', "int main(void) {"]
     for name, (_, fields) in checks.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
@@ -373,3 +377,43 @@ def test_snapshot_restore_rejects_another_layer():
         gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), _FakeTensor(FAKE), slot=3,
                              num_slots=3, stream=_FakeStream())
     assert "outside" in ei.value.detail
+
+
+# ---- projections and the whole layer (host-side checks) ---------------------
+
+@pytest.mark.parametrize("kw, msg", [
+    (dict(K=12), "multiples of 8"),
+    (dict(lda=4, K=8), "multiples of 8"),
+    (dict(c_dtype=7), "c_dtype"),
+    (dict(M=-1), ">= 0"),
+    (dict(ldc=2), "leading dimension"),
+])
+def test_gemm_rejects(kw, msg):
+    args = dict(A=FAKE, lda=16, B=FAKE, ldb=16, C=FAKE, ldc=8, c_dtype=gdn.GDN_DTYPE_FP32,
+                M=4, N=8, K=16)
+    args.update(kw)
+    st = gdn.lib().gdn_gemm_bf16(args["A"], args["lda"], args["B"], args["ldb"], args["C"],
+                                 args["ldc"], args["c_dtype"], args["M"], args["N"], args["K"], None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and msg in gdn.lib().gdn_last_error().decode()
+
+
+def test_layer_workspace_and_rejects():
+    """The layer workspace is the bf16 projection [T][P], the bf16 gated
+    output [T][Hv dv] (each 256-byte rounded) and gdn_prefill's workspace;
+    fp32 activations are refused (the projection is handed over in bf16)."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
+                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE), w_out=_FakeTensor(FAKE))
+    T = 4096
+    P = 2 * 16 * 128 + 2 * 32 * 128 + 2 * 32
+    rnd = lambda n: -(-n // 256) * 256
+    assert gdn.layer_prefill_workspace_bytes(lay, proj, 1, T) == (
+        rnd(2 * T * P) + rnd(2 * T * 32 * 128) + gdn.prefill_workspace_bytes(lay, 1, T))
+    lay32 = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
+                      A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE),
+                      act_dtype=gdn.GDN_DTYPE_FP32)
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.layer_prefill_workspace_bytes(lay32, proj, 1, T)
+    assert "bf16" in ei.value.detail
+    with pytest.raises(gdn.GdnError):
+        gdn.layer_prefill_workspace_bytes(lay, gdn.Proj(hidden=2047, w_in=None, w_out=None), 1, T)

@@ -1,0 +1,115 @@
+"""The projections either side of the layer: the bf16 matrix-core GEMM
+against fp64 products of the same bf16 values, and gdn_layer_prefill
+(in_proj -> layer -> out_proj) against the oracle's layer_forward."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_linear_03_amd as gdn
+import oracle
+from gated_deltanet_linear_03_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import TOL, dims, make_layer, per_seq_errors, state_errors, to_dev  # noqa: E402
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M, N, K", [(300, 200, 136), (1, 392, 64), (257, 12352, 2048),
+                                     (64, 2048, 4096)])
+def test_gemm_matches_fp64(M, N, K):
+    r = np.random.default_rng(M + N + K)
+    A = synth.bf16_round(r.standard_normal((M, K)).astype(np.float32))
+    B = synth.bf16_round((r.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    C16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gdn.gemm_bf16(_bf16(A), _bf16(B), C32)
+    gdn.gemm_bf16(_bf16(A), _bf16(B), C16)
+    torch.cuda.synchronize()
+    got = C32.cpu().numpy().astype(np.float64)
+    # fp32 accumulation of K exact products: a few ulp of the largest partial sum
+    bound = 4 * K * 2.0 ** -24 * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+    # bf16 output: the nearest bf16 of the fp32 result
+    assert torch.equal(C16.float(), C32.to(torch.bfloat16).float())
+
+
+def test_gemm_strided_rows():
+    """Row strides beyond K (views into wider buffers)."""
+    r = np.random.default_rng(3)
+    M, N, K = 130, 70, 96
+    Aw = _bf16(r.standard_normal((M, K + 24)))
+    Bw = _bf16(r.standard_normal((N, K + 8)))
+    A, B = Aw[:, 8:8 + K], Bw[:, :K]
+    Cw = torch.zeros((M, N + 5), dtype=torch.float32, device="cuda")
+    gdn.gemm_bf16(A, B, Cw[:, :N])
+    torch.cuda.synchronize()
+    ref = A.float().cpu().double() @ B.float().cpu().double().T
+    assert torch.allclose(Cw[:, :N].cpu().double(), ref, rtol=1e-5, atol=1e-5)
+    assert not Cw[:, N:].any()
+
+
+def _layer_case(sh, hidden, lens, seed, with_states):
+    p = synth.layer_params(sh, seed)
+    w_in, w_out = synth.proj_weights(sh, hidden, seed)
+    cu = synth.cu_from_lengths(lens)
+    T, N = int(cu[-1]), len(lens)
+    x = synth.hidden_inputs(T, hidden, seed)
+    S0 = synth.initial_states(sh, N, seed) if with_states else None
+    C0 = synth.conv_states(sh, N, seed) if with_states else None
+    return p, w_in, w_out, cu, x, S0, C0
+
+
+def _run_layer(sh, hidden, p, w_in, w_out, cu, x, S0, C0):
+    layer = make_layer(sh, p)
+    proj = gdn.Proj(hidden=hidden, w_in=_bf16(w_in), w_out=_bf16(w_out))
+    T, N = int(cu[-1]), len(cu) - 1
+    y = torch.empty((T, hidden), dtype=torch.float32, device="cuda")
+    fs = torch.empty((N, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device="cuda")
+    cs = torch.empty((N, sh.K - 1, sh.Cc), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.layer_prefill_workspace_bytes(layer, proj, N, T), dtype=torch.uint8,
+                     device="cuda")
+    gdn.layer_prefill_raw(layer, proj, N=N, T_total=T, cu_seqlens=to_dev(cu), x=_bf16(x), y=y,
+                          initial_state=None if S0 is None else to_dev(S0), final_state=fs,
+                          conv_state_in=None if C0 is None else _bf16(C0), conv_state_out=cs,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), fs.cpu().numpy(), cs.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("shape, hidden, lens, states", [
+    ("small", 64, [37, 0, 27, 1, 16], True),
+    ("full", 2048, [200], False),
+    ("full", 2048, [70, 5, 130], True),
+])
+def test_layer_prefill_parity(shape, hidden, lens, states):
+    sh = synth.FULL if shape == "full" else synth.LayerShape(Hk=2, Hv=4, dk=32, dv=32, chunk=16)
+    p, w_in, w_out, cu, x, S0, C0 = _layer_case(sh, hidden, lens, 601, states)
+    y, fs, cs = _run_layer(sh, hidden, p, w_in, w_out, cu, x, S0, C0)
+    ref = oracle.layer_forward(dims(sh), cu, x, w_in, w_out, p["conv_w"], p["A_log"],
+                               p["dt_bias"], p["norm_w"], state_in=S0, conv_state_in=C0)
+    e_y = per_seq_errors(cu, y, ref["y"])
+    e_s = state_errors(fs, ref["final_state"])
+    print(f"layer {shape} {lens}: y {e_y:.3e} state {e_s:.3e}", flush=True)
+    assert e_s < TOL
+    # y: the gated output is handed to out_proj in bf16 on both sides, from
+    # values that differ within the layer's tolerance, so an element may round
+    # one bf16 ulp (2^-8 relative) apart; bound each y by that over its
+    # |products| plus the layer tolerance of the sequence's largest |y|
+    T = int(cu[-1])
+    g = np.abs(oracle.round_bf16(ref["out"]).reshape(T, -1))
+    handover = 2.0 ** -8 * (g @ np.abs(w_out.astype(np.float64)).T)
+    for n_ in range(len(cu) - 1):
+        a, b = int(cu[n_]), int(cu[n_ + 1])
+        if b > a:
+            scale = np.abs(ref["y"][a:b]).max()
+            assert np.all(np.abs(y[a:b] - ref["y"][a:b]) <= handover[a:b] + TOL * scale), n_
+    # the conv state holds raw projection values: the nearest bf16 of the same
+    # product on both sides, which fp32 and fp64 sums may round one ulp apart
+    d = np.abs(cs - ref["conv_state_out"])
+    assert np.all(d <= 2.0 ** -7 * np.abs(ref["conv_state_out"]) + 1e-30)
+    assert (d > 0).mean() < 0.01

@@ -218,3 +218,62 @@ def test_synth_bf16_rounding_is_nearest_even():
     assert y[3] == 1.0
     assert np.all((y.view(np.uint32) & 0xFFFF) == 0)
     assert abs(y[4] - x[4]) <= abs(x[4]) * 2**-8
+
+
+# ---- the projections either side --------------------------------------------
+
+def test_round_bf16_is_nearest_even():
+    """Values straddling bf16's 8-bit mantissa: ties go to the even pattern,
+    others to the nearest; exactly representable values pass through."""
+    one = 1.0
+    ulp = 2.0 ** -7                      # bf16 spacing in [1, 2)
+    x = np.array([one, one + ulp / 2, one + 3 * ulp / 2, one + ulp / 2 + 2.0 ** -20,
+                  -(one + ulp / 2), 3.0, 2.0 ** -130])
+    want = np.array([one, one, one + 2 * ulp, one + ulp, -one, 3.0, 2.0 ** -130])
+    assert np.array_equal(oracle.round_bf16(x), want)
+
+
+def test_layer_forward_with_identity_projections_is_the_layer():
+    """in_proj = identity (hidden = P) and out_proj = [I; 0] reduce
+    layer_forward to gdn_forward on the input columns, its gated output
+    rounded to bf16 in the first Hv*dv columns of y and zeros after."""
+    d = _dims()
+    T = 23
+    P = 2 * d.Hk * d.dk + 2 * d.Hv * d.dv + 2 * d.Hv
+    hd = d.Hv * d.dv
+    r = np.random.default_rng(5)
+    x = oracle.round_bf16(r.standard_normal((T, P)))
+    w_in = np.eye(P)
+    w_out = np.zeros((P, hd))
+    w_out[:hd] = np.eye(hd)
+    p = _params(d, 6)
+    cu = np.array([0, 9, 9, 23])
+    res = oracle.layer_forward(d, cu, x, w_in, w_out, p["conv_w"], p["A_log"], p["dt_bias"],
+                               p["norm_w"])
+    qk = d.Hk * d.dk
+    cols = dict(q=x[:, :qk].reshape(T, d.Hk, d.dk), k=x[:, qk:2 * qk].reshape(T, d.Hk, d.dk),
+                v=x[:, 2 * qk:2 * qk + hd].reshape(T, d.Hv, d.dv),
+                z=x[:, 2 * qk + hd:2 * qk + 2 * hd].reshape(T, d.Hv, d.dv),
+                a=x[:, 2 * qk + 2 * hd:2 * qk + 2 * hd + d.Hv], b=x[:, 2 * qk + 2 * hd + d.Hv:])
+    ref = _run(d, cu, cols, p)
+    assert np.array_equal(res["out"], ref["out"])
+    assert np.array_equal(res["y"][:, :hd], oracle.round_bf16(ref["out"]).reshape(T, hd))
+    assert not res["y"][:, hd:].any()
+
+
+def test_layer_forward_projection_is_linear():
+    """y scales with w_out and the projection is x w_in^T before rounding:
+    doubling w_out doubles y exactly (powers of two commute with rounding)."""
+    d = _dims()
+    T, hidden = 11, 16
+    P = 2 * d.Hk * d.dk + 2 * d.Hv * d.dv + 2 * d.Hv
+    r = np.random.default_rng(7)
+    x = oracle.round_bf16(r.standard_normal((T, hidden)))
+    w_in = oracle.round_bf16(r.standard_normal((P, hidden)) / 4)
+    w_out = oracle.round_bf16(r.standard_normal((hidden, d.Hv * d.dv)) / 8)
+    p = _params(d, 8)
+    cu = np.array([0, T])
+    a = oracle.layer_forward(d, cu, x, w_in, w_out, p["conv_w"], p["A_log"], p["dt_bias"], p["norm_w"])
+    b = oracle.layer_forward(d, cu, x, w_in, 2 * w_out, p["conv_w"], p["A_log"], p["dt_bias"], p["norm_w"])
+    assert np.array_equal(b["y"], 2 * a["y"])
+    assert np.allclose(a["proj"], x @ w_in.T, rtol=2 ** -8, atol=0)
