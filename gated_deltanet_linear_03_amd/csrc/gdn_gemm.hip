@@ -141,16 +141,153 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_nt_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// K % 32 == 0: the k loop streams 32-wide slices straight from global memory
+// into four LDS stages (global_load_lds_dwordx4: each lane's 16 bytes land at
+// the wave's LDS block + 16 * lane, no registers in between), so a slice is
+// requested three slices before it is multiplied.  A stage holds rows of 32
+// bf16 (64 bytes) with the 16-byte chunks of row r permuted by
+// chunk ^ ((r >> 2) & 3), which keeps a 16-lane fragment read on 16 distinct
+// groups of four banks.
+// ---------------------------------------------------------------------------
+constexpr int kSK = 32;                       // k per stage
+constexpr int kStages = 4;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+template <int BM, int BN, bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_nt_dma_kernel(
+        const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+        void* __restrict__ Cv, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    using G = GemmGeom<BM, BN>;
+    constexpr int AW = BM * kSK * 2 / 1024, BW = BN * kSK * 2 / 1024;   // 1 KiB wave loads per stage
+    constexpr int NW = kGemmThreads / kWave;
+    static_assert(AW % NW == 0 && BW % NW == 0, "loads per wave");
+    __shared__ __align__(1024) uint16_t As0[BM * kSK], As1[BM * kSK], As2[BM * kSK], As3[BM * kSK];
+    __shared__ __align__(1024) uint16_t Bs0[BN * kSK], Bs1[BN * kSK], Bs2[BN * kSK], Bs3[BN * kSK];
+
+    const int64_t mtiles = (M + BM - 1) / BM;
+    const int64_t m0 = (blockIdx.x % mtiles) * BM, n0 = (blockIdx.x / mtiles) * BN;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int l16 = lane % 16, lq = lane / 16;
+    const int wm = wave / G::WGN, wn = wave % G::WGN;
+
+    // wave load j of a stage covers rows 16 j .. 16 j + 15; lane l fills
+    // physical chunk l % 4 of row 16 j + l / 4, i.e. logical chunk
+    // swz(row, l % 4) of that row; rows past M / N read row 0 (their outputs
+    // are never stored).  Stages are separate LDS objects addressed with
+    // compile-time indices, so the compiler can tell that a slice's reads do
+    // not depend on the loads still in flight into the other stages.
+    const int lrow = lane / 4, lpc = lane % 4;
+    auto issue = [&](uint16_t* as, uint16_t* bs, int64_t k0) {
+#pragma unroll
+        for (int u = 0; u < AW / NW; ++u) {
+            const int j = wave + u * NW;
+            const int row = 16 * j + lrow;
+            const int64_t gr = m0 + row < M ? m0 + row : 0;
+            const uint16_t* src = A + gr * lda + k0 + 8 * swz(row, lpc);
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(as + j * 512), 16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < BW / NW; ++u) {
+            const int j = wave + u * NW;
+            const int row = 16 * j + lrow;
+            const int64_t gr = n0 + row < N ? n0 + row : 0;
+            const uint16_t* src = B + gr * ldb + k0 + 8 * swz(row, lpc);
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(bs + j * 512), 16, 0, 0);
+        }
+    };
+
+    f32x4 acc[G::TM][G::TN];
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto multiply = [&](const uint16_t* as, const uint16_t* bs) {
+        u32x4 fb[G::TN];
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) {
+            const int row = wn * G::WN + j * 16 + l16;
+            fb[j] = *reinterpret_cast<const u32x4*>(bs + row * kSK + 8 * swz(row, lq));
+        }
+#pragma unroll
+        for (int i = 0; i < G::TM; ++i) {
+            const int row = wm * G::WM + i * 16 + l16;
+            const u32x4 fa = *reinterpret_cast<const u32x4*>(as + row * kSK + 8 * swz(row, lq));
+#pragma unroll
+            for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma(fa, fb[j], acc[i][j]);
+        }
+    };
+
+    const int64_t nk = K / kSK;
+    constexpr int per = (AW + BW) / NW;      // loads per wave per slice
+    // slice k from stage (as, bs); slice k + 3 into stage (an, bn), the one
+    // slice k - 1 used
+    auto step = [&](int64_t k, const uint16_t* as, const uint16_t* bs, uint16_t* an, uint16_t* bn) {
+        // this wave's loads of slice k have landed once at most the loads of
+        // the (up to two) later slices are outstanding
+        if (k + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per));
+        else if (k + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | per);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        // every wave's slice k is in and slice k-1's stage is free.  A plain
+        // s_barrier: the waits above already cover the loads that matter,
+        // and __syncthreads' release fence would also wait for the slices
+        // still in flight
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (k + 3 < nk) issue(an, bn, (k + 3) * kSK);
+        multiply(as, bs);
+    };
+    if (nk > 0) issue(As0, Bs0, 0);
+    if (nk > 1) issue(As1, Bs1, kSK);
+    if (nk > 2) issue(As2, Bs2, 2 * kSK);
+    int64_t k = 0;
+    for (; k + 3 < nk; k += 4) {
+        step(k, As0, Bs0, As3, Bs3);
+        step(k + 1, As1, Bs1, As0, Bs0);
+        step(k + 2, As2, Bs2, As1, Bs1);
+        step(k + 3, As3, Bs3, As2, Bs2);
+    }
+    if (k < nk) step(k, As0, Bs0, As3, Bs3);
+    if (k + 1 < nk) step(k + 1, As1, Bs1, As0, Bs0);
+    if (k + 2 < nk) step(k + 2, As2, Bs2, As1, Bs1);
+
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) {
+            const int64_t col = n0 + wn * G::WN + j * 16 + l16;
+            if (col >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * G::WM + i * 16 + lq * 4 + e;
+                if (row >= M) continue;
+                if constexpr (OUT_BF16)
+                    static_cast<uint16_t*>(Cv)[row * ldc + col] = f32_to_bf16_bits(acc[i][j][e]);
+                else
+                    static_cast<float*>(Cv)[row * ldc + col] = acc[i][j][e];
+            }
+        }
+    }
+}
+
 template <int BM, int BN>
 hipError_t launch_gemm_t(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, void* C,
                          int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (out_bf16)
-        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, true>), dim3(static_cast<unsigned>(tiles)),
-                           dim3(kGemmThreads), 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    const dim3 grid(static_cast<unsigned>(tiles)), block(kGemmThreads);
+    const bool dma = K % kSK == 0 && lda % 8 == 0 && ldb % 8 == 0;
+    if (dma && out_bf16)
+        hipLaunchKernelGGL((gemm_bf16_nt_dma_kernel<BM, BN, true>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    else if (dma)
+        hipLaunchKernelGGL((gemm_bf16_nt_dma_kernel<BM, BN, false>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    else if (out_bf16)
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, true>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
     else
-        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, false>), dim3(static_cast<unsigned>(tiles)),
-                           dim3(kGemmThreads), 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, false>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
     return hipGetLastError();
 }
 
