@@ -33,7 +33,8 @@ EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
            "gdn_step", "gdn_snapshot_bytes", "gdn_snapshot_save", "gdn_snapshot_inspect",
            "gdn_snapshot_restore", "gdn_gemm_bf16", "gdn_layer_prefill_workspace_bytes",
-           "gdn_layer_prefill", "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
+           "gdn_layer_prefill", "gdn_layer_decode_workspace_bytes", "gdn_layer_decode",
+           "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
 PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
@@ -64,6 +65,14 @@ class CLayerIO(ctypes.Structure):
                 ("cu_seqlens", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("y_dtype", ctypes.c_int32), ("initial_state", ctypes.c_void_p),
                 ("final_state", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
+                ("conv_state_out", ctypes.c_void_p), ("state_slots", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int32)]
+
+
+class CLayerDecodeIO(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("y_dtype", ctypes.c_int32), ("state_in", ctypes.c_void_p),
+                ("state_out", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
                 ("conv_state_out", ctypes.c_void_p), ("state_slots", ctypes.c_void_p),
                 ("num_slots", ctypes.c_int32)]
 
@@ -161,6 +170,13 @@ def lib():
         L.gdn_layer_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CProj),
                                         ctypes.POINTER(CLayerIO), ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
+        L.gdn_layer_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_layer_decode_workspace_bytes.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CProj),
+                                                       ctypes.c_int32]
+        L.gdn_layer_decode.restype = ctypes.c_int
+        L.gdn_layer_decode.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CProj),
+                                       ctypes.POINTER(CLayerDecodeIO), ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
         L.gdn_snapshot_bytes.restype = ctypes.c_size_t
         L.gdn_snapshot_bytes.argtypes = [ctypes.POINTER(CLayer)]
         L.gdn_snapshot_save.restype = ctypes.c_int
@@ -482,6 +498,30 @@ def layer_prefill_raw(layer: Layer, proj: Proj, *, N, T_total, cu_seqlens, x, y,
         workspace.numel() * workspace.element_size() if workspace is not None else 0)
     _check(lib().gdn_layer_prefill(ctypes.byref(cl), ctypes.byref(cp), ctypes.byref(io),
                                    _ptr(workspace), nb, _stream(stream)))
+
+
+def layer_decode_workspace_bytes(layer: Layer, proj: Proj, B: int) -> int:
+    cl, cp = layer.c(), proj.c()
+    n = lib().gdn_layer_decode_workspace_bytes(ctypes.byref(cl), ctypes.byref(cp), int(B))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return int(n)
+
+
+def layer_decode_raw(layer: Layer, proj: Proj, *, B, x, y, state_in, state_out, conv_state_in,
+                     conv_state_out, workspace, workspace_bytes=None, state_slots=None, num_slots=0,
+                     stream=None):
+    """Call ``gdn_layer_decode``: x [B, hidden] bf16 -> y [B, hidden], one
+    token per sequence through in_proj, the decode step and out_proj."""
+    import torch
+    cl, cp = layer.c(), proj.c()
+    yd = GDN_DTYPE_BF16 if y is not None and y.dtype == torch.bfloat16 else GDN_DTYPE_FP32
+    io = CLayerDecodeIO(int(B), _ptr(x), _ptr(y), yd, _ptr(state_in), _ptr(state_out),
+                        _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_slots), int(num_slots))
+    nb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    _check(lib().gdn_layer_decode(ctypes.byref(cl), ctypes.byref(cp), ctypes.byref(io),
+                                  _ptr(workspace), nb, _stream(stream)))
 
 
 def snapshot_bytes(layer: Layer) -> int:

@@ -402,23 +402,34 @@ struct LayerWs {
     int64_t P = 0, off_proj = 0, off_gated = 0, off_pf = 0, total = 0;
 };
 
-gdn_status layer_ws(const gdn_layer* L, const gdn_proj* pr, int32_t N, int64_t T, LayerWs* w) {
-    gdn_status st = check_layer(L, true);
+// the projection [rows][P] and the gated output [rows][Hv*dv], bf16
+gdn_status proj_ws(const gdn_layer* L, const gdn_proj* pr, int64_t rows, bool prefill, LayerWs* w) {
+    gdn_status st = check_layer(L, prefill);
     if (st != GDN_OK) return st;
     if (!pr) return fail(GDN_ERR_INVALID_ARGUMENT, "proj is NULL");
-    if (pr->hidden <= 0 || pr->hidden % 8) return fail(GDN_ERR_INVALID_ARGUMENT, "hidden (%d) must be a positive multiple of 8", pr->hidden);
+    if (pr->hidden <= 0 || pr->hidden % 8)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "hidden (%d) must be a positive multiple of 8", pr->hidden);
     if (L->act_dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_INVALID_ARGUMENT, "the layer path needs act_dtype bf16");
-    if (N < 0 || T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "N and T_total must be >= 0");
+    if (rows < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "row count must be >= 0");
     w->P = 2ll * L->Hk * L->dk + 2ll * L->Hv * L->dv + 2ll * L->Hv;
     if ((2ll * L->Hk * L->dk) % 8 || (static_cast<int64_t>(L->Hv) * L->dv) % 8 || w->P % 8)
         return fail(GDN_ERR_INVALID_ARGUMENT, "projection widths must be multiples of 8");
     int64_t o = 0;
     w->off_proj = o;
-    o = round_up(o + 2 * T * w->P, 256);
+    o = round_up(o + 2 * rows * w->P, 256);
     w->off_gated = o;
-    o = round_up(o + 2 * T * static_cast<int64_t>(L->Hv) * L->dv, 256);
+    o = round_up(o + 2 * rows * static_cast<int64_t>(L->Hv) * L->dv, 256);
     w->off_pf = o;
-    w->total = o + ws_layout(L, N, T, true, 0).total;
+    w->total = o;
+    return GDN_OK;
+}
+
+
+gdn_status layer_ws(const gdn_layer* L, const gdn_proj* pr, int32_t N, int64_t T, LayerWs* w) {
+    if (N < 0 || T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "N and T_total must be >= 0");
+    gdn_status st = proj_ws(L, pr, T, true, w);
+    if (st != GDN_OK) return st;
+    w->total = w->off_pf + ws_layout(L, N, T, true, 0).total;
     return GDN_OK;
 }
 
@@ -487,6 +498,71 @@ gdn_status gdn_layer_prefill(const gdn_layer* L, const gdn_proj* pr, const gdn_l
     st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
     if (st != GDN_OK) return st;
     e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, T,
+                                 pr->hidden, HD, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+
+size_t gdn_layer_decode_workspace_bytes(const gdn_layer* L, const gdn_proj* pr, int32_t B) {
+    g_err[0] = 0;
+    LayerWs w;
+    if (proj_ws(L, pr, B, false, &w) != GDN_OK) return 0;
+    return static_cast<size_t>(w.total > 0 ? w.total : 256);
+}
+
+gdn_status gdn_layer_decode(const gdn_layer* L, const gdn_proj* pr, const gdn_layer_decode_io* io, void* ws,
+                            size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!io) return fail(GDN_ERR_INVALID_ARGUMENT, "io is NULL");
+    LayerWs w;
+    gdn_status st = proj_ws(L, pr, io->B, false, &w);
+    if (st != GDN_OK) return st;
+    const int64_t B = io->B;
+    if (B == 0) return GDN_OK;
+    const int64_t HD = static_cast<int64_t>(L->Hv) * L->dv;
+    if (!io->x || !io->y || !pr->w_in || !pr->w_out)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "x, y, w_in and w_out are required");
+    if (io->y_dtype != GDN_DTYPE_BF16 && io->y_dtype != GDN_DTYPE_FP32)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "y_dtype %d unknown", io->y_dtype);
+    if (!aligned(io->x, 16) || !aligned(pr->w_in, 16) || !aligned(pr->w_out, 16) || !aligned(io->y, 16))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "x, y, w_in and w_out must be 16-byte aligned");
+    if (!ws || !aligned(ws, 256)) return fail(GDN_ERR_WORKSPACE, "workspace missing or not 256-byte aligned");
+    if (static_cast<int64_t>(ws_bytes) < w.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, the layer needs %lld", ws_bytes,
+                    static_cast<long long>(w.total));
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint16_t* proj = reinterpret_cast<uint16_t*>(base + w.off_proj);
+    uint16_t* gated = reinterpret_cast<uint16_t*>(base + w.off_gated);
+    const int64_t qk = static_cast<int64_t>(L->Hk) * L->dk;
+    gdn_layer Lg = *L;
+    Lg.out_dtype = GDN_DTYPE_BF16;
+    gdn_decode_io dio{};
+    dio.B = io->B;
+    dio.q = proj;
+    dio.k = proj + qk;
+    dio.v = proj + 2 * qk;
+    dio.z = proj + 2 * qk + HD;
+    dio.a = proj + 2 * qk + 2 * HD;
+    dio.b = proj + 2 * qk + 2 * HD + L->Hv;
+    dio.q_stride = dio.k_stride = dio.v_stride = dio.z_stride = dio.a_stride = dio.b_stride = w.P;
+    dio.state_in = io->state_in;
+    dio.state_out = io->state_out;
+    dio.conv_state_in = io->conv_state_in;
+    dio.conv_state_out = io->conv_state_out;
+    dio.out = gated;
+    dio.core_out = nullptr;
+    dio.state_slots = io->state_slots;
+    dio.num_slots = io->num_slots;
+    st = decode_impl(&Lg, &dio, 0, nullptr, stream, false);
+    if (st != GDN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, B, w.P,
+                                            pr->hidden, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
+    st = decode_impl(&Lg, &dio, 0, nullptr, stream);
+    if (st != GDN_OK) return st;
+    e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, B,
                                  pr->hidden, HD, s);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
     return GDN_OK;

@@ -112,6 +112,21 @@ def proj_weights(shape: LayerShape, hidden: int, seed: int):
     return w_in, w_out
 
 
+def proj_weights_exact(shape: LayerShape, hidden: int, seed: int):
+    """w_in with one nonzero per row, +-1 or +-1/2 at a random column, so a
+    projection of bf16 inputs is exact in bf16 whatever the summation order
+    (both sides of a parity test then see the same projection bits); w_out as
+    in proj_weights."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 8])))
+    P = proj_rows(shape)
+    w_in = np.zeros((P, hidden), dtype=np.float32)
+    cols = rng.integers(0, hidden, P)
+    vals = rng.choice(np.array([-1.0, -0.5, 0.5, 1.0], dtype=np.float32), P)
+    w_in[np.arange(P), cols] = vals
+    _, w_out = proj_weights(shape, hidden, seed)
+    return w_in, w_out
+
+
 def hidden_inputs(T: int, hidden: int, seed: int):
     """x [T, hidden] ~ N(0, 1), rounded to bf16 (as fp32 values)."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))

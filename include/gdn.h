@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
     GDN_OK = 0,
@@ -272,6 +272,32 @@ size_t gdn_layer_prefill_workspace_bytes(const gdn_layer* layer,
 gdn_status gdn_layer_prefill(const gdn_layer* layer, const gdn_proj* proj,
                              const gdn_layer_io* io, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* One token per sequence through the whole layer: x [B][hidden] bf16 in, y
+ * [B][hidden] in y_dtype out, states as in gdn_decode_io (state pools
+ * included).  The workspace holds the projection [B][P] and the gated
+ * output [B][Hv*dv] (bf16). */
+typedef struct {
+    int32_t B;
+    const void* x;
+    void* y;
+    int32_t y_dtype;
+    const float* state_in;
+    float* state_out;
+    const void* conv_state_in;
+    void* conv_state_out;
+    const int32_t* state_slots;
+    int32_t num_slots;
+} gdn_layer_decode_io;
+
+size_t gdn_layer_decode_workspace_bytes(const gdn_layer* layer,
+                                        const gdn_proj* proj, int32_t B);
+
+/* in_proj GEMM -> gdn_decode on views into the projection -> out_proj GEMM,
+ * on `stream`; validation as for gdn_decode plus the projection's shapes. */
+gdn_status gdn_layer_decode(const gdn_layer* layer, const gdn_proj* proj,
+                            const gdn_layer_decode_io* io, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ---- session snapshots ------------------------------------------------
  * Park one sequence's layer state (recurrent + conv) in host memory and

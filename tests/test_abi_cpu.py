@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 6
+    assert L.gdn_abi_version() == 7
 
 
 def test_status_strings():
@@ -291,7 +291,10 @@ def test_binding_structs_match_the_header(tmp_path):
               "gdn_proj": (gdn.CProj, ["hidden", "w_in", "w_out"]),
               "gdn_layer_io": (gdn.CLayerIO, ["N", "T_total", "cu_seqlens", "x", "y", "y_dtype",
                                               "initial_state", "conv_state_out", "state_slots",
-                                              "num_slots"])}
+                                              "num_slots"]),
+              "gdn_layer_decode_io": (gdn.CLayerDecodeIO, ["B", "x", "y", "y_dtype", "state_in",
+                                                           "conv_state_out", "state_slots",
+                                                           "num_slots"])}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gdn.h"', "int main(void) {"]
     for name, (_, fields) in checks.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
@@ -417,3 +420,15 @@ def test_layer_workspace_and_rejects():
     assert "bf16" in ei.value.detail
     with pytest.raises(gdn.GdnError):
         gdn.layer_prefill_workspace_bytes(lay, gdn.Proj(hidden=2047, w_in=None, w_out=None), 1, T)
+
+
+def test_layer_decode_workspace():
+    """The decode layer's workspace: the bf16 projection [B][P] and gated
+    output [B][Hv dv], each 256-byte rounded."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
+                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE), w_out=_FakeTensor(FAKE))
+    P = 2 * 16 * 128 + 2 * 32 * 128 + 2 * 32
+    rnd = lambda n: -(-n // 256) * 256
+    for B in (1, 3, 64):
+        assert gdn.layer_decode_workspace_bytes(lay, proj, B) == rnd(2 * B * P) + rnd(2 * B * 32 * 128)
