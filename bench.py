@@ -525,6 +525,46 @@ def main():
         del xs, y, lws, lfs, lcs, pbuf, gbuf, w_in, w_out
         torch.cuda.empty_cache()
 
+        # decode with projections: 8 layers' weights (~540 MB, more than the
+        # Infinity Cache holds) rotated, one token per sequence
+        NL = 8
+        projs = [gdn.Proj(hidden=H,
+                          w_in=(torch.randn((P, H), generator=gen, device=dev) / math.sqrt(H)).to(torch.bfloat16),
+                          w_out=(torch.randn((H, HD), generator=gen, device=dev) / math.sqrt(HD)).to(torch.bfloat16))
+                 for _ in range(NL)]
+        dec = {}
+        for Bd in (1, 64):
+            xd = torch.randn((Bd, H), generator=gen, device=dev).to(torch.bfloat16)
+            yd = torch.empty((Bd, H), dtype=torch.bfloat16, device=dev)
+            sd = [torch.randn((Bd, sh.Hv, sh.dk, sh.dv), generator=gen, device=dev) * 0.1 for _ in range(NL)]
+            cd = [torch.zeros((Bd, 3, sh.Cc), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+            dws = torch.empty(gdn.layer_decode_workspace_bytes(lay, projs[0], Bd), dtype=torch.uint8, device=dev)
+
+            def dstep(l):
+                gdn.layer_decode_raw(lay, projs[l], B=Bd, x=xd, y=yd, state_in=sd[l], state_out=sd[l],
+                                     conv_state_in=cd[l], conv_state_out=cd[l], workspace=dws)
+
+            for l in range(NL):
+                dstep(l)
+            d0, d1 = new_events(2)
+            d0.record(stream)
+            R = 3
+            for _ in range(R):
+                for l in range(NL):
+                    dstep(l)
+            d1.record(stream)
+            torch.cuda.synchronize()
+            ms_l = d0.elapsed_time(d1) / (R * NL)
+            wbytes = 2 * (P * H + H * HD)
+            sbytes = Bd * 2 * sh.Hv * sh.dk * sh.dv * 4
+            dec[f"B{Bd}"] = {"ms_per_layer": ms_l, "weight_and_state_GBps": (wbytes + sbytes) / (ms_l * 1e-3) / 1e9}
+            log(f"layer decode with projections B={Bd}: {ms_l * 1e3:.1f} us per layer, weights + state "
+                f"{(wbytes + sbytes) / (ms_l * 1e-3) / 1e9:.0f} GB/s")
+            del xd, yd, sd, cd, dws
+        result["layer_with_projections"]["decode"] = dec
+        del projs
+        torch.cuda.empty_cache()
+
     # ---------------- CPU baseline: the fp64 oracle on the host ----------------
     if not args.no_cpu_baseline:
         import oracle
