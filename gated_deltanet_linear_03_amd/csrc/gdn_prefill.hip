@@ -17,14 +17,14 @@
 // Kernels, in stream order:
 //   plan_kernel   first chunk index of every sequence (chunks restart at each
 //                 sequence start, so results do not depend on the packing)
-//   prep_kernel   chunk-parallel over (chunk, value head): conv1d+SiLU, L2
-//                 norms, gates, Gram matrices, the diagonal blocks of
-//                 (I + A)^{-1} and a block forward substitution for W and U~;
-//                 writes the per-chunk operands -W, Q_G = diag(e^gamma) Q,
-//                 K_d^T, P, U~ in matrix-core fragment order (split bf16
-//                 hi/lo); see gdn_prep.hpp
+//   prep_kernel   chunk-parallel over (chunk, one or two value heads of a
+//                 key head): conv1d+SiLU, L2 norms, gates, Gram matrices, the
+//                 diagonal blocks of (I + A)^{-1} and a block forward
+//                 substitution for W and U~; writes the per-chunk operands
+//                 -W, Q_G = diag(e^gamma) Q, K_d^T, P (fp16) and U~ (fp32) in
+//                 matrix-core fragment order; see gdn_prep.hpp
 //   scan_kernel   sequential over the chunks of one (sequence, value head,
-//                 dv slice of 16 or 32 columns): U, O and H' on split-bf16
+//                 dv slice of 16 or 32 columns): U, O and H' on fp16
 //                 matrix-core products, H kept in fp32 accumulators for the
 //                 whole sequence; also writes the final state and the conv
 //                 state tail
@@ -581,9 +581,15 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
         q.win_idx = w;
         q.win_lo = w * W;
         q.win_hi = min(p.max_chunks, (w + 1) * W);
-        if (q.win_hi > q.win_lo)
-            hipLaunchKernelGGL((prep_kernel<DK, DV, C, BF16>), dim3(q.win_hi - q.win_lo, p.Hv),
-                               dim3(kPrepThreads), 0, s, q);
+        if (q.win_hi > q.win_lo) {
+            // value heads in pairs when each key head has an even number of them
+            if (p.G % 2 == 0)
+                hipLaunchKernelGGL((prep_kernel<DK, DV, C, 2, BF16>), dim3(q.win_hi - q.win_lo, p.Hv / 2),
+                                   dim3(kPrepThreads), 0, s, q);
+            else
+                hipLaunchKernelGGL((prep_kernel<DK, DV, C, 1, BF16>), dim3(q.win_hi - q.win_lo, p.Hv),
+                                   dim3(kPrepThreads), 0, s, q);
+        }
         mark(ev_i++);
         if (pairs > 0) {
             const int groups = (pairs + 7) / 8;

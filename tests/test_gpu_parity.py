@@ -99,6 +99,45 @@ def test_prefill_dk_ne_dv():
     check_prefill(case, gpu_prefill(case), oracle_prefill(case), label="dk!=dv")
 
 
+@pytest.mark.parametrize("Hk,Hv", [(4, 4), (2, 6), (1, 4)])
+def test_prefill_value_heads_per_key_head(Hk, Hv):
+    """Hv / Hk = 1 and 3 run the prep kernel on one value head per
+    work-group, 4 on two pairs of value heads per key head."""
+    sh = synth.LayerShape(Hk=Hk, Hv=Hv, dk=32, dv=32, chunk=16, act_dtype="bf16")
+    case = synth.prefill_case(sh, [37, 0, 27, 1, 16], seed=11, with_state=True,
+                              with_conv_state=True)
+    check_prefill(case, gpu_prefill(case), oracle_prefill(case), label=f"Hk{Hk}-Hv{Hv}")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (32, 64)])
+def test_prefill_head_pairs_bitwise_vs_single_heads(dk, dv):
+    """2 key / 4 value heads run the prep kernel on value-head pairs; the same
+    layer written with 4 key heads (each key head's q, k, conv weights and
+    conv-state channels duplicated) runs one value head per work-group.  Every
+    value head's results must be the same bits."""
+    sh2 = synth.LayerShape(Hk=2, Hv=4, dk=dk, dv=dv, chunk=16, act_dtype="bf16")
+    case2 = synth.prefill_case(sh2, [37, 0, 27, 1, 16], seed=12, with_state=True,
+                               with_conv_state=True)
+    sh1 = synth.LayerShape(Hk=4, Hv=4, dk=dk, dv=dv, chunk=16, act_dtype="bf16")
+    dup = [0, 0, 1, 1]                       # key head of each value head
+    qk2 = sh2.Hk * dk
+    ch = ([k * dk + i for k in dup for i in range(dk)] +
+          [qk2 + k * dk + i for k in dup for i in range(dk)] +
+          list(range(2 * qk2, sh2.Cc)))       # channels of sh1 in terms of sh2's
+    x1 = dict(case2.inputs)
+    x1["q"] = np.ascontiguousarray(case2.inputs["q"][:, dup])
+    x1["k"] = np.ascontiguousarray(case2.inputs["k"][:, dup])
+    p1 = dict(case2.params)
+    p1["conv_w"] = np.ascontiguousarray(case2.params["conv_w"][ch])
+    case1 = synth.PrefillCase(sh1, case2.cu_seqlens, x1, p1, case2.initial_state,
+                              np.ascontiguousarray(case2.conv_state[:, :, ch]))
+    r2, r1 = gpu_prefill(case2), gpu_prefill(case1)
+    for key in ("out", "core_out", "final_state"):
+        assert torch.equal(r1[key], r2[key]), key
+    assert torch.equal(r1["conv_state_out"], r2["conv_state_out"][:, :, ch])
+    check_prefill(case2, r2, oracle_prefill(case2), label=f"pairs-{dk}x{dv}")
+
+
 def test_prefill_full_shape_ragged():
     """16/32 heads, 128/128, chunk 64, bf16: several chunks and ragged tails."""
     case = synth.prefill_case(synth.FULL, [200, 64, 1, 130, 0], seed=7,
