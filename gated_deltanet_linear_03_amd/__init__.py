@@ -37,7 +37,7 @@ EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
-PREFILL_KERNELS = ("plan", "prep", "scan", "epi")
+PREFILL_KERNELS = ("prep", "scan", "epi")
 
 
 class GdnError(RuntimeError):
@@ -256,15 +256,15 @@ def prefill_workspace_bytes(layer: Layer, N: int, T_total: int) -> int:
 
 def prefill_launches(layer: Layer, N: int, T_total: int, workspace_bytes: int | None = None):
     """Names of the kernels gdn_prefill enqueues, in order, for these sizes
-    and workspace size (default: gdn_prefill_workspace_bytes): plan, then
-    prep and scan per window of chunks, then epi."""
+    and workspace size (default: gdn_prefill_workspace_bytes): prep and
+    scan per window of chunks, then epi."""
     if workspace_bytes is None:
         workspace_bytes = prefill_workspace_bytes(layer, N, T_total)
     cl = layer.c()
     n = lib().gdn_prefill_launches(ctypes.byref(cl), int(N), int(T_total), int(workspace_bytes))
     if n < 0:
         raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
-    return ["plan"] + ["prep", "scan"] * ((n - 2) // 2) + ["epi"]
+    return ["prep", "scan"] * ((n - 1) // 2) + ["epi"]
 
 
 def _prefill_io(N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,

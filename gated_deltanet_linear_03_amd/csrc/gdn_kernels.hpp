@@ -53,7 +53,7 @@ struct PrefillParams {
     float* core;                          // o before the gated norm (user or workspace)
     const int32_t* slots;                 // [N] pool entry of each sequence's states, or NULL (entry n)
     // workspace views
-    int32_t* chunk_off;                   // [N+1] first chunk of each sequence
+    int32_t* chunk_off;                   // [N+1] first chunk of each sequence (written by the first prep)
     float* decay;                         // [max_chunks][Hv] exp(gamma_last)
     float* sink;                          // [64] target of stores to rows past a sequence end
     float* carry;                         // [2][Hv][dk][dv] state across a window boundary
@@ -94,10 +94,10 @@ inline int64_t prefill_window_slots(int DK, int DV, int C, int Hv, int N, int64_
     return (cap + nwin - 1) / nwin;
 }
 
-// Kernel launches of one prefill: plan, (prep, scan) per window, epi.
+// Kernel launches of one prefill: (prep, scan) per window, epi.
 inline int64_t prefill_launches(int64_t max_chunks, int64_t win_slots) {
     const int64_t nwin = max_chunks > win_slots ? (max_chunks + win_slots - 1) / win_slots : 1;
-    return 2 + 2 * nwin;
+    return 1 + 2 * nwin;
 }
 
 hipError_t launch_decode(int DK, int DV, bool bf16, const DecodeParams& p, hipStream_t s,

@@ -15,10 +15,9 @@
 // underflow inside a chunk go to zero as they should.
 //
 // Kernels, in stream order:
-//   plan_kernel   first chunk index of every sequence (chunks restart at each
-//                 sequence start, so results do not depend on the packing)
 //   prep_kernel   chunk-parallel over (chunk, one or two value heads of a
-//                 key head): conv1d+SiLU, L2 norms, gates, Gram matrices, the
+//                 key head); its first window also builds the chunk table
+//                 (first chunk of every sequence): conv1d+SiLU, L2 norms, gates, Gram matrices, the
 //                 diagonal blocks of (I + A)^{-1} and a block forward
 //                 substitution for W and U~; writes the per-chunk operands
 //                 -W, Q_G = diag(e^gamma) Q, K_d^T, P (fp16) and U~ (fp32) in
@@ -35,33 +34,58 @@
 namespace gdn {
 
 // ---------------------------------------------------------------------------
-// plan: chunk_off[n] = sum_{m<n} ceil(L_m / C), chunk_off[N] = total chunks.
+// Chunk table: chunk_off[n] = sum_{m<n} ceil(L_m / C), chunk_off[N] = total
+// chunks (chunks restart at each sequence start, so results do not depend on
+// the packing).  Each work-group of the first prep window derives the total
+// and its own slot's sequence from cu_seqlens with a block-wide scan; the one
+// given `out` also stores the table for the kernels after it.  `scratch`:
+// NT / 64 + 2 ints of LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int N, int C,
-                                                   int32_t* chunk_off) {
-    __shared__ int32_t part[256];
-    const int tid = threadIdx.x;
-    const int per = (N + 255) / 256;
+struct ChunkPos {
+    int total;   // chunks of the batch
+    int n;       // sequence owning the slot (when slot < total)
+    int first;   // its first chunk
+};
+
+template <int NT>
+__device__ ChunkPos chunk_table(const int32_t* cu, int N, int C, int slot, int32_t* scratch,
+                                int32_t* out) {
+    constexpr int NW = NT / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int per = (N + NT - 1) / NT;
     const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
-    int32_t s = 0;
-    for (int n = n0; n < n1; ++n) s += (cu[n + 1] - cu[n] + C - 1) / C;
-    part[tid] = s;
+    int s = 0;
+    for (int m = n0; m < n1; ++m) s += (cu[m + 1] - cu[m] + C - 1) / C;
+    int incl = s;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += u;
+    }
+    if (lane == kWave - 1) scratch[wave] = incl;
     __syncthreads();
-    if (tid == 0) {
-        int32_t acc = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int32_t v = part[i];
-            part[i] = acc;
-            acc += v;
+    int acc = incl - s, total = 0;
+    for (int w = 0; w < NW; ++w) {
+        const int v = scratch[w];
+        acc += w < wave ? v : 0;
+        total += v;
+    }
+    for (int m = n0; m < n1; ++m) {
+        const int c = (cu[m + 1] - cu[m] + C - 1) / C;
+        if (out) out[m] = acc;
+        if (acc <= slot && slot < acc + c) {
+            scratch[NW] = m;
+            scratch[NW + 1] = acc;
         }
-        chunk_off[N] = acc;
+        acc += c;
     }
+    if (out && tid == 0) out[N] = total;
     __syncthreads();
-    int32_t acc = part[tid];
-    for (int n = n0; n < n1; ++n) {
-        chunk_off[n] = acc;
-        acc += (cu[n + 1] - cu[n] + C - 1) / C;
-    }
+    ChunkPos r;
+    r.total = total;
+    r.n = scratch[NW];
+    r.first = scratch[NW + 1];
+    return r;
 }
 
 // Sequence owning chunk slot c: the last n with chunk_off[n] <= c.
@@ -568,26 +592,26 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
     };
     int ev_i = 0;
     mark(ev_i++);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.N, C, p.chunk_off);
-    mark(ev_i++);
     // windows of chunk slots: prep writes a window's operand blocks, scan
     // consumes them while they are still cache-resident, then the next
     // window reuses the blocks
     const int W = p.win_slots;
-    const int nwin = static_cast<int>(prefill_launches(p.max_chunks, W) - 2) / 2;
+    const int nwin = static_cast<int>(prefill_launches(p.max_chunks, W) - 1) / 2;
     const int pairs = p.N * p.Hv;
     for (int w = 0; w < nwin; ++w) {
         PrefillParams q = p;
         q.win_idx = w;
         q.win_lo = w * W;
         q.win_hi = min(p.max_chunks, (w + 1) * W);
-        if (q.win_hi > q.win_lo) {
+        // the first window runs even without chunks: it writes the chunk table
+        const int gx = max(q.win_hi - q.win_lo, w == 0 ? 1 : 0);
+        if (gx > 0) {
             // value heads in pairs when each key head has an even number of them
             if (p.G % 2 == 0)
-                hipLaunchKernelGGL((prep_kernel<DK, DV, C, 2, BF16>), dim3(q.win_hi - q.win_lo, p.Hv / 2),
+                hipLaunchKernelGGL((prep_kernel<DK, DV, C, 2, BF16>), dim3(gx, p.Hv / 2),
                                    dim3(kPrepThreads), 0, s, q);
             else
-                hipLaunchKernelGGL((prep_kernel<DK, DV, C, 1, BF16>), dim3(q.win_hi - q.win_lo, p.Hv),
+                hipLaunchKernelGGL((prep_kernel<DK, DV, C, 1, BF16>), dim3(gx, p.Hv),
                                    dim3(kPrepThreads), 0, s, q);
         }
         mark(ev_i++);

@@ -210,11 +210,26 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
-    const int total = min(p.chunk_off[p.N], p.win_hi);
+    // the chunk table: built here in the first window (work-group (0, 0)
+    // stores it), read from the workspace after that
+    int total, n = 0, first = 0;
+    if (p.win_idx == 0) {
+        const ChunkPos cp = chunk_table<kPrepThreads>(p.cu, p.N, C, slot, reinterpret_cast<int32_t*>(smem + S::oS),
+                                                      blockIdx.x == 0 && blockIdx.y == 0 ? p.chunk_off : nullptr);
+        total = cp.total;
+        n = cp.n;
+        first = cp.first;
+    } else {
+        total = p.chunk_off[p.N];
+    }
+    total = min(total, p.win_hi);
     if (slot >= total) return;
-    const int n = seq_of_chunk(p.chunk_off, p.N, slot);
+    if (p.win_idx != 0) {
+        n = seq_of_chunk(p.chunk_off, p.N, slot);
+        first = p.chunk_off[n];
+    }
     const int64_t start = p.cu[n], end = p.cu[n + 1];
-    const int64_t t0 = start + static_cast<int64_t>(slot - p.chunk_off[n]) * C;
+    const int64_t t0 = start + static_cast<int64_t>(slot - first) * C;
     const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
     const int qk = p.Hk * DK;
     const int Cc = 2 * qk + p.Hv * DV;

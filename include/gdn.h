@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum {
     GDN_OK = 0,
@@ -165,9 +165,9 @@ gdn_status gdn_prefill(const gdn_layer* layer, const gdn_prefill_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of kernels gdn_prefill enqueues for these sizes and this
- * workspace size, in order: plan (chunk table), then per window prep
- * (chunk-parallel operands) and scan (sequential state passing), then epi
- * (gated RMSNorm): 2 + 2 * windows.  -1 on an invalid layer, sizes or a
+ * workspace size, in order: per window prep (chunk-parallel operands; the
+ * first one also builds the chunk table) and scan (sequential state
+ * passing), then epi (gated RMSNorm): 1 + 2 * windows.  -1 on an invalid layer, sizes or a
  * too small workspace (detail in gdn_last_error()). */
 int64_t gdn_prefill_launches(const gdn_layer* layer, int32_t N,
                              int64_t T_total, size_t workspace_bytes);

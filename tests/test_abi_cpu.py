@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 7
+    assert L.gdn_abi_version() == 8
 
 
 def test_status_strings():
@@ -230,21 +230,21 @@ def test_prefill_windows_follow_the_workspace():
     T = 4096
     nb = gdn.prefill_workspace_bytes(lay, 1, T)
     names = gdn.prefill_launches(lay, 1, T, nb)
-    assert names[0] == "plan" and names[-1] == "epi"
-    assert names[1:-1] == ["prep", "scan"] * ((len(names) - 2) // 2)
+    assert names[-1] == "epi"
+    assert names[:-1] == ["prep", "scan"] * ((len(names) - 1) // 2)
     n_chunks = (T + 63) // 64                     # the bound the library plans for
     win = window(n_chunks)                        # chunk slots per window
-    assert win == 32 and len(names) == 2 + 2 * 2
+    assert win == 32 and len(names) == 1 + 2 * 2
     # beyond the pre-norm output and the decay table, only the window grows
     nb_long = gdn.prefill_workspace_bytes(lay, 1, 131072)
     assert nb_long - nb == ((131072 - T) * 32 * 128 * 4 + 4 * (131072 - T) // 64 * 32
                             + (window(131072 // 64) - win) * slot)
     # half the window: twice the windows
     half = len(gdn.prefill_launches(lay, 1, T, nb - (win - win // 2) * slot))
-    assert half == 2 + 2 * -(-n_chunks // (win // 2))
+    assert half == 1 + 2 * -(-n_chunks // (win // 2))
     # the smallest workspace holds one slot: a window per chunk slot
     floor = nb - (win - 1) * slot
-    assert len(gdn.prefill_launches(lay, 1, T, floor)) == 2 + 2 * n_chunks
+    assert len(gdn.prefill_launches(lay, 1, T, floor)) == 1 + 2 * n_chunks
     with pytest.raises(gdn.GdnError):
         gdn.prefill_launches(lay, 1, T, floor - 256)
 
