@@ -291,6 +291,119 @@ hipError_t launch_gemm_t(const uint16_t* a, int64_t lda, const uint16_t* b, int6
     return hipGetLastError();
 }
 
+// ---- skinny products: M <= kSkinnyMax rows (decode batches) ----
+// With few rows of A the product is a stream over the weight matrix B, which
+// a tiled kernel reads at a fraction of the memory bandwidth.  Here a
+// work-group owns NTW matrix-core n tiles (16 NTW rows of B) and splits K
+// over its NWV waves.  Per 128-wide k step, lane (l16, q) reads 64 contiguous
+// bytes of B row n0 + l16 (of each n tile), k in [32 q, 32 q + 32), as four
+// 8-wide fragments, and the same k set of every A row (the products only
+// need both operands to use one k mapping), so each B row is read as
+// 256-byte runs.  Every pair of the MT 16-row tiles of A and the NTW B tiles
+// is multiplied; the waves' partial tiles are summed in LDS in wave order.
+// Each output depends on its A row, B row, K and NWV only, never on M or on
+// the other rows.
+constexpr int kSkinnyMax = 64;
+constexpr int kSkinnyStep = 128;
+
+template <int MT, int NTW, int NWV, bool OUT_BF16>
+__global__ __launch_bounds__(NWV * kWave) void gemm_skinny_kernel(
+        const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+        void* __restrict__ Cv, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    __shared__ f32x4 part[NWV][MT * NTW][kWave];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int l16 = lane % 16, lq = lane / 16;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16 * NTW;
+    const int64_t steps = (K + kSkinnyStep - 1) / kSkinnyStep;
+    const int64_t s0 = steps * wave / NWV, s1 = steps * (wave + 1) / NWV;
+    const uint16_t* brow[NTW];
+    bool nok[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+        const int64_t n = n0 + t * 16 + l16;
+        nok[t] = n < N;
+        brow[t] = B + (nok[t] ? n : 0) * ldb;
+    }
+    const uint16_t* arow[MT];
+    bool mok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = mt * 16 + l16;
+        mok[mt] = m < M;
+        arow[mt] = A + (mok[mt] ? m : 0) * lda;
+    }
+    f32x4 acc[MT][NTW];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll 2
+    for (int64_t st = s0; st < s1; ++st) {
+        const int64_t kb = st * kSkinnyStep + lq * 32;
+        u32x4 bf[NTW][4];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t k = kb + 8 * j;
+                bf[t][j] = (nok[t] && k < K) ? *reinterpret_cast<const u32x4*>(brow[t] + k) : zero;
+            }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            u32x4 af[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t k = kb + 8 * j;
+                af[j] = (mok[mt] && k < K) ? *reinterpret_cast<const u32x4*>(arow[mt] + k) : zero;
+            }
+#pragma unroll
+            for (int t = 0; t < NTW; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[mt][t] = mfma(af[j], bf[t][j], acc[mt][t]);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) part[wave][mt * NTW + t][lane] = acc[mt][t];
+    __syncthreads();
+    // wave i sums output tile i (m tile i / NTW, n tile i % NTW) over the
+    // waves in order and stores it
+    for (int i = wave; i < MT * NTW; i += NWV) {
+        const int mt = i / NTW, t = i % NTW;
+        f32x4 s = part[0][i][lane];
+        for (int w = 1; w < NWV; ++w) {
+            const f32x4 v = part[w][i][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] += v[e];
+        }
+        const int64_t n = n0 + t * 16 + l16;
+        if (n >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t m = mt * 16 + lq * 4 + e;
+            if (m >= M) continue;
+            if constexpr (OUT_BF16)
+                static_cast<uint16_t*>(Cv)[m * ldc + n] = f32_to_bf16_bits(s[e]);
+            else
+                static_cast<float*>(Cv)[m * ldc + n] = s[e];
+        }
+    }
+}
+
+template <int MT, int NTW, int NWV>
+hipError_t launch_skinny_t(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, void* C,
+                           int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>((N + 16 * NTW - 1) / (16 * NTW))), block(NWV * kWave);
+    if (out_bf16)
+        hipLaunchKernelGGL((gemm_skinny_kernel<MT, NTW, NWV, true>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<MT, NTW, NWV, false>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
@@ -304,6 +417,33 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (M <= kSkinnyMax) {
+        // few rows (A rows and lda are 16-byte aligned, K a multiple of 8)
+        // With n tiles to spare (at least two per compute unit) K is split
+        // over 4 waves and, past 16 rows, a work-group takes 4 n tiles so
+        // that each A fragment serves 4 B tiles; otherwise K is split over 16
+        // waves, one n tile each.  The split depends on N only, so a row's
+        // bits do not depend on M.
+        const bool many = (N + 15) / 16 >= 2ll * cus;
+        const int mt = static_cast<int>((M + 15) / 16);
+#define GDN_SKINNY(MT_, NTW_, NWV_) \
+    return launch_skinny_t<MT_, NTW_, NWV_>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s)
+        if (many) {
+            switch (mt) {
+                case 1: GDN_SKINNY(1, 1, 4);
+                case 2: GDN_SKINNY(2, 4, 4);
+                case 3: GDN_SKINNY(3, 4, 4);
+                default: GDN_SKINNY(4, 4, 4);
+            }
+        }
+        switch (mt) {
+            case 1: GDN_SKINNY(1, 1, 16);
+            case 2: GDN_SKINNY(2, 1, 16);
+            case 3: GDN_SKINNY(3, 1, 16);
+            default: GDN_SKINNY(4, 1, 16);
+        }
+#undef GDN_SKINNY
+    }
     const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
     if (wide >= cus) return launch_gemm_t<256, 256>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);
     return launch_gemm_t<256, 128>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);

@@ -24,7 +24,8 @@ def _bf16(a):
 
 
 @pytest.mark.parametrize("M, N, K", [(300, 200, 136), (1, 392, 64), (257, 12352, 2048),
-                                     (64, 2048, 4096)])
+                                     (64, 2048, 4096), (17, 12352, 2048), (40, 100, 200),
+                                     (3, 2056, 4104)])
 def test_gemm_matches_fp64(M, N, K):
     r = np.random.default_rng(M + N + K)
     A = synth.bf16_round(r.standard_normal((M, K)).astype(np.float32))
@@ -43,10 +44,12 @@ def test_gemm_matches_fp64(M, N, K):
     assert torch.equal(C16.float(), C32.to(torch.bfloat16).float())
 
 
-def test_gemm_strided_rows():
-    """Row strides beyond K (views into wider buffers)."""
+@pytest.mark.parametrize("M", [130, 7])
+def test_gemm_strided_rows(M):
+    """Row strides beyond K (views into wider buffers); 7 rows take the
+    few-row kernel."""
     r = np.random.default_rng(3)
-    M, N, K = 130, 70, 96
+    N, K = 70, 96
     Aw = _bf16(r.standard_normal((M, K + 24)))
     Bw = _bf16(r.standard_normal((N, K + 8)))
     A, B = Aw[:, 8:8 + K], Bw[:, :K]
@@ -56,6 +59,23 @@ def test_gemm_strided_rows():
     ref = A.float().cpu().double() @ B.float().cpu().double().T
     assert torch.allclose(Cw[:, :N].cpu().double(), ref, rtol=1e-5, atol=1e-5)
     assert not Cw[:, N:].any()
+
+
+def test_gemm_few_rows_batch_invariant():
+    """Up to 64 rows: each output row's bits depend on its own A row only,
+    not on how many rows are in the call (the decode projections' batch
+    invariance)."""
+    r = np.random.default_rng(11)
+    N, K = 12352, 2048
+    A = _bf16(r.standard_normal((64, K)))
+    B = _bf16(r.standard_normal((N, K)) / np.sqrt(K))
+    full = torch.empty((64, N), dtype=torch.float32, device="cuda")
+    gdn.gemm_bf16(A, B, full)
+    for rows in ((0, 1), (5, 8), (16, 33), (60, 64)):
+        part = torch.empty((rows[1] - rows[0], N), dtype=torch.float32, device="cuda")
+        gdn.gemm_bf16(A[rows[0]:rows[1]], B, part)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[rows[0]:rows[1]]), rows
 
 
 def _layer_case(sh, hidden, lens, seed, with_states):
