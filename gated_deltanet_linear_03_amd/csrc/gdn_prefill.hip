@@ -258,9 +258,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 
     if (!out_role) {
         // ---------------- state waves ----------------
-        // Two operand sets in registers (ping-pong): chunk c+1's fragments
-        // load while chunk c computes, W's per k step between the products,
-        // K_d^T's after the state update.
+        // Three operand sets in registers, rotated: chunk c+2's fragments
+        // load while chunk c computes (W's per k step between the products,
+        // K_d^T's after the state update), two chunk steps ahead of use.
         struct Ops {
             u32x4 w[KTH];
             f32x4 ut[NTL];
@@ -348,21 +348,29 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             __syncthreads();
         };
 
-        Ops opA, opB;
+        Ops opA, opB, opC;
         if (c_begin < c_end) {
+            const int c1 = min(c_begin + 1, c_end - 1);
 #pragma unroll
             for (int kt = 0; kt < KTH; ++kt) load_w(opA, c_begin, kt);
             load_k(opA, c_begin);
+#pragma unroll
+            for (int kt = 0; kt < KTH; ++kt) load_w(opB, c1, kt);
+            load_k(opB, c1);
         }
         // drain the memory counter once before the loop, so the loop's waits
         // are set by its own steady-state load/store order
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        // at the top of each round opA holds chunk c and opB chunk c + 1;
+        // loads past the window's last chunk repeat that chunk (unused)
         int c = c_begin;
-        for (; c + 1 < c_end; c += 2) {
-            step(opA, opB, c, c + 1);
-            step(opB, opA, c + 1, (c + 2 < c_end) ? c + 2 : c + 1);
+        for (; c + 2 < c_end; c += 3) {
+            step(opA, opC, c, c + 2);
+            step(opB, opA, c + 1, min(c + 3, c_end - 1));
+            step(opC, opB, c + 2, min(c + 4, c_end - 1));
         }
-        if (c < c_end) step(opA, opB, c, c);
+        if (c < c_end) step(opA, opC, c, c_end - 1);
+        if (c + 1 < c_end) step(opB, opA, c + 1, c_end - 1);
 
         // leaving state
         if (hout) {
@@ -394,6 +402,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) o.p[kt] = frag(blk + L::P + (mt * KTC + kt) * 1024);
         };
+        // o rows of this lane: element offset of (row mt*16 + 4 lq, column l16)
+        // from a chunk's first row, and the stride between token rows
+        const int64_t rstride = static_cast<int64_t>(p.Hv) * DV;
+        const int64_t lane_off = (mt * 16 + lq * 4) * rstride + l16;
         auto step = [&](Ops& cur, Ops& nxt, int c, int cn) {
             const int64_t t0 = start + static_cast<int64_t>(c - cb) * C;
             const int Lc = static_cast<int>(min(static_cast<int64_t>(C), end - t0));
@@ -429,36 +441,51 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
                     for (int nt = 0; nt < NTL; ++nt) acco[nt] = mfma_h(cur.p[kt], ub[kt][nt], acco[nt]);
-                // rows past the sequence end go to a sink, so that every lane
-                // issues the same stores (the memory counter the next chunk's
-                // operand waits rely on then counts them exactly)
+                // a full chunk stores at a per-chunk base plus this lane's
+                // offset; in a partial one, rows past the sequence end go to
+                // a sink, so that every lane issues the same stores (the
+                // memory counter the next chunk's operand waits rely on then
+                // counts them exactly)
+                float* cbase = p.core + (t0 * p.Hv + h) * DV + col0;
+                if (Lc == C) {
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
+                    for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = mt * 16 + lq * 4 + i;
-                        float* dst = r < Lc ? p.core + ((t0 + r) * p.Hv + h) * DV + col0 + nt * 16 + l16
-                                            : p.sink + lane;
-                        *dst = acco[nt][i];
+                        for (int i = 0; i < 4; ++i) cbase[lane_off + i * rstride + nt * 16] = acco[nt][i];
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = mt * 16 + lq * 4 + i;
+                            float* dst = r < Lc ? cbase + lane_off + i * rstride + nt * 16 : p.sink + lane;
+                            *dst = acco[nt][i];
+                        }
                     }
                 }
             }
             __syncthreads();
         };
 
-        Ops opA, opB;
+        Ops opA, opB, opC;
         if (c_begin < c_end) {
+            const int c1 = min(c_begin + 1, c_end - 1);
 #pragma unroll
             for (int kt = 0; kt < KTH; ++kt) load_q(opA, c_begin, kt);
             load_p(opA, c_begin);
+#pragma unroll
+            for (int kt = 0; kt < KTH; ++kt) load_q(opB, c1, kt);
+            load_p(opB, c1);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
         int c = c_begin;
-        for (; c + 1 < c_end; c += 2) {
-            step(opA, opB, c, c + 1);
-            step(opB, opA, c + 1, (c + 2 < c_end) ? c + 2 : c + 1);
+        for (; c + 2 < c_end; c += 3) {
+            step(opA, opC, c, c + 2);
+            step(opB, opA, c + 1, min(c + 3, c_end - 1));
+            step(opC, opB, c + 2, min(c + 4, c_end - 1));
         }
-        if (c < c_end) step(opA, opB, c, c);
+        if (c < c_end) step(opA, opC, c, c_end - 1);
+        if (c + 1 < c_end) step(opB, opA, c + 1, c_end - 1);
     }
 
     // conv state tail: the last K-1 raw rows of (old conv state ++ inputs).
