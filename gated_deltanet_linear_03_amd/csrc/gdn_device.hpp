@@ -78,6 +78,16 @@ __device__ __forceinline__ uint2 pack4_f16(f32x4 x) {
     return uint2{pack_f16(x[0], x[1]), pack_f16(x[2], x[3])};
 }
 
+// Four floats as fp16 hi = fp16(x) and lo = fp16(x - hi) (x - hi is exact
+// in fp32 for |x| in the fp16 normal range).
+__device__ __forceinline__ void split4_f16(f32x4 x, uint2& hi, uint2& lo) {
+    hi = pack4_f16(x);
+    const f16x2 h0 = __builtin_bit_cast(f16x2, hi.x), h1 = __builtin_bit_cast(f16x2, hi.y);
+    const f32x4 r = {x[0] - static_cast<float>(h0[0]), x[1] - static_cast<float>(h0[1]),
+                     x[2] - static_cast<float>(h1[0]), x[3] - static_cast<float>(h1[1])};
+    lo = pack4_f16(r);
+}
+
 __device__ __forceinline__ u32x4 pack8_f16(const float* x) {
     return u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]),
                  pack_f16(x[6], x[7])};
@@ -135,6 +145,13 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 acc) {
 __device__ __forceinline__ f32x4 mfma_h(u32x4 a, u32x4 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+// The same on fp16 hi + lo fragments (16x16x32 f16).
+__device__ __forceinline__ f32x4 mfma_h3(u32x4 ahi, u32x4 alo, u32x4 bhi, u32x4 blo, f32x4 acc) {
+    acc = mfma_h(alo, bhi, acc);
+    acc = mfma_h(ahi, blo, acc);
+    return mfma_h(ahi, bhi, acc);
 }
 
 // acc += (a_hi + a_lo) * (b_hi + b_lo) without the lo*lo term.

@@ -65,13 +65,14 @@ struct PrefillParams {
 };
 
 // Bytes of the per-(chunk, value head) operand block for a compiled shape:
-// the scan's matrix-core operands as fp16 fragments, U~ as fp32 fragments.
+// the scan's matrix-core operands as fp16 fragments (the output products'
+// Q_G and P as hi + lo pairs), U~ as fp32 fragments.
 __host__ __device__ constexpr int ck_pad(int C) { return C < 32 ? 32 : C; }
 __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
     return 2ll * C * DK          // -W    (A fragments)
-         + 2ll * C * DK          // Q_G   (A fragments)
+         + 4ll * C * DK          // Q_G   (A fragments, hi and lo)
          + 2ll * DK * ck_pad(C)  // K_d^T (A fragments)
-         + 2ll * C * ck_pad(C)   // P     (A fragments)
+         + 4ll * C * ck_pad(C)   // P     (A fragments, hi and lo)
          + 4ll * C * DV;         // U~    (fp32 accumulator fragments)
 }
 

@@ -108,9 +108,11 @@ struct VchLayout {
     static constexpr int CK = ck_pad(C);
     static constexpr int64_t negW = 0;
     static constexpr int64_t QG = negW + 2ll * C * DK;
-    static constexpr int64_t KdT = QG + 2ll * C * DK;
+    static constexpr int64_t QGl = QG + 2ll * C * DK;       // lo parts, same tile order
+    static constexpr int64_t KdT = QGl + 2ll * C * DK;
     static constexpr int64_t P = KdT + 2ll * DK * CK;
-    static constexpr int64_t Ut = P + 2ll * C * CK;
+    static constexpr int64_t Pl = P + 2ll * C * CK;
+    static constexpr int64_t Ut = Pl + 2ll * C * CK;
     static constexpr int64_t bytes = Ut + 4ll * C * DV;
     static_assert(bytes == vch_bytes(DK, DV, C), "layout");
 };
@@ -154,10 +156,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     static_assert(DV % DVS == 0 && DVS % 16 == 0 && DK % 32 == 0 && C % 16 == 0, "shape");
     static_assert(MT <= NW, "one chunk-row tile per wave");
 
-    // the matrix-core copies of H^T and U^T (fp16; the state itself stays in
-    // fp32 accumulators)
+    // the matrix-core copies of H^T and U^T as fp16 hi and lo parts (the
+    // state itself stays in fp32 accumulators); the state chain uses the hi
+    // parts, the output products both
     __shared__ __align__(16) uint16_t HT[DVS * HS];
+    __shared__ __align__(16) uint16_t HTl[DVS * HS];
     __shared__ __align__(16) uint16_t UT[DVS * US];
+    __shared__ __align__(16) uint16_t UTl[DVS * US];
 
     // XCD-aware order: the NS slices of one head land on the same XCD
     // (consecutive work-groups are dealt round-robin over the 8 XCDs), so the
@@ -187,7 +192,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     const bool has_row = (MT >= NW) || mt < MT;
 
     // zero U^T (including the padded chunk rows C..CK-1, never written later)
-    for (int i = tid; i < DVS * US; i += kScanThreads) UT[i] = 0;
+    for (int i = tid; i < DVS * US; i += kScanThreads) {
+        UT[i] = 0;
+        UTl[i] = 0;
+    }
 
     // entering state: the caller's initial state where the sequence starts,
     // else what the previous window left in the carry slot of its parity
@@ -211,7 +219,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) {
                 const int off = (nt * 16 + l16) * HS + mth * 16 + lq * 4;
-                *reinterpret_cast<uint2*>(&HT[off]) = pack4_f16(hacc[qh][nt]);
+                uint2 hi, lo;
+                split4_f16(hacc[qh][nt], hi, lo);
+                *reinterpret_cast<uint2*>(&HT[off]) = hi;
+                *reinterpret_cast<uint2*>(&HTl[off]) = lo;
             }
         }
     };
@@ -241,17 +252,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
         return p.vch + (static_cast<int64_t>(c - p.win_lo) * p.Hv + h) * L::bytes;
     };
     // B fragments of H^T (k over dk) and of U^T (k over the chunk) from LDS
-    auto read_H = [&](int kt, u32x4* b) {
+    auto read_H = [&](const uint16_t* ht, int kt, u32x4* b) {
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
-            b[nt] = *reinterpret_cast<const u32x4*>(&HT[(nt * 16 + l16) * HS + kt * 32 + lq * 8]);
+            b[nt] = *reinterpret_cast<const u32x4*>(&ht[(nt * 16 + l16) * HS + kt * 32 + lq * 8]);
     };
-    auto read_U = [&](u32x4 (*ub)[NTL]) {
+    auto read_U = [&](const uint16_t* ut, u32x4 (*ub)[NTL]) {
 #pragma unroll
         for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt)
-                ub[kt][nt] = *reinterpret_cast<const u32x4*>(&UT[(nt * 16 + l16) * US + kt * 32 + lq * 8]);
+                ub[kt][nt] = *reinterpret_cast<const u32x4*>(&ut[(nt * 16 + l16) * US + kt * 32 + lq * 8]);
     };
     // one lane's 16 bytes of a 1 KiB fp16 fragment tile
     auto frag = [&](const uint8_t* tile) { return *reinterpret_cast<const u32x4*>(tile + lane * 16); };
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 load_w(nxt, cn, kt);
                 if (!has_row) continue;
                 u32x4 b[NTL];
-                read_H(kt, b);
+                read_H(HT, kt, b);
                 f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h(cur.w[kt], b[nt], a[nt]);
@@ -318,13 +329,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                     f32x4 u;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) u[i] = a0[nt][i] + a1[nt][i];
-                    *reinterpret_cast<uint2*>(&UT[(nt * 16 + l16) * US + mt * 16 + lq * 4]) = pack4_f16(u);
+                    uint2 hi, lo;
+                    split4_f16(u, hi, lo);
+                    *reinterpret_cast<uint2*>(&UT[(nt * 16 + l16) * US + mt * 16 + lq * 4]) = hi;
+                    *reinterpret_cast<uint2*>(&UTl[(nt * 16 + l16) * US + mt * 16 + lq * 4]) = lo;
                 }
             }
             __syncthreads();
             // (3) H' = e^{gamma_last} H + K_d^T U
             u32x4 ub[KTC][NTL];
-            read_U(ub);
+            read_U(UT, ub);
 #pragma unroll
             for (int qh = 0; qh < QH; ++qh) {
                 if (!ALL_H && wave + NW * qh >= MTH) continue;
@@ -390,17 +404,23 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     } else {
         // ---------------- output waves ----------------
         struct Ops {
-            u32x4 q[KTH];
-            u32x4 p[KTC];
+            u32x4 q[KTH], ql[KTH];
+            u32x4 p[KTC], pl[KTC];
         };
         auto load_q = [&](Ops& o, int c, int kt) {
-            if (has_row) o.q[kt] = frag(block_of(c) + L::QG + (mt * KTH + kt) * 1024);
+            if (!has_row) return;
+            const uint8_t* blk = block_of(c);
+            o.q[kt] = frag(blk + L::QG + (mt * KTH + kt) * 1024);
+            o.ql[kt] = frag(blk + L::QGl + (mt * KTH + kt) * 1024);
         };
         auto load_p = [&](Ops& o, int c) {
             if (!has_row) return;
             const uint8_t* blk = block_of(c);
 #pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) o.p[kt] = frag(blk + L::P + (mt * KTC + kt) * 1024);
+            for (int kt = 0; kt < KTC; ++kt) {
+                o.p[kt] = frag(blk + L::P + (mt * KTC + kt) * 1024);
+                o.pl[kt] = frag(blk + L::Pl + (mt * KTC + kt) * 1024);
+            }
         };
         // o rows of this lane: element offset of (row mt*16 + 4 lq, column l16)
         // from a chunk's first row, and the stride between token rows
@@ -420,17 +440,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             for (int kt = 0; kt < KTH; ++kt) {
                 load_q(nxt, cn, kt);
                 if (!has_row) continue;
-                u32x4 b[NTL];
-                read_H(kt, b);
+                u32x4 b[NTL], bl[NTL];
+                read_H(HT, kt, b);
+                read_H(HTl, kt, bl);
                 f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h(cur.q[kt], b[nt], a[nt]);
+                for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h3(cur.q[kt], cur.ql[kt], b[nt], bl[nt], a[nt]);
             }
             __syncthreads();
             if (has_row) {
                 // (2) O += P U, store the valid rows
-                u32x4 ub[KTC][NTL];
-                read_U(ub);
+                u32x4 ub[KTC][NTL], ubl[KTC][NTL];
+                read_U(UT, ub);
+                read_U(UTl, ubl);
                 load_p(nxt, cn);
                 f32x4 acco[NTL];
 #pragma unroll
@@ -440,7 +462,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 #pragma unroll
                 for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) acco[nt] = mfma_h(cur.p[kt], ub[kt][nt], acco[nt]);
+                    for (int nt = 0; nt < NTL; ++nt)
+                        acco[nt] = mfma_h3(cur.p[kt], cur.pl[kt], ub[kt][nt], ubl[kt][nt], acco[nt]);
                 // a full chunk stores at a per-chunk base plus this lane's
                 // offset; in a partial one, rows past the sequence end go to
                 // a sink, so that every lane issues the same stores (the

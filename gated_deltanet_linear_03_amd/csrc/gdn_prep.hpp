@@ -19,8 +19,9 @@
 //           16-token blocks, split-bf16 MFMA; a wave runs one W and one U~
 //           column tile of a head, which share the A and T fragments
 // and writes, per value head, the scan's operands in MFMA fragment order:
-// -W, Q_G = diag(e^gamma) Q^, K_d^T = (diag(e^{gamma_last - gamma}) K^)^T
-// and P as fp16, U~ as fp32, plus e^{gamma_last}.  (Chunk form of Yang,
+// -W and K_d^T = (diag(e^{gamma_last - gamma}) K^)^T as fp16, Q_G =
+// diag(e^gamma) Q^ and P as fp16 hi + lo pairs (the output products run
+// split), U~ as fp32, plus e^{gamma_last}.  (Chunk form of Yang,
 // Kautz, Hatamizadeh, "Gated Delta Networks", ICLR 2025, on the UT
 // transform of Yang et al., NeurIPS 2024.)  Every value head's operands are
 // the same bits whichever GH produced them.
@@ -36,17 +37,18 @@ struct PrepSmem {
     static constexpr int NB = C / 16;
     static constexpr int SQ = DK + 8;    // bf16 row stride of Q^, K^ [C][SQ]; fp16 stride of the -W staging
     static constexpr int SV = DV + 8;    // fp32 row stride of V^ [C][SV]
-    static constexpr int SP = C + 8;     // fp16 row stride of P [C][SP]
-    static constexpr int SA = C + 8;     // bf16 row stride of -A below the diagonal blocks [C][SA]
+    static constexpr int SP = C + 8;     // fp16 row stride of P (hi, lo) [C][SP]
+    static constexpr int NBLK = NB * (NB - 1) / 2;   // 16x16 blocks of A below the diagonal blocks
+    static constexpr int SAB = 24;       // bf16 row stride inside a block of -A (hi, lo) [NBLK][16][SAB]
     static constexpr int SD = 20;        // fp32 row stride of A's diagonal blocks [NB][16][SD]
     static constexpr int STT = 24;       // bf16 row stride of the blocks T_bb [NB][16][STT]
     static constexpr int qk_bytes = C * SQ * 4;     // hi + lo
     static constexpr int w_bytes = (2 * DK + GH * DV) * 16;
     static constexpr int v_bytes = C * SV * 4;
-    // per value head, after the conv: A's diagonal blocks, -A (hi, lo), P, T_bb (hi, lo)
+    // per value head, after the conv: A's diagonal blocks, -A (hi, lo), P (hi, lo), T_bb (hi, lo)
     static constexpr int ad_bytes = NB * 16 * SD * 4;
-    static constexpr int a_bytes = C * SA * 4;
-    static constexpr int p_bytes = C * SP * 2;
+    static constexpr int a_bytes = NBLK * 16 * SAB * 4;
+    static constexpr int p_bytes = C * SP * 4;
     static constexpr int tt_bytes = NB * 16 * STT * 4;
     static constexpr int oA = ad_bytes, oP = oA + a_bytes, oT = oP + p_bytes;
     static constexpr int head_bytes = oT + tt_bytes;
@@ -176,7 +178,8 @@ template <int DK, int DV, int C, int GH, bool BF16>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     using S = PrepSmem<DK, DV, C, GH>;
     using L = VchLayout<DK, DV, C>;
-    constexpr int CK = S::CK, SQ = S::SQ, SV = S::SV, SP = S::SP, SA = S::SA, SD = S::SD, STT = S::STT;
+    constexpr int CK = S::CK, SQ = S::SQ, SV = S::SV, SP = S::SP, SAB = S::SAB, SD = S::SD, STT = S::STT;
+    constexpr int NBLK = S::NBLK;
     constexpr int NB = C / 16;           // 16-token blocks in a chunk
     constexpr int NT = kPrepThreads;
     constexpr int NW = NT / kWave;
@@ -194,8 +197,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     auto hb = [&](int g) { return smem + S::oR + g * S::head_bytes; };
     auto sAd = [&](int g) { return reinterpret_cast<float*>(hb(g)); };
     auto sAh = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oA); };
-    auto sAl = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oA) + C * SA; };
+    auto sAl = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oA) + NBLK * 16 * SAB; };
     auto sP = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oP); };
+    auto sPl = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oP) + C * SP; };
+    // block (i, j), j < i, of -A: NBLK blocks of 16 x 16 in row-major block order
+    auto ablk = [&](int i, int j) { return (i * (i - 1) / 2 + j) * 16 * SAB; };
     auto sTh = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oT); };
     auto sTl = [&](int g) { return reinterpret_cast<uint16_t*>(hb(g) + S::oT) + NB * 16 * STT; };
     auto sW = [&](int g) { return sQh + g * C * SQ; };      // -W staging (fp16) over Q^
@@ -469,16 +475,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 br[g] = *reinterpret_cast<const f32x4*>(sbeta(g) + r0);
                 gs[g] = sgam(g)[s];
             }
-            if (isq) {
+            if (isq) {                                       // P as fp16 hi + lo
 #pragma unroll
                 for (int g = 0; g < GH; ++g)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float d = exp_neg(gr[g][i] - gs[g]);
-                        sP(g)[(r0 + i) * SP + s] = __builtin_bit_cast(
-                            uint16_t, static_cast<_Float16>((s <= r0 + i) ? acc[i] * d : 0.f));
+                        const float v = (s <= r0 + i) ? acc[i] * d : 0.f;
+                        const _Float16 hi = static_cast<_Float16>(v);
+                        sP(g)[(r0 + i) * SP + s] = __builtin_bit_cast(uint16_t, hi);
+                        sPl(g)[(r0 + i) * SP + s] =
+                            __builtin_bit_cast(uint16_t, static_cast<_Float16>(v - static_cast<float>(hi)));
                     }
             } else {                                         // -A split, a matrix-core operand
+                const int bo = ablk(mt, nt) + (lq * 4) * SAB + l16;
 #pragma unroll
                 for (int g = 0; g < GH; ++g)
 #pragma unroll
@@ -486,8 +496,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                         const float d = exp_neg(gr[g][i] - gs[g]);
                         uint16_t hi, lo;
                         split_bf16(-(br[g][i] * d * acc[i]), hi, lo);
-                        sAh(g)[(r0 + i) * SA + s] = hi;
-                        sAl(g)[(r0 + i) * SA + s] = lo;
+                        sAh(g)[bo + i * SAB] = hi;
+                        sAl(g)[bo + i * SAB] = lo;
                     }
             }
         }
@@ -504,10 +514,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
 #pragma unroll
             for (int g = 0; g < GH; ++g) {
                 const float e = sE(g)[r];
-                float y[8];
+                float y[8], yl[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] = x[i] * e;
+                for (int i = 0; i < 8; ++i) {
+                    y[i] = x[i] * e;
+                    yl[i] = y[i] - static_cast<float>(static_cast<_Float16>(y[i]));
+                }
                 *reinterpret_cast<u32x4*>(blk(g) + L::QG + tile * 1024 + ln * 16) = pack8_f16(y);
+                *reinterpret_cast<u32x4*>(blk(g) + L::QGl + tile * 1024 + ln * 16) = pack8_f16(yl);
             }
         }
     }
@@ -544,7 +558,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             }
 #pragma unroll
             for (int j = 0; j < i; ++j) {
-                const int ao = (16 * i + l16) * SA + 16 * j + 4 * lq;
+                const int ao = ablk(i, j) + l16 * SAB + 4 * lq;
                 const uint2 a_h = *reinterpret_cast<const uint2*>(ahp + ao);
                 const uint2 a_l = *reinterpret_cast<const uint2*>(alp + ao);
                 if (has_w) aw = mfma3_k16(a_h, a_l, wh[j], wl[j], aw);
@@ -591,8 +605,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         const int r = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
         // eight columns of one 16-column tile: tiles above the diagonal and
         // columns past C are zero
-        const u32x4 v = (s0 / 16 <= r / 16 && s0 < C) ? lds16(sP(g) + r * SP + s0) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(blk(g) + L::P + tile * 1024 + ln * 16) = v;
+        const bool nz = s0 / 16 <= r / 16 && s0 < C;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(blk(g) + L::P + tile * 1024 + ln * 16) = nz ? lds16(sP(g) + r * SP + s0) : zero;
+        *reinterpret_cast<u32x4*>(blk(g) + L::Pl + tile * 1024 + ln * 16) = nz ? lds16(sPl(g) + r * SP + s0) : zero;
     }
     for (int sl = tid; sl < DK * CK / 8; sl += NT) {              // K_d^T [DK][CK]
         const int tile = sl / 64, ln = sl % 64;

@@ -45,10 +45,11 @@ def dims(sh):
 
 
 def chunk_slot_bytes(Hv, dk, dv, C):
-    """Operand-block bytes of one chunk slot (all value heads): -W, Q_G,
-    K_d^T and P as fp16 fragments, U~ as fp32 fragments."""
+    """Operand-block bytes of one chunk slot (all value heads): -W and K_d^T
+    as fp16 fragments, Q_G and P as fp16 hi + lo fragments, U~ as fp32
+    fragments."""
     CK = max(C, 32)
-    return Hv * (2 * C * dk * 2 + 2 * dk * CK + 2 * C * CK + 4 * C * dv)
+    return Hv * (2 * C * dk + 4 * C * dk + 2 * dk * CK + 4 * C * CK + 4 * C * dv)
 
 
 def default_window_slots(layer, N, T):

@@ -221,7 +221,7 @@ def test_prefill_windows_follow_the_workspace():
                     conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
                     dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
     # -W, Q_G, K_d^T, P as fp16 fragments and U~ as fp32, for 32 value heads
-    slot = 32 * (2 * 64 * 128 * 2 + 2 * 128 * 64 + 2 * 64 * 64 + 4 * 64 * 128)
+    slot = 32 * (2 * 64 * 128 + 4 * 64 * 128 + 2 * 128 * 64 + 4 * 64 * 64 + 4 * 64 * 128)
 
     def window(n_chunks):
         w = min((144 << 20) // slot, n_chunks)

@@ -91,6 +91,28 @@ def test_prefill_wide_batch_bitwise_vs_alone():
     check_prefill(case, packed, oracle_prefill(case), label="wide-batch")
 
 
+def test_prefill_more_sequences_than_threads():
+    """1500 sequences of 0-5 tokens: the first prep window's block-wide chunk
+    table then takes two sequences per thread, and the scan runs one
+    work-group per (sequence, head, slice) group."""
+    lens = [int(v) for v in np.random.default_rng(51).integers(0, 6, 1500)]
+    case = synth.prefill_case(synth.TINY, lens, seed=52, with_state=True,
+                              with_conv_state=True)
+    res = gpu_prefill(case)
+    check_prefill(case, res, oracle_prefill(case), label="1500-seqs")
+    # the table the first window wrote is the one the later kernels used: a
+    # sequence alone gives the same bits
+    cu = case.cu_seqlens
+    for n in (0, 777, 1499):
+        a, b = int(cu[n]), int(cu[n + 1])
+        alone = synth.PrefillCase(case.shape, np.array([0, b - a], dtype=np.int32),
+                                  {k: v[a:b] for k, v in case.inputs.items()}, case.params,
+                                  case.initial_state[n:n + 1], case.conv_state[n:n + 1])
+        r = gpu_prefill(alone)
+        assert torch.equal(r["out"], res["out"][a:b]), n
+        assert torch.equal(r["final_state"][0], res["final_state"][n]), n
+
+
 def test_prefill_dk_ne_dv():
     """dk = 32, dv = 64: a transposed state would not match."""
     sh = synth.LayerShape(Hk=2, Hv=4, dk=32, dv=64, chunk=16, act_dtype="bf16")
