@@ -413,11 +413,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             o.q[kt] = frag(blk + L::QG + (mt * KTH + kt) * 1024);
             o.ql[kt] = frag(blk + L::QGl + (mt * KTH + kt) * 1024);
         };
+        // P tiles wholly above the diagonal (first column past the tile's
+        // last row) are zero: prep does not write them and they are neither
+        // loaded nor multiplied
+        auto p_tile = [&](int kt) { return kt * 32 <= mt * 16 + 15; };
         auto load_p = [&](Ops& o, int c) {
             if (!has_row) return;
             const uint8_t* blk = block_of(c);
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
+                if (!p_tile(kt)) continue;
                 o.p[kt] = frag(blk + L::P + (mt * KTC + kt) * 1024);
                 o.pl[kt] = frag(blk + L::Pl + (mt * KTC + kt) * 1024);
             }
@@ -460,10 +465,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acco[nt][i] = a0[nt][i] + a1[nt][i];
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt)
+                for (int kt = 0; kt < KTC; ++kt) {
+                    if (!p_tile(kt)) continue;
 #pragma unroll
                     for (int nt = 0; nt < NTL; ++nt)
                         acco[nt] = mfma_h3(cur.p[kt], cur.pl[kt], ub[kt][nt], ubl[kt][nt], acco[nt]);
+                }
                 // a full chunk stores at a per-chunk base plus this lane's
                 // offset; in a partial one, rows past the sequence end go to
                 // a sink, so that every lane issues the same stores (the

@@ -603,6 +603,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         const int g = sl / NPS, tile = (sl % NPS) / 64, ln = sl % 64;
         const int mt = tile / (CK / 32), kt = tile % (CK / 32);
         const int r = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
+        if (kt * 32 > mt * 16 + 15) continue;       // a zero tile: never read
         // eight columns of one 16-column tile: tiles above the diagonal and
         // columns past C are zero
         const bool nz = s0 / 16 <= r / 16 && s0 < C;
