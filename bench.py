@@ -43,8 +43,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--decode-batches", default="64,3,1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -191,29 +191,41 @@ def main():
     for i in range(W):
         prefill_step(layer, sets[i % NSET], cu, 1, T, out, fs, cs)
     torch.cuda.synchronize()
-    evs = [new_events(len(names) + 1) for _ in range(K)]
+    # timed region: K plain steps between two events (an event recorded
+    # between launches costs several microseconds of its own, so the
+    # per-kernel times come from a second, instrumented pass below)
     e0, e1 = new_events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(K):
-        prefill_step(layer, sets[i % NSET], cu, 1, T, out, fs, cs, events=evs[i])
+        prefill_step(layer, sets[i % NSET], cu, 1, T, out, fs, cs)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / K
+    tok_s = T / (ms_step * 1e-3)
+    # instrumented pass: the same K steps with an event before every launch
+    evs = [new_events(len(names) + 1) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        prefill_step(layer, sets[i % NSET], cu, 1, T, out, fs, cs, events=evs[i])
+    torch.cuda.synchronize()
     steps_ms = sorted(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K))
     pct = lambda q: steps_ms[min(K - 1, int(round(q * (K - 1))))]
     kern_ms, kern_n = kernel_ms(evs, K)
-    tok_s = T / (ms_step * 1e-3)
-    log(f"prefill 4k: {ms_step:.3f} ms/step ({wall / K * 1e3:.3f} wall; median {pct(0.5):.3f}, "
-        f"p10 {pct(0.1):.3f}, p90 {pct(0.9):.3f}) {tok_s:.4g} tok/s kernels {kern_ms} launches {kern_n}")
+    log(f"prefill 4k: {ms_step:.3f} ms/step ({wall / K * 1e3:.3f} wall) {tok_s:.4g} tok/s; with an event "
+        f"between launches: median {pct(0.5):.3f}, p10 {pct(0.1):.3f}, p90 {pct(0.9):.3f} ms, "
+        f"kernels {kern_ms} launches {kern_n}")
     # the same with one input set: Infinity-Cache-warm inputs (context only)
-    warm_ev = [new_events(len(names) + 1) for _ in range(K)]
-    for i in range(K):
-        prefill_step(layer, x, cu, 1, T, out, fs, cs, events=warm_ev[i])
+    w0, w1 = new_events(2)
     torch.cuda.synchronize()
-    warm_ms = sum(warm_ev[i][0].elapsed_time(warm_ev[i][-1]) for i in range(K)) / K
+    w0.record(stream)
+    for i in range(K):
+        prefill_step(layer, x, cu, 1, T, out, fs, cs)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
     log(f"prefill 4k, one input set (cache-warm): {warm_ms:.3f} ms/step")
     del sets
 
@@ -254,7 +266,7 @@ def main():
         "roofline": roof,
         "prefill_kernels_ms": kern_ms,
         "prefill_kernel_launches": kern_n,
-        "ms_per_step_median_p10_p90": [pct(0.5), pct(0.1), pct(0.9)],
+        "instrumented_ms_per_step_median_p10_p90": [pct(0.5), pct(0.1), pct(0.9)],
         "input_sets": NSET,
         "ms_per_step_one_input_set": warm_ms,
         "prefill_kernel_roofline": {k: dict(v, frac=v["achieved"] / v["peak"]) for k, v in rl.items()},
@@ -329,15 +341,20 @@ def main():
             for _ in range(W):
                 dstep()
             torch.cuda.synchronize()
-            devs = [[new_events(2) for _ in range(L)] for _ in range(K)]
             d0, d1 = new_events(2)
             torch.cuda.synchronize()
             d0.record(stream)
             for i in range(K):
-                dstep(devs[i])
+                dstep()
             d1.record(stream)
             torch.cuda.synchronize()
             ms = d0.elapsed_time(d1) / K
+            # kernel times from a second pass with events around each launch
+            devs = [[new_events(2) for _ in range(L)] for _ in range(K)]
+            torch.cuda.synchronize()
+            for i in range(K):
+                dstep(devs[i])
+            torch.cuda.synchronize()
             kms = sum(devs[i][l][0].elapsed_time(devs[i][l][1]) for i in range(K) for l in range(L)) / (K * L)
             state_gbs = L * B * state_per_seq / (ms * 1e-3) / 1e9
             all_gbs = L * B * per_seq / (ms * 1e-3) / 1e9
@@ -397,14 +414,18 @@ def main():
         for _ in range(W):
             vstep()
         torch.cuda.synchronize()
-        vevs = [[new_events(2) for _ in range(L)] for _ in range(K)]
         v0, v1 = new_events(2)
         v0.record(stream)
         for i in range(K):
-            vstep(vevs[i])
+            vstep()
         v1.record(stream)
         torch.cuda.synchronize()
         vms = v0.elapsed_time(v1) / K
+        vevs = [[new_events(2) for _ in range(L)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            vstep(vevs[i])
+        torch.cuda.synchronize()
         vkms = sum(vevs[i][l][0].elapsed_time(vevs[i][l][1]) for i in range(K) for l in range(L)) / (K * L)
         result["verify"] = {"B": VB, "tokens": VT, "layers": L, "ms_per_step": vms,
                             "tokens_per_s": VB * VT / (vms * 1e-3),
@@ -434,14 +455,19 @@ def main():
         prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0)
         torch.cuda.synchronize()
         lnames = gdn.prefill_launches(lay, NN, TT, ws.numel())
-        ev = [new_events(len(lnames) + 1) for _ in range(reps)]
         a0, a1 = new_events(2)
         a0.record(stream)
         for i in range(reps):
-            prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0, events=ev[i])
+            prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0)
         a1.record(stream)
         torch.cuda.synchronize()
         ms = a0.elapsed_time(a1) / reps
+        # kernel times from a second pass with an event before every launch
+        ev = [new_events(len(lnames) + 1) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            prefill_step(lay, xx, cuu, NN, TT, oo, ff, cc, S0=S0, events=ev[i])
+        torch.cuda.synchronize()
         km = {}
         for j, n in enumerate(lnames):
             km[n] = km.get(n, 0.0) + sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(reps)) / reps
