@@ -298,7 +298,10 @@ def main():
     # ---------------- decode, 30 layers x B ----------------
     if not args.no_decode:
         L = args.layers
-        Bmax = max(int(b) for b in args.decode_batches.split(","))
+        # multi-token verify below: VB sequences x VT draft tokens, on the
+        # same state pool, which therefore holds at least VB sequences
+        VB, VT = 8, 4
+        Bmax = max([int(b) for b in args.decode_batches.split(",")] + [VB])
         gen = torch.Generator(device=dev)
         layers, states, convs, toks = [], [], [], []
         Tpre = 2048
@@ -393,7 +396,6 @@ def main():
         result["decode"] = dec
 
         # multi-token verify: VB sequences x VT draft tokens x the same layers
-        VB, VT = 8, 4
         vt = []
         for l in range(L):
             gen.manual_seed(2000 + l)

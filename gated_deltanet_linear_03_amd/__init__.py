@@ -203,6 +203,72 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _need(t, name, rows, row_elems, esize=None, whole=False):
+    """Raise ValueError unless t (None passes) is a device tensor of at least
+    `rows` rows, each of at least `row_elems` elements stored densely, with
+    element size `esize`; with whole=True the rows must also be packed
+    back to back.  The library trusts the sizes it is given, so buffers are
+    measured here, before any launch, rather than read out of bounds."""
+    if t is None:
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: a device tensor is required")
+    if t.dim() < 1 or int(t.shape[0]) < rows:
+        raise ValueError(f"{name}: {rows} rows needed, shape is {tuple(t.shape)}")
+    per_row = 1
+    for d in t.shape[1:]:
+        per_row *= int(d)
+    if per_row < row_elems:
+        raise ValueError(f"{name}: rows of {row_elems} elements needed, shape is {tuple(t.shape)}")
+    if esize is not None and t.element_size() != esize:
+        raise ValueError(f"{name}: {esize}-byte elements needed, not {t.element_size()}")
+    step = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if int(t.shape[d]) != 1 and int(t.stride(d)) != step:
+            raise ValueError(f"{name}: the elements of a row must be contiguous")
+        step *= int(t.shape[d])
+    if whole and t.dim() > 1 and int(t.shape[0]) > 1 and int(t.stride(0)) != step:
+        raise ValueError(f"{name}: rows must be packed back to back")
+
+
+def _act_size(layer) -> int:
+    return 2 if layer.act_dtype == GDN_DTYPE_BF16 else 4
+
+
+def _out_size(layer) -> int:
+    return 2 if layer.out_dtype == GDN_DTYPE_BF16 else 4
+
+
+def _check_tokens(layer, rows, q, k, v, z, a, b, out, core_out):
+    asz = _act_size(layer)
+    _need(q, "q", rows, layer.Hk * layer.dk, asz)
+    _need(k, "k", rows, layer.Hk * layer.dk, asz)
+    _need(v, "v", rows, layer.Hv * layer.dv, asz)
+    _need(z, "z", rows, layer.Hv * layer.dv, asz)
+    _need(a, "a", rows, layer.Hv, asz)
+    _need(b, "b", rows, layer.Hv, asz)
+    _need(out, "out", rows, layer.Hv * layer.dv, _out_size(layer), whole=True)
+    _need(core_out, "core_out", rows, layer.Hv * layer.dv, 4, whole=True)
+
+
+def _check_states(layer, rows, state_in, state_out, conv_state_in, conv_state_out,
+                  names=("state_in", "state_out")):
+    se = layer.Hv * layer.dk * layer.dv
+    ce = (layer.conv_K - 1) * layer.Cc
+    _need(state_in, names[0], rows, se, 4, whole=True)
+    _need(state_out, names[1], rows, se, 4, whole=True)
+    _need(conv_state_in, "conv_state_in", rows, ce, _act_size(layer), whole=True)
+    _need(conv_state_out, "conv_state_out", rows, ce, _act_size(layer), whole=True)
+
+
+def _check_index(t, name, n):
+    if t is None:
+        return
+    if not getattr(t, "is_cuda", False) or t.element_size() != 4 or t.numel() < n \
+            or not t.is_contiguous():
+        raise ValueError(f"{name}: a contiguous device int32 tensor of {n} entries is required")
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -235,6 +301,10 @@ class Layer:
         return 2 * self.Hk * self.dk + self.Hv * self.dv
 
     def c(self) -> CLayer:
+        _need(self.conv_w, "conv_w", self.Cc, self.conv_K, 4, whole=True)
+        _need(self.A_log, "A_log", self.Hv, 1, 4, whole=True)
+        _need(self.dt_bias, "dt_bias", self.Hv, 1, 4, whole=True)
+        _need(self.norm_w, "norm_w", self.dv, 1, 4, whole=True)
         scale = self.scale if self.scale is not None else self.dk ** -0.5
         return CLayer(self.Hk, self.Hv, self.dk, self.dv, self.conv_K, self.chunk,
                       self.act_dtype, self.out_dtype, scale, self.eps_l2,
@@ -267,8 +337,13 @@ def prefill_launches(layer: Layer, N: int, T_total: int, workspace_bytes: int | 
     return ["prep", "scan"] * ((n - 1) // 2) + ["epi"]
 
 
-def _prefill_io(N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
+def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
                 final_state, conv_state_in, conv_state_out, state_slots, num_slots):
+    _check_tokens(layer, int(T_total), q, k, v, z, a, b, out, core_out)
+    _check_index(cu_seqlens, "cu_seqlens", int(N) + 1)
+    _check_index(state_slots, "state_slots", int(N))
+    _check_states(layer, int(num_slots) if state_slots is not None else int(N), initial_state,
+                  final_state, conv_state_in, conv_state_out, ("initial_state", "final_state"))
     return CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
                       _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
                       _tok_stride(q), _tok_stride(k), _tok_stride(v),
@@ -278,8 +353,12 @@ def _prefill_io(N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial
                       int(num_slots))
 
 
-def _decode_io(B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
-               conv_state_out, state_slots, num_slots):
+def _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
+               conv_state_out, state_slots, num_slots, tokens=1):
+    _check_tokens(layer, int(B) * int(tokens), q, k, v, z, a, b, out, core_out)
+    _check_index(state_slots, "state_slots", int(B))
+    _check_states(layer, int(num_slots) if state_slots is not None else int(B), state_in,
+                  state_out, conv_state_in, conv_state_out)
     return CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
                      _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
                      _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
@@ -297,7 +376,7 @@ def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
     torch.cuda.Event(enable_timing=True) objects; the call then goes through
     ``gdn_prefill_timed`` and consecutive events bracket each kernel."""
     cl = layer.c()
-    io = _prefill_io(N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
+    io = _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
                      final_state, conv_state_in, conv_state_out, state_slots, num_slots)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -355,7 +434,7 @@ def decode_raw(layer: Layer, *, B, q, k, v, z, a, b, out, state_in, state_out,
     """Call ``gdn_decode`` on caller-provided buffers (no allocation).  With
     state_slots (device int32 [B]) the states are pools of num_slots entries."""
     cl = layer.c()
-    io = _decode_io(B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
+    io = _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
                     conv_state_out, state_slots, num_slots)
     _check(lib().gdn_decode(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
 
@@ -370,14 +449,14 @@ def step_raw(layer: Layer, *, prefill=None, decode=None, workspace=None, workspa
         f = dict(core_out=None, initial_state=None, final_state=None, conv_state_in=None,
                  conv_state_out=None, state_slots=None, num_slots=0)
         f.update(prefill)
-        pio = _prefill_io(f["N"], f["T_total"], f["cu_seqlens"], f["q"], f["k"], f["v"], f["z"],
+        pio = _prefill_io(layer, f["N"], f["T_total"], f["cu_seqlens"], f["q"], f["k"], f["v"], f["z"],
                           f["a"], f["b"], f["out"], f["core_out"], f["initial_state"],
                           f["final_state"], f["conv_state_in"], f["conv_state_out"],
                           f["state_slots"], f["num_slots"])
     if decode is not None:
         f = dict(core_out=None, state_slots=None, num_slots=0)
         f.update(decode)
-        dio = _decode_io(f["B"], f["q"], f["k"], f["v"], f["z"], f["a"], f["b"], f["out"],
+        dio = _decode_io(layer, f["B"], f["q"], f["k"], f["v"], f["z"], f["a"], f["b"], f["out"],
                          f["core_out"], f["state_in"], f["state_out"], f["conv_state_in"],
                          f["conv_state_out"], f["state_slots"], f["num_slots"])
     if workspace_bytes is None:
@@ -396,8 +475,10 @@ def decode_multi_raw(layer: Layer, *, B, tokens, q, k, v, z, a, b, out, state_in
     """Call ``gdn_decode_multi``: `tokens` tokens for each of B sequences
     (token tensors with B * tokens rows, sequence-major)."""
     cl = layer.c()
-    io = _decode_io(B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
-                    conv_state_out, None, 0)
+    io = _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
+                    conv_state_out, None, 0, tokens=tokens)
+    _need(state_snapshots, "state_snapshots", int(B),
+          int(tokens) * layer.Hv * layer.dk * layer.dv, 4, whole=True)
     _check(lib().gdn_decode_multi(ctypes.byref(cl), ctypes.byref(io), int(tokens),
                                   _ptr(state_snapshots), _stream(stream)))
 
@@ -456,6 +537,9 @@ def gemm_bf16(A, B, C, stream=None):
     import torch
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[0])
+    _need(A, "A", M, K, 2)
+    _need(B, "B", N, K, 2)
+    _need(C, "C", M, N)
     cd = GDN_DTYPE_BF16 if C.dtype == torch.bfloat16 else GDN_DTYPE_FP32
     _check(lib().gdn_gemm_bf16(_ptr(A), int(A.stride(0)), _ptr(B), int(B.stride(0)), _ptr(C),
                                int(C.stride(0)), cd, M, N, K, _stream(stream)))
@@ -469,6 +553,11 @@ class Proj:
     hidden: int
     w_in: object
     w_out: object
+
+    def check(self, layer: Layer):
+        P = 2 * layer.Hk * layer.dk + 2 * layer.Hv * layer.dv + 2 * layer.Hv
+        _need(self.w_in, "w_in", P, self.hidden, 2, whole=True)
+        _need(self.w_out, "w_out", self.hidden, layer.Hv * layer.dv, 2, whole=True)
 
     def c(self) -> CProj:
         return CProj(self.hidden, _ptr(self.w_in), _ptr(self.w_out))
@@ -490,6 +579,13 @@ def layer_prefill_raw(layer: Layer, proj: Proj, *, N, T_total, cu_seqlens, x, y,
     or fp32), through in_proj, the layer and out_proj."""
     import torch
     cl, cp = layer.c(), proj.c()
+    proj.check(layer)
+    _need(x, "x", int(T_total), proj.hidden, 2, whole=True)
+    _need(y, "y", int(T_total), proj.hidden, None, whole=True)
+    _check_index(cu_seqlens, "cu_seqlens", int(N) + 1)
+    _check_index(state_slots, "state_slots", int(N))
+    _check_states(layer, int(num_slots) if state_slots is not None else int(N), initial_state,
+                  final_state, conv_state_in, conv_state_out, ("initial_state", "final_state"))
     yd = GDN_DTYPE_BF16 if y is not None and y.dtype == torch.bfloat16 else GDN_DTYPE_FP32
     io = CLayerIO(int(N), int(T_total), _ptr(cu_seqlens), _ptr(x), _ptr(y), yd,
                   _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
@@ -515,6 +611,12 @@ def layer_decode_raw(layer: Layer, proj: Proj, *, B, x, y, state_in, state_out, 
     token per sequence through in_proj, the decode step and out_proj."""
     import torch
     cl, cp = layer.c(), proj.c()
+    proj.check(layer)
+    _need(x, "x", int(B), proj.hidden, 2, whole=True)
+    _need(y, "y", int(B), proj.hidden, None, whole=True)
+    _check_index(state_slots, "state_slots", int(B))
+    _check_states(layer, int(num_slots) if state_slots is not None else int(B), state_in,
+                  state_out, conv_state_in, conv_state_out)
     yd = GDN_DTYPE_BF16 if y is not None and y.dtype == torch.bfloat16 else GDN_DTYPE_FP32
     io = CLayerDecodeIO(int(B), _ptr(x), _ptr(y), yd, _ptr(state_in), _ptr(state_out),
                         _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_slots), int(num_slots))
@@ -542,6 +644,7 @@ def snapshot_save(layer: Layer, state, conv_state, slot: int = 0, num_slots=None
         num_slots = int(state.shape[0])
     buf = np.zeros(snapshot_bytes(layer), dtype=np.uint8)
     cl = layer.c()
+    _check_states(layer, int(num_slots), state, None, conv_state, None)
     _check(lib().gdn_snapshot_save(ctypes.byref(cl), _ptr(state), _ptr(conv_state), int(slot),
                                    int(num_slots), buf.ctypes.data, buf.nbytes, _stream(stream)))
     return buf
@@ -566,6 +669,7 @@ def snapshot_restore(layer: Layer, buf, state, conv_state, slot: int = 0, num_sl
         num_slots = int(state.shape[0])
     arr = np.frombuffer(buf, dtype=np.uint8)
     cl = layer.c()
+    _check_states(layer, int(num_slots), state, None, conv_state, None)
     _check(lib().gdn_snapshot_restore(ctypes.byref(cl), arr.ctypes.data if arr.size else None,
                                       arr.nbytes, _ptr(state), _ptr(conv_state), int(slot),
                                       int(num_slots), _stream(stream)))

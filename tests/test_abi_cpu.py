@@ -150,21 +150,40 @@ def test_decode_unsupported_shape():
 
 
 class _FakeTensor:
-    """Stands in for a device tensor: only data_ptr/stride/numel are read."""
-    def __init__(self, ptr, stride0=0, numel=0, esize=1):
-        self._p, self._s, self._n, self._e = ptr, stride0, numel, esize
+    """Stands in for a device tensor of 2**20 rows, each row `stride0`
+    elements long (2**22 if not given) and stored densely, of `esize`-byte
+    elements: large enough for the binding's own size checks, so that the
+    C ABI's validation is what these tests reach.  Nothing dereferences it."""
+    is_cuda = True
+
+    def __init__(self, ptr, stride0=0, numel=0, esize=4, rows=1 << 20):
+        self._p, self._e = ptr, esize
+        self._row = stride0 if stride0 else 1 << 22
+        self._n = numel if numel else rows * self._row
+        self.shape = (rows, self._row)
 
     def data_ptr(self):
         return self._p
 
+    def dim(self):
+        return 2
+
     def stride(self, i):
-        return self._s
+        return self._row if i == 0 else 1
 
     def numel(self):
         return self._n
 
     def element_size(self):
         return self._e
+
+    def is_contiguous(self):
+        return True
+
+
+def _fake_act(ptr, stride0=0):
+    """A bf16 activation or conv-state stand-in."""
+    return _FakeTensor(ptr, stride0, esize=2)
 
 
 class _FakeStream:
@@ -181,19 +200,19 @@ def test_binding_marshals_to_the_abi_and_raises():
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
                     conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
                     dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
-    t = _FakeTensor(FAKE, 16 * 128)
+    t = _fake_act(FAKE, 16 * 128)
     kw = dict(N=1, T_total=64, cu_seqlens=_FakeTensor(FAKE), q=t, k=t,
-              v=_FakeTensor(FAKE, 32 * 128), z=_FakeTensor(FAKE, 32 * 128),
-              a=_FakeTensor(FAKE, 32), b=_FakeTensor(FAKE, 32), out=_FakeTensor(FAKE),
+              v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE),
               stream=_FakeStream())
     with pytest.raises(gdn.GdnError) as ei:
         gdn.prefill_raw(lay, workspace=None, **kw)
     assert ei.value.status == gdn.GDN_ERR_WORKSPACE
     with pytest.raises(gdn.GdnError) as ei:
-        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16), **kw)
+        gdn.prefill_raw(lay, workspace=_FakeTensor(FAKE, numel=16, esize=1), **kw)
     assert ei.value.status == gdn.GDN_ERR_WORKSPACE              # too small
     nb = gdn.prefill_workspace_bytes(lay, 1, 64)
-    ws = _FakeTensor(FAKE, numel=nb)
+    ws = _FakeTensor(FAKE, numel=nb, esize=1)
     n_ev = len(gdn.prefill_launches(lay, 1, 64, nb)) + 1
     with pytest.raises(gdn.GdnError) as ei:
         gdn.prefill_raw(lay, workspace=ws, events=[_FakeEvent()] * n_ev, **kw)
@@ -203,11 +222,11 @@ def test_binding_marshals_to_the_abi_and_raises():
         gdn.prefill_raw(lay, workspace=ws, events=[_FakeEvent()] * (n_ev - 1), **kw)
     assert b"timing events" in gdn.lib().gdn_last_error()
     with pytest.raises(gdn.GdnError):
-        gdn.decode_raw(lay, B=2, q=t, k=t, v=_FakeTensor(FAKE, 32 * 128),
-                       z=_FakeTensor(FAKE, 32 * 128), a=_FakeTensor(FAKE, 32),
-                       b=_FakeTensor(FAKE, 32), out=_FakeTensor(FAKE + 4),
+        gdn.decode_raw(lay, B=2, q=t, k=t, v=_fake_act(FAKE, 32 * 128),
+                       z=_fake_act(FAKE, 32 * 128), a=_fake_act(FAKE, 32),
+                       b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE + 4),
                        state_in=None, state_out=_FakeTensor(FAKE),
-                       conv_state_in=None, conv_state_out=_FakeTensor(FAKE),
+                       conv_state_in=None, conv_state_out=_fake_act(FAKE),
                        stream=_FakeStream())
     assert gdn.prefill_workspace_bytes(lay, 1, 4096) > 0
 
@@ -255,11 +274,11 @@ def test_decode_multi_rejects_token_counts():
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
                     conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
                     dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
-    t = _FakeTensor(FAKE, 16 * 128)
-    kw = dict(B=2, q=t, k=t, v=_FakeTensor(FAKE, 32 * 128), z=_FakeTensor(FAKE, 32 * 128),
-              a=_FakeTensor(FAKE, 32), b=_FakeTensor(FAKE, 32), out=_FakeTensor(FAKE + 4096),
+    t = _fake_act(FAKE, 16 * 128)
+    kw = dict(B=2, q=t, k=t, v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE + 4096),
               state_in=_FakeTensor(FAKE + (1 << 24)), state_out=_FakeTensor(FAKE + (1 << 24)),
-              conv_state_in=None, conv_state_out=_FakeTensor(FAKE + (1 << 26)),
+              conv_state_in=None, conv_state_out=_fake_act(FAKE + (1 << 26)),
               stream=_FakeStream())
     for bad in (0, gdn.MAX_VERIFY_TOKENS + 1):
         with pytest.raises(gdn.GdnError) as ei:
@@ -269,6 +288,60 @@ def test_decode_multi_rejects_token_counts():
     with pytest.raises(gdn.GdnError) as ei:
         gdn.decode_multi_raw(lay, tokens=4, state_snapshots=_FakeTensor(FAKE + (1 << 24) + 4096), **kw)
     assert b"snapshots" in gdn.lib().gdn_last_error()
+
+
+def _verify_kw(**over):
+    t = _fake_act(FAKE, 16 * 128)
+    kw = dict(B=8, tokens=4, q=t, k=t, v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE),
+              state_in=_FakeTensor(FAKE), state_out=_FakeTensor(FAKE),
+              conv_state_in=_fake_act(FAKE), conv_state_out=_fake_act(FAKE), stream=_FakeStream())
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over, name", [
+    # a pool of 3 states handed to an 8-sequence verify
+    (dict(state_in=_FakeTensor(FAKE, rows=3)), "state_in"),
+    (dict(state_out=_FakeTensor(FAKE, rows=3)), "state_out"),
+    (dict(conv_state_out=_fake_act(FAKE, 8192)), "conv_state_out"),       # rows of 1 tap
+    (dict(out=_FakeTensor(FAKE, rows=31)), "out"),                      # 8 x 4 token rows
+    (dict(q=_fake_act(FAKE, 16 * 64)), "q"),                            # half a row
+    (dict(v=_FakeTensor(FAKE, 32 * 128)), "v"),                         # fp32, layer is bf16
+    (dict(state_snapshots=_FakeTensor(FAKE, 4 * 32 * 128 * 128, rows=7)), "state_snapshots"),
+])
+def test_binding_refuses_short_buffers(over, name):
+    """The binding measures every buffer against the sizes it passes to the
+    library (which trusts them) and refuses a short or mistyped one before
+    anything is launched."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    with pytest.raises(ValueError, match=name):
+        gdn.decode_multi_raw(lay, **_verify_kw(**over))
+
+
+def test_binding_refuses_short_prefill_buffers():
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    t = _fake_act(FAKE, 16 * 128)
+    kw = dict(N=2, T_total=64, cu_seqlens=_FakeTensor(FAKE), q=t, k=t,
+              v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE),
+              stream=_FakeStream())
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        gdn.prefill_raw(lay, **dict(kw, cu_seqlens=_FakeTensor(FAKE, 1, rows=2)))
+    with pytest.raises(ValueError, match="final_state"):
+        gdn.prefill_raw(lay, final_state=_FakeTensor(FAKE, rows=1), **kw)
+    with pytest.raises(ValueError, match="initial_state"):     # a pool of 4 entries, 5 claimed
+        gdn.prefill_raw(lay, initial_state=_FakeTensor(FAKE, rows=4),
+                        state_slots=_FakeTensor(FAKE, 1, rows=2), num_slots=5, **kw)
+    with pytest.raises(ValueError, match="conv_w"):
+        bad = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                        conv_w=_FakeTensor(FAKE, 4, rows=8191), A_log=_FakeTensor(FAKE),
+                        dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+        gdn.prefill_raw(bad, **kw)
 
 
 def test_binding_structs_match_the_header(tmp_path):
@@ -369,8 +442,9 @@ def test_snapshot_restore_rejects_another_layer():
                dict(Hk=2, Hv=4, dk=32, dv=32, act_dtype=gdn.GDN_DTYPE_BF16)):
         lay = gdn.Layer(chunk=16, conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
                         dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE), **kw)
+        conv = _FakeTensor(FAKE, esize=2 if lay.act_dtype == gdn.GDN_DTYPE_BF16 else 4)
         with pytest.raises(gdn.GdnError) as ei:
-            gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), _FakeTensor(FAKE), slot=0,
+            gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), conv, slot=0,
                                  num_slots=1, stream=_FakeStream())
         assert "does not fit this layer" in ei.value.detail
     lay = gdn.Layer(Hk=2, Hv=4, dk=32, dv=32, chunk=16, conv_w=_FakeTensor(FAKE),
