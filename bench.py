@@ -351,7 +351,7 @@ def main():
                 dstep()
             d1.record(stream)
             torch.cuda.synchronize()
-            ms = d0.elapsed_time(d1) / K
+            eager_ms = d0.elapsed_time(d1) / K
             # kernel times from a second pass with events around each launch
             devs = [[new_events(2) for _ in range(L)] for _ in range(K)]
             torch.cuda.synchronize()
@@ -359,11 +359,9 @@ def main():
                 dstep(devs[i])
             torch.cuda.synchronize()
             kms = sum(devs[i][l][0].elapsed_time(devs[i][l][1]) for i in range(K) for l in range(L)) / (K * L)
-            state_gbs = L * B * state_per_seq / (ms * 1e-3) / 1e9
-            all_gbs = L * B * per_seq / (ms * 1e-3) / 1e9
             kern_gbs = B * per_seq / (kms * 1e-3) / 1e9
-            dec[f"B{B}"] = {"ms_per_step": ms, "layers": L, "state_GBps": state_gbs,
-                            "all_bytes_GBps": all_gbs, "state_frac_hbm": state_gbs / PEAK_HBM_GBS,
+            dec[f"B{B}"] = {"layers": L, "eager_ms_per_step": eager_ms,
+                            "eager_state_GBps": L * B * state_per_seq / (eager_ms * 1e-3) / 1e9,
                             "kernel_avg_ms": kms,
                             "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
@@ -388,11 +386,16 @@ def main():
             g1.record(stream)
             torch.cuda.synchronize()
             gms = g0.elapsed_time(g1) / K
-            dec[f"B{B}"]["graph_ms_per_step"] = gms
-            dec[f"B{B}"]["graph_state_GBps"] = L * B * state_per_seq / (gms * 1e-3) / 1e9
+            # the step as a serving loop runs it, replayed from a graph: the
+            # headline decode figures (the eager loop above also pays the
+            # Python binding's per-call cost, which B = 64 no longer hides)
+            state_gbs = L * B * state_per_seq / (gms * 1e-3) / 1e9
+            dec[f"B{B}"].update({"ms_per_step": gms, "state_GBps": state_gbs,
+                                 "all_bytes_GBps": L * B * per_seq / (gms * 1e-3) / 1e9,
+                                 "state_frac_hbm": state_gbs / PEAK_HBM_GBS})
             del g
-            log(f"decode B={B}: {ms:.3f} ms/step ({gms:.3f} from a graph), state {state_gbs:.1f} GB/s, "
-                f"kernel {kms * 1e3:.1f} us = {kern_gbs:.1f} GB/s")
+            log(f"decode B={B}: {gms:.3f} ms/step from a graph ({eager_ms:.3f} eager), state "
+                f"{state_gbs:.1f} GB/s, kernel {kms * 1e3:.1f} us = {kern_gbs:.1f} GB/s")
         result["decode"] = dec
 
         # multi-token verify: VB sequences x VT draft tokens x the same layers

@@ -215,6 +215,11 @@ def _need(t, name, rows, row_elems, esize=None, whole=False):
         raise ValueError(f"{name}: a device tensor is required")
     if t.dim() < 1 or int(t.shape[0]) < rows:
         raise ValueError(f"{name}: {rows} rows needed, shape is {tuple(t.shape)}")
+    if t.is_contiguous() and (esize is None or t.element_size() == esize):
+        # the common case, in a few calls: dense rows packed back to back
+        n0 = int(t.shape[0])
+        if n0 == 0 or t.numel() // n0 >= row_elems:
+            return
     per_row = 1
     for d in t.shape[1:]:
         per_row *= int(d)
@@ -301,10 +306,16 @@ class Layer:
         return 2 * self.Hk * self.dk + self.Hv * self.dv
 
     def c(self) -> CLayer:
-        _need(self.conv_w, "conv_w", self.Cc, self.conv_K, 4, whole=True)
-        _need(self.A_log, "A_log", self.Hv, 1, 4, whole=True)
-        _need(self.dt_bias, "dt_bias", self.Hv, 1, 4, whole=True)
-        _need(self.norm_w, "norm_w", self.dv, 1, 4, whole=True)
+        # the parameters are measured once per set of tensors and shapes
+        key = tuple((t.data_ptr(), t.numel()) if t is not None else None
+                    for t in (self.conv_w, self.A_log, self.dt_bias, self.norm_w)) + \
+            (self.Hk, self.Hv, self.dk, self.dv, self.conv_K)
+        if getattr(self, "_checked", None) != key:
+            _need(self.conv_w, "conv_w", self.Cc, self.conv_K, 4, whole=True)
+            _need(self.A_log, "A_log", self.Hv, 1, 4, whole=True)
+            _need(self.dt_bias, "dt_bias", self.Hv, 1, 4, whole=True)
+            _need(self.norm_w, "norm_w", self.dv, 1, 4, whole=True)
+            self._checked = key
         scale = self.scale if self.scale is not None else self.dk ** -0.5
         return CLayer(self.Hk, self.Hv, self.dk, self.dv, self.conv_K, self.chunk,
                       self.act_dtype, self.out_dtype, scale, self.eps_l2,

@@ -40,6 +40,62 @@ namespace gdn {
 constexpr int kDecodeHalf = 256;                 // threads per value head
 constexpr int kDecodeThreads = 2 * kDecodeHalf;  // two value heads stream at once
 
+// z-gated RMSNorm of one value head's o over dv, shared by the one-token and
+// the multi-token kernels so that both give the same bits: lane t < DV/4 of one wave holds
+// columns 4t..4t+3 of o and of z; the sum of squares is the lane's four
+// terms in a fixed order, then the wave sum.  Stores y to out (bf16 or fp32)
+// and, when core is given, o to core.
+template <int DV>
+__device__ __forceinline__ void gated_rmsnorm_store(int t, const f32x4& o, const float* z,
+                                                    const float* norm_w, float eps, void* out,
+                                                    int out_bf16, float* core, size_t obase) {
+    constexpr int CG = DV / 4;
+    float ps = 0.f;
+    if (t < CG) ps = fmaf(o[3], o[3], fmaf(o[2], o[2], fmaf(o[1], o[1], o[0] * o[0])));
+    ps = wave_sum(ps);
+    if (t >= CG) return;
+    const float r = 1.0f / sqrtf(ps / DV + eps);
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = norm_w[4 * t + e] * (o[e] * r) * silu(z[e]);
+    if (out_bf16) {
+        uint16_t* op = static_cast<uint16_t*>(out) + obase;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase) = f32x4{y[0], y[1], y[2], y[3]};
+    }
+    if (core) *reinterpret_cast<f32x4*>(core + obase) = o;
+}
+
+// conv1d (K = 4) + SiLU of one channel: oldest tap first, the token last
+__device__ __forceinline__ float conv4_silu(const f32x4& w, float t0, float t1, float t2, float x) {
+    float acc = w[0] * t0;
+    acc = fmaf(w[1], t1, acc);
+    acc = fmaf(w[2], t2, acc);
+    acc = fmaf(w[3], x, acc);
+    return silu(acc);
+}
+
+// 1 / sqrt(sum of squares + eps) times num, over DK values in LDS: lane l
+// sums entries l, l + 64, ... in order, then the wave sum (every lane of the
+// wave takes part)
+template <int DK>
+__device__ __forceinline__ float l2_scale(const float* src, int lane, float num, float eps) {
+    float ss = 0.f;
+    for (int i = lane; i < DK; i += kWave) ss = fmaf(src[i], src[i], ss);
+    ss = wave_sum(ss);
+    return num / sqrtf(ss + eps);
+}
+
+// k^ . q^ over DK values in LDS, in the same lane order
+template <int DK>
+__device__ __forceinline__ float dot_wave(const float* a, const float* b, int lane) {
+    float d = 0.f;
+    for (int i = lane; i < DK; i += kWave) d = fmaf(a[i], b[i], d);
+    return wave_sum(d);
+}
+
 template <int DK, int DV, bool BF16>
 __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams p) {
     using A = Act<BF16>;
@@ -128,11 +184,7 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
                 av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
                 bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
             }
-            float acc = w[0] * A::load(&t0);
-            acc = fmaf(w[1], A::load(&t1), acc);
-            acc = fmaf(w[2], A::load(&t2), acc);
-            acc = fmaf(w[3], A::load(&x), acc);
-            const float y = silu(acc);
+            const float y = conv4_silu(w, A::load(&t0), A::load(&t1), A::load(&t2), A::load(&x));
             if (is_qk) {
                 (tid >= DK ? sk : sq)[tid >= DK ? tid - DK : tid] = y;
             } else {
@@ -152,11 +204,8 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
     }
     __syncthreads();
     if (wave < 2) {
-        const float* src = wave == 0 ? sq : sk;
-        float ss = 0.f;
-        for (int i = lane; i < DK; i += kWave) ss = fmaf(src[i], src[i], ss);
-        ss = wave_sum(ss);
-        if (lane == 0) s_r[wave] = (wave == 0 ? p.scale : 1.0f) / sqrtf(ss + p.eps_l2);
+        const float r = l2_scale<DK>(wave == 0 ? sq : sk, lane, wave == 0 ? p.scale : 1.0f, p.eps_l2);
+        if (lane == 0) s_r[wave] = r;
     }
     __syncthreads();
     if (tid < 2 * DK) {
@@ -165,9 +214,7 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
     }
     __syncthreads();
     if (wave == 0) {
-        float d = 0.f;
-        for (int i = lane; i < DK; i += kWave) d = fmaf(sk[i], sq[i], d);
-        d = wave_sum(d);
+        const float d = dot_wave<DK>(sk, sq, lane);
         if (lane == 0) s_kq = d;
     }
 
@@ -186,12 +233,8 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
                 T t0 = cin ? cin[crow + c] : T(0);
                 T t1 = cin ? cin[crow + Cc + c] : T(0);
                 T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
-                const float* w = p.conv_w + static_cast<size_t>(c) * 4;
-                float acc = w[0] * A::load(&t0);
-                acc = fmaf(w[1], A::load(&t1), acc);
-                acc = fmaf(w[2], A::load(&t2), acc);
-                acc = fmaf(w[3], A::load(&x), acc);
-                sv[half][j] = silu(acc);
+                const f32x4 w = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c) * 4);
+                sv[half][j] = conv4_silu(w, A::load(&t0), A::load(&t1), A::load(&t2), A::load(&x));
                 sz[half][j] = A::load(static_cast<const T*>(p.z) + b * p.zs + h * DV + j);
                 cout[crow + c] = t1;
                 cout[crow + Cc + c] = t2;
@@ -245,29 +288,9 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
             }
             // z-gated RMSNorm over dv: row group 0 = lanes 0..CG-1 of the
             // half's first wave.
-            if (t < kWave) {
-                float ps = 0.f;
-                if (t < CG) ps = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-                ps = wave_sum(ps);
-                if (t < CG) {
-                    const float r = 1.0f / sqrtf(ps / DV + p.eps_rms);
-                    const size_t obase = (static_cast<size_t>(b) * p.Hv + h) * DV + 4 * cg;
-                    float y[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y[e] = p.norm_w[4 * cg + e] * (o[e] * r) * silu(sz[half][4 * cg + e]);
-                    if (p.out_bf16) {
-                        uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
-                    } else {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) =
-                            f32x4{y[0], y[1], y[2], y[3]};
-                    }
-                    if (p.core_out)
-                        *reinterpret_cast<f32x4*>(p.core_out + obase) = o;
-                }
-            }
+            if (t < kWave)
+                gated_rmsnorm_store<DV>(t, o, &sz[half][4 * cg], p.norm_w, p.eps_rms, p.out, p.out_bf16,
+                                        p.core_out, (static_cast<size_t>(b) * p.Hv + h) * DV + 4 * cg);
         }
         __syncthreads();   // LDS (sv, sz, red_*) reused by the next pair of heads
     }
@@ -348,11 +371,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
 #pragma unroll
         for (int s = 0; s < TSM; ++s) {
             if (s < Ts) {
-                float acc = w[0] * A::load(&w0);
-                acc = fmaf(w[1], A::load(&w1), acc);
-                acc = fmaf(w[2], A::load(&w2), acc);
-                acc = fmaf(w[3], A::load(&xs[s]), acc);
-                y[s * ystride] = silu(acc);
+                y[s * ystride] = conv4_silu(w, A::load(&w0), A::load(&w1), A::load(&w2), A::load(&xs[s]));
                 w0 = w1;
                 w1 = w2;
                 w2 = xs[s];
@@ -398,11 +417,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
     __syncthreads();
     if (wave < 2) {
         for (int s = 0; s < Ts; ++s) {
-            const float* src = wave == 0 ? sq[s] : sk[s];
-            float ss = 0.f;
-            for (int i = lane; i < DK; i += kWave) ss = fmaf(src[i], src[i], ss);
-            ss = wave_sum(ss);
-            if (lane == 0) s_r[wave][s] = (wave == 0 ? p.scale : 1.0f) / sqrtf(ss + p.eps_l2);
+            const float r = l2_scale<DK>(wave == 0 ? sq[s] : sk[s], lane, wave == 0 ? p.scale : 1.0f,
+                                         p.eps_l2);
+            if (lane == 0) s_r[wave][s] = r;
         }
     }
     __syncthreads();
@@ -415,9 +432,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
     __syncthreads();
     if (wave == 0) {
         for (int s = 0; s < Ts; ++s) {
-            float d = 0.f;
-            for (int i = lane; i < DK; i += kWave) d = fmaf(sk[s][i], sq[s][i], d);
-            d = wave_sum(d);
+            const float d = dot_wave<DK>(sk[s], sq[s], lane);
             if (lane == 0) s_kq[s] = d;
         }
     }
@@ -482,29 +497,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
                 }
                 // z-gated RMSNorm over dv: row group 0 = lanes 0..CG-1 of the
                 // half's first wave.
-                if (t < kWave) {
-                    float ps = 0.f;
-                    if (t < CG) ps = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-                    ps = wave_sum(ps);
-                    if (t < CG) {
-                        const float r = 1.0f / sqrtf(ps / DV + p.eps_rms);
-                        const size_t obase = (static_cast<size_t>(row0 + s) * p.Hv + h) * DV + 4 * cg;
-                        float y[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            y[e] = p.norm_w[4 * cg + e] * (o[e] * r) * silu(sz[half][s][4 * cg + e]);
-                        if (p.out_bf16) {
-                            uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(y[e]);
-                        } else {
-                            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) =
-                                f32x4{y[0], y[1], y[2], y[3]};
-                        }
-                        if (p.core_out)
-                            *reinterpret_cast<f32x4*>(p.core_out + obase) = o;
-                    }
-                }
+                if (t < kWave)
+                    gated_rmsnorm_store<DV>(t, o, &sz[half][s][4 * cg], p.norm_w, p.eps_rms, p.out,
+                                            p.out_bf16, p.core_out,
+                                            (static_cast<size_t>(row0 + s) * p.Hv + h) * DV + 4 * cg);
             }
             __syncthreads();   // red_* reused by the next token, sv/sz by the next pair
         }

@@ -195,6 +195,31 @@ def test_decode_batch_invariance():
             assert _bits_equal(r["conv_state_out"][j], full["conv_state_out"][b])
 
 
+def test_decode_small_batch_core_and_bf16_out():
+    """Small batches split each head's columns over several work-groups and
+    finish the norm in a second kernel, carrying o through core_out (bf16
+    out) or out (fp32 out): the same bits as the one-kernel path at B = 64,
+    for out, core_out and both states."""
+    sh = synth.FULL
+    params = synth.layer_params(sh, 65)
+    ad = act_dtype(sh)
+    B = 64
+    t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, B, 66).items()}
+    st = to_dev(synth.initial_states(sh, B, 67))
+    cs = to_dev(synth.conv_states(sh, B, 68), ad)
+    for out_dtype in (gdn.GDN_DTYPE_BF16, gdn.GDN_DTYPE_FP32):
+        layer = make_layer(sh, params, out_dtype=out_dtype)
+        full = _decode(layer, t, st, cs, want_core=True)
+        for sel in ([7], [1, 2], [60, 3, 33, 12]):
+            idx = torch.tensor(sel, device="cuda")
+            sub = {k: v[idx] for k, v in t.items()}
+            r = _decode(layer, sub, st[idx], cs[idx], want_core=True)
+            torch.cuda.synchronize()
+            for j, b in enumerate(sel):
+                for key in ("out", "core_out", "final_state", "conv_state_out"):
+                    assert _bits_equal(r[key][j], full[key][b]), (out_dtype, sel, key)
+
+
 def test_decode_chain_matches_prefill_and_oracle():
     """T single-token decode steps from carried states equal one prefill of
     the same T tokens within the bar (they reassociate differently, so only
