@@ -269,6 +269,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 
     if (!out_role) {
         // ---------------- state waves ----------------
+        // they are the chain: raised issue priority lets their dependent
+        // instructions win the SIMD over the output wave sharing it
+        __builtin_amdgcn_s_setprio(3);
         // Three operand sets in registers, rotated: chunk c+2's fragments
         // load while chunk c computes (W's per k step between the products,
         // K_d^T's after the state update), two chunk steps ahead of use.
