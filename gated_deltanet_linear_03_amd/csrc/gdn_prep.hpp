@@ -527,6 +527,38 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     }
     __syncthreads();
 
+    // ---- the P and K_d^T fragments go out first: they read only LDS the
+    //      substitution leaves alone (P, K^ and the decays), so their stores
+    //      drain while it computes ----
+    constexpr int NPS = C * CK / 8;                                // P slots per head
+    for (int sl = tid; sl < GH * NPS; sl += NT) {                  // P [C][CK]
+        const int g = sl / NPS, tile = (sl % NPS) / 64, ln = sl % 64;
+        const int mt = tile / (CK / 32), kt = tile % (CK / 32);
+        const int r = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
+        if (kt * 32 > mt * 16 + 15) continue;       // a zero tile: never read
+        // eight columns of one 16-column tile: tiles above the diagonal and
+        // columns past C are zero
+        const bool nz = s0 / 16 <= r / 16 && s0 < C;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(blk(g) + L::P + tile * 1024 + ln * 16) = nz ? lds16(sP(g) + r * SP + s0) : zero;
+        *reinterpret_cast<u32x4*>(blk(g) + L::Pl + tile * 1024 + ln * 16) = nz ? lds16(sPl(g) + r * SP + s0) : zero;
+    }
+    for (int sl = tid; sl < DK * CK / 8; sl += NT) {              // K_d^T [DK][CK]
+        const int tile = sl / 64, ln = sl % 64;
+        const int mt = tile / (CK / 32), kt = tile % (CK / 32);
+        const int i = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
+        float kv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[e] = s0 + e < C ? hl(sKh, sKl, (s0 + e) * SQ + i) : 0.f;
+#pragma unroll
+        for (int g = 0; g < GH; ++g) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = s0 + e < C ? sD(g)[s0 + e] * kv[e] : 0.f;
+            *reinterpret_cast<u32x4*>(blk(g) + L::KdT + tile * 1024 + ln * 16) = pack8_f16(x);
+        }
+    }
+
     // ---- 3. [W | U~] = Tm [diag(beta e^gamma) K^ | diag(beta) V^] by block
     //         forward substitution over the 16-token blocks,
     //             X_i = T_ii (B_i - sum_{j<i} A_ij X_j),
@@ -534,8 +566,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     //         layout is their B-operand layout, so X_j stays in registers and
     //         the waves never wait for each other.  A wave's W and U~ tiles
     //         are two independent chains on the same A and T fragments.  U~
-    //         goes out directly, -W is staged (fp16) over Q^ (dead).
-    //         Then the P and K_d^T fragments. ----
+    //         goes out directly, -W is staged (fp16) over Q^ (dead). ----
     if (sub) {
         const float* be = sbeta(g3);
         const float* ee = sE(g3);
@@ -596,34 +627,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 const int tile = i * NTU + j3;
                 *reinterpret_cast<f32x4*>(b + L::Ut + tile * 1024 + lane * 16) = XU[i];
             }
-        }
-    }
-    constexpr int NPS = C * CK / 8;                                // P slots per head
-    for (int sl = tid; sl < GH * NPS; sl += NT) {                  // P [C][CK]
-        const int g = sl / NPS, tile = (sl % NPS) / 64, ln = sl % 64;
-        const int mt = tile / (CK / 32), kt = tile % (CK / 32);
-        const int r = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
-        if (kt * 32 > mt * 16 + 15) continue;       // a zero tile: never read
-        // eight columns of one 16-column tile: tiles above the diagonal and
-        // columns past C are zero
-        const bool nz = s0 / 16 <= r / 16 && s0 < C;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(blk(g) + L::P + tile * 1024 + ln * 16) = nz ? lds16(sP(g) + r * SP + s0) : zero;
-        *reinterpret_cast<u32x4*>(blk(g) + L::Pl + tile * 1024 + ln * 16) = nz ? lds16(sPl(g) + r * SP + s0) : zero;
-    }
-    for (int sl = tid; sl < DK * CK / 8; sl += NT) {              // K_d^T [DK][CK]
-        const int tile = sl / 64, ln = sl % 64;
-        const int mt = tile / (CK / 32), kt = tile % (CK / 32);
-        const int i = mt * 16 + ln % 16, s0 = kt * 32 + 8 * (ln / 16);
-        float kv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kv[e] = s0 + e < C ? hl(sKh, sKl, (s0 + e) * SQ + i) : 0.f;
-#pragma unroll
-        for (int g = 0; g < GH; ++g) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = s0 + e < C ? sD(g)[s0 + e] * kv[e] : 0.f;
-            *reinterpret_cast<u32x4*>(blk(g) + L::KdT + tile * 1024 + ln * 16) = pack8_f16(x);
         }
     }
     __syncthreads();
