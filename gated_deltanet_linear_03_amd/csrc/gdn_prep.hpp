@@ -609,6 +609,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 split4(au, yh, yl);
                 XU[i] = mfma3_k16(t_h, t_l, yh, yl, f32x4{0.f, 0.f, 0.f, 0.f});
                 if (i + 1 < NB) split4(XU[i], uh[i], ul[i]);
+                // block i of U~ is final: out now, while the later blocks compute
+                *reinterpret_cast<f32x4*>(blk(g3) + L::Ut + (i * NTU + j3) * 1024 + lane * 16) = XU[i];
             }
         }
         if (has_w) {
@@ -618,14 +620,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sw[(16 * i + 4 * lq + r) * SQ + ch] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-XW[i][r]));
-            }
-        }
-        if (has_u) {
-            uint8_t* b = blk(g3);
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int tile = i * NTU + j3;
-                *reinterpret_cast<f32x4*>(b + L::Ut + tile * 1024 + lane * 16) = XU[i];
             }
         }
     }
