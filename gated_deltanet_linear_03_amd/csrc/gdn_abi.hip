@@ -80,7 +80,8 @@ WsLayout ws_layout(const gdn_layer* L, int32_t N, int64_t T, bool need_core, int
     // sum_n ceil(L_n / C) <= (T + N (C - 1)) / C for every split of T into N lengths
     w.max_chunks = L->chunk > 0 ? (T + static_cast<int64_t>(N) * (L->chunk - 1)) / L->chunk : N;
     w.win_slots = win_slots > 0 ? win_slots
-                                : gdn::prefill_window_slots(L->dk, L->dv, L->chunk, L->Hv, N, w.max_chunks);
+                                : gdn::prefill_window_slots(L->dk, L->dv, L->chunk, L->Hk, L->Hv, N,
+                                                            w.max_chunks, gdn::compute_units());
     w.slot_bytes = static_cast<int64_t>(L->Hv) * gdn::vch_bytes(L->dk, L->dv, L->chunk);
     int64_t o = 0;
     w.off_chunk = o;

@@ -84,16 +84,28 @@ __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
 constexpr int64_t kPrefillWindowBytes = 144ll << 20;
 constexpr int64_t kPrefillBatchWindowBytes = 4ll << 30;
 
-// Chunk slots per window for a layer: as many as the target size allows,
-// then evened out over the windows that takes.
-inline int64_t prefill_window_slots(int DK, int DV, int C, int Hv, int N, int64_t max_chunks) {
+// Chunk slots per window for a layer: as many as the target size allows.
+// When that takes several windows and holds at least one round of prep
+// work-groups over the compute units (one per value-head pair, or per value
+// head when a key head has an odd number of them, per chunk slot), the
+// window is cut to whole rounds: a window of 2.5 rounds costs as much prep
+// time as one of 3.  Otherwise the slots are evened out over the windows.
+inline int64_t prefill_window_slots(int DK, int DV, int C, int Hk, int Hv, int N, int64_t max_chunks,
+                                    int compute_units) {
     const int64_t slot = static_cast<int64_t>(Hv) * vch_bytes(DK, DV, C);
     int64_t w = (N > 1 ? kPrefillBatchWindowBytes : kPrefillWindowBytes) / slot;
     const int64_t cap = max_chunks > 1 ? max_chunks : 1;
     w = w < 1 ? 1 : (w > cap ? cap : w);
+    const int G = Hk > 0 ? Hv / Hk : 1;
+    const int64_t per_slot = G % 2 == 0 ? Hv / 2 : Hv;             // prep work-groups per slot
+    const int64_t round = compute_units / (per_slot > 0 ? per_slot : 1);
+    if (w < cap && round >= 1 && w >= round) return w / round * round;
     const int64_t nwin = (cap + w - 1) / w;
     return (cap + nwin - 1) / nwin;
 }
+
+// Compute units of the current device (256 where there is none).
+int compute_units();
 
 // Kernel launches of one prefill: (prep, scan) per window, epi.
 inline int64_t prefill_launches(int64_t max_chunks, int64_t win_slots) {

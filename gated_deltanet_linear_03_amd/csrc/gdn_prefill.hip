@@ -625,10 +625,13 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
 
 // ---------------------------------------------------------------------------
 // Compute units of the current device (cached per device).
-static int compute_units() {
+int compute_units() {
     static int cached[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();          // no device here: plan for 256
+        return 256;
+    }
     if (cached[dev] == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)

@@ -234,8 +234,9 @@ def test_binding_marshals_to_the_abi_and_raises():
 def test_prefill_windows_follow_the_workspace():
     """The prefill runs window by window over the chunk slots: the default
     workspace gives windows of up to ~144 MiB of operand blocks at the 35B-A3B
-    shape (evened out over the windows), a smaller one more windows, down to
-    one chunk slot; below that the call is refused."""
+    shape, cut to whole rounds of prep work-groups when several windows are
+    needed, a smaller workspace more windows, down to one chunk slot; below
+    that the call is refused."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
                     conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
                     dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
@@ -243,7 +244,12 @@ def test_prefill_windows_follow_the_workspace():
     slot = 32 * (2 * 64 * 128 + 4 * 64 * 128 + 2 * 128 * 64 + 4 * 64 * 64 + 4 * 64 * 128)
 
     def window(n_chunks):
+        # whole rounds of the 16 value-head pairs' prep work-groups over 256
+        # compute units (16 slots) when several windows are needed, else
+        # evened out
         w = min((144 << 20) // slot, n_chunks)
+        if w < n_chunks and w >= 16:
+            return w // 16 * 16
         return -(-n_chunks // -(-n_chunks // w))
 
     T = 4096
@@ -255,6 +261,9 @@ def test_prefill_windows_follow_the_workspace():
     win = window(n_chunks)                        # chunk slots per window
     assert win == 32 and len(names) == 1 + 2 * 2
     # beyond the pre-norm output and the decay table, only the window grows
+    # (131072 tokens: 64 windows of 32 slots, two rounds each)
+    assert window(131072 // 64) == 32
+    assert len(gdn.prefill_launches(lay, 1, 131072)) == 1 + 2 * 64
     nb_long = gdn.prefill_workspace_bytes(lay, 1, 131072)
     assert nb_long - nb == ((131072 - T) * 32 * 128 * 4 + 4 * (131072 - T) // 64 * 32
                             + (window(131072 // 64) - win) * slot)
