@@ -22,8 +22,8 @@
  *          o_t = S_t q_t,           S in R^{dv x dk};
  *   5. the output gate y = w (.) o / sqrt(mean(o^2) + eps2) (.) SiLU(z).
  *
- * The layer is the recurrent block of the hybrid Qwen3.x models served on the
- * pages this build follows (llmxabe README, "Status" and the model section:
+ * The layer is the recurrent block of the hybrid Qwen3.x models that the
+ * engines on the pages serve (llmxabe README, "Status" and the model section:
  * three of every four layers are Gated DeltaNet with a fixed-size state per
  * sequence; skindeep.ai "Our own inference runtime", "What it is": 36 of 48
  * layers are gated delta net).  The pages give no formula; the recurrence is
