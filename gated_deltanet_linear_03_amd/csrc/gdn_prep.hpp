@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     //         layout is their B-operand layout, so X_j stays in registers and
     //         the waves never wait for each other.  A wave's W and U~ tiles
     //         are two independent chains on the same A and T fragments.  U~
-    //         goes out directly, -W is staged (fp16) over Q^ (dead). ----
+    //         goes out block by block, -W once the wave's chain is done. ----
     if (sub) {
         const float* be = sbeta(g3);
         const float* ee = sE(g3);
@@ -614,6 +614,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             }
         }
         if (has_w) {
+            // ---- 4. -W out as A fragments, by each wave for its own 16
+            //      columns: they go through LDS (fp16, over Q^, dead) to
+            //      change lanes, and the wave stores its half of each 16 x 32
+            //      fragment tile (lanes 16 h' .. 16 h' + 15 with h' = 2 (j3 % 2)
+            //      + h) as soon as its substitution is done, with no wait on
+            //      the other waves ----
             uint16_t* sw = sW(g3);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
@@ -621,17 +627,18 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
                 for (int r = 0; r < 4; ++r)
                     sw[(16 * i + 4 * lq + r) * SQ + ch] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-XW[i][r]));
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint8_t* b = blk(g3) + L::negW;
+            for (int idx = lane; idx < NB * 32; idx += kWave) {
+                const int mt = idx / 32, h = (idx / 16) % 2, row = idx % 16;
+                const int slot = (2 * (j3 % 2) + h) * 16 + row;          // lane slot in the tile
+                const int tile = mt * (DK / 32) + j3 / 2;
+                *reinterpret_cast<u32x4*>(b + tile * 1024 + slot * 16) =
+                    lds16(sw + (16 * mt + row) * SQ + 16 * j3 + 8 * h);
+            }
         }
-    }
-    __syncthreads();
-
-    // ---- 4. -W out as A fragments ----
-    constexpr int NWS = C * DK / 8;
-    for (int sl = tid; sl < GH * NWS; sl += NT) {
-        const int g = sl / NWS, tile = (sl % NWS) / 64, ln = sl % 64;
-        const int mt = tile / (DK / 32), kt = tile % (DK / 32);
-        const int r = mt * 16 + ln % 16, c0 = kt * 32 + 8 * (ln / 16);
-        *reinterpret_cast<u32x4*>(blk(g) + L::negW + tile * 1024 + ln * 16) = lds16(sW(g) + r * SQ + c0);
     }
 }
 
