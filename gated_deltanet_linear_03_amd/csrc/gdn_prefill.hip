@@ -159,8 +159,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     // the matrix-core copies of H^T and U^T as fp16 hi and lo parts (the
     // state itself stays in fp32 accumulators); the state chain uses the hi
     // parts, the output products both
-    __shared__ __align__(16) uint16_t HT[DVS * HS];
-    __shared__ __align__(16) uint16_t HTl[DVS * HS];
+    // H^T double-buffered by chunk parity: the state waves write chunk c+1's
+    // copy while the output waves still read chunk c's
+    __shared__ __align__(16) uint16_t HTb[2 * DVS * HS];
+    __shared__ __align__(16) uint16_t HTlb[2 * DVS * HS];
+    auto HT = [&](int c) { return HTb + (c & 1) * (DVS * HS); };
+    auto HTl = [&](int c) { return HTlb + (c & 1) * (DVS * HS); };
     __shared__ __align__(16) uint16_t UT[DVS * US];
     __shared__ __align__(16) uint16_t UTl[DVS * US];
 
@@ -211,7 +215,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     // H slice in accumulator fragments of the state waves: tile
     // (mth = wave + NW*qh, nt)
     f32x4 hacc[QH][NTL];
-    auto store_H_lds = [&]() {
+    auto store_H_lds = [&](int c) {      // H entering chunk c
+        uint16_t* ht = HT(c);
+        uint16_t* htl = HTl(c);
 #pragma unroll
         for (int qh = 0; qh < QH; ++qh) {
             const int mth = wave + NW * qh;
@@ -221,8 +227,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 const int off = (nt * 16 + l16) * HS + mth * 16 + lq * 4;
                 uint2 hi, lo;
                 split4_f16(hacc[qh][nt], hi, lo);
-                *reinterpret_cast<uint2*>(&HT[off]) = hi;
-                *reinterpret_cast<uint2*>(&HTl[off]) = lo;
+                *reinterpret_cast<uint2*>(&ht[off]) = hi;
+                *reinterpret_cast<uint2*>(&htl[off]) = lo;
             }
         }
     };
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 hacc[qh][nt] = v;
             }
         }
-        store_H_lds();
+        store_H_lds(c_begin);
     }
     __syncthreads();
 
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 load_w(nxt, cn, kt);
                 if (!has_row) continue;
                 u32x4 b[NTL];
-                read_H(HT, kt, b);
+                read_H(HT(c), kt, b);
                 f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h(cur.w[kt], b[nt], a[nt]);
@@ -359,8 +365,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                     for (int nt = 0; nt < NTL; ++nt) hacc[qh][nt] = mfma_h(cur.k[qh][kt], ub[kt][nt], hacc[qh][nt]);
                 }
             }
-            // (4) H' into LDS for the next chunk (every wave read H in (1))
-            store_H_lds();
+            // (4) H' into LDS for the next chunk, in the other buffer (the
+            // output waves read this chunk's until the step's last barrier)
+            store_H_lds(c + 1);
             load_k(nxt, cn);
             __syncthreads();
         };
@@ -444,18 +451,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 a0[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 a1[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int kt = 0; kt < KTH; ++kt) {
+            // the last k step of Q_G H waits for the step's second half, so
+            // that each half carries about the same matrix-core work
+            auto qh_step = [&](int kt) {
                 load_q(nxt, cn, kt);
-                if (!has_row) continue;
+                if (!has_row) return;
                 u32x4 b[NTL], bl[NTL];
-                read_H(HT, kt, b);
-                read_H(HTl, kt, bl);
+                read_H(HT(c), kt, b);
+                read_H(HTl(c), kt, bl);
                 f32x4* a = (kt & 1) ? a1 : a0;
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) a[nt] = mfma_h3(cur.q[kt], cur.ql[kt], b[nt], bl[nt], a[nt]);
-            }
+            };
+#pragma unroll
+            for (int kt = 0; kt < KTH - 1; ++kt) qh_step(kt);
             __syncthreads();
+            qh_step(KTH - 1);
             if (has_row) {
                 // (2) O += P U, store the valid rows
                 u32x4 ub[KTC][NTL], ubl[KTC][NTL];
