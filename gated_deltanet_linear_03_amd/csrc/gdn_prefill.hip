@@ -130,11 +130,14 @@ namespace gdn {
 //                      H' = e^{gamma_last} H + K_d^T U for the H row tiles
 //                      wave, wave + 4, ...  (registers, fp32)
 //   output waves 4..7  O = Q_G H + P U for chunk-row tile `wave - 4`
-// Per chunk:  [state: U -> LDS | output: Q_G H]  barrier
-//             [state: H' -> LDS | output: + P U, store O]  barrier.
+// Per chunk:  [state: U -> LDS | output: Q_G H, all but its last k step]  barrier
+//             [state: H' -> the other H^T buffer | output: last k step of
+//              Q_G H, + P U, store O]  barrier.
 // Only the state waves are on the chunk-to-chunk chain; the output products,
 // their stores and their operand loads run beside it on the other wave of
-// each SIMD.
+// each SIMD.  H^T is double-buffered by chunk parity, so the output waves
+// can read chunk c's copy in both halves of the step while the state waves
+// write chunk c+1's.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
 
