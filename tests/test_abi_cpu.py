@@ -156,8 +156,8 @@ class _FakeTensor:
     C ABI's validation is what these tests reach.  Nothing dereferences it."""
     is_cuda = True
 
-    def __init__(self, ptr, stride0=0, numel=0, esize=4, rows=1 << 20):
-        self._p, self._e = ptr, esize
+    def __init__(self, ptr, stride0=0, numel=0, esize=4, rows=1 << 20, pad=0):
+        self._p, self._e, self._pad = ptr, esize, pad
         self._row = stride0 if stride0 else 1 << 22
         self._n = numel if numel else rows * self._row
         self.shape = (rows, self._row)
@@ -169,7 +169,7 @@ class _FakeTensor:
         return 2
 
     def stride(self, i):
-        return self._row if i == 0 else 1
+        return self._row + self._pad if i == 0 else 1
 
     def numel(self):
         return self._n
@@ -178,7 +178,7 @@ class _FakeTensor:
         return self._e
 
     def is_contiguous(self):
-        return True
+        return self._pad == 0
 
 
 def _fake_act(ptr, stride0=0):
@@ -328,6 +328,24 @@ def test_binding_refuses_short_buffers(over, name):
                     dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
     with pytest.raises(ValueError, match=name):
         gdn.decode_multi_raw(lay, **_verify_kw(**over))
+
+
+def test_binding_refuses_padded_state_rows():
+    """States and outputs are read as packed rows: a view with padding
+    between its rows is refused, token inputs may have it (their token
+    stride is passed on)."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
+                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    padded_state = _FakeTensor(FAKE, 32 * 128 * 128, rows=8, pad=64)
+    with pytest.raises(ValueError, match="state_out: rows must be packed"):
+        gdn.decode_multi_raw(lay, **_verify_kw(state_out=padded_state))
+    with pytest.raises(ValueError, match="out: rows must be packed"):
+        gdn.decode_multi_raw(lay, **_verify_kw(out=_FakeTensor(FAKE, 32 * 128, rows=32, pad=8)))
+    # a token stride longer than the row is fine for the token inputs (the
+    # binding's own check, called alone: nothing reaches the library)
+    gdn._check_tokens(lay, 32, _FakeTensor(FAKE, 16 * 128, esize=2, pad=64), None, None, None,
+                      None, None, None, None)
 
 
 def test_binding_refuses_short_prefill_buffers():
