@@ -35,6 +35,21 @@ bool bad_alias(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// [lo, hi) byte ranges share any byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// An output buffer (out, core_out) that shares bytes with a recurrent or
+// conv state would be overwritten, or overwrite it, while the kernels run.
+bool output_hits_state(const void* o, size_t no, const void* s_in, const void* s_out, size_t ns,
+                       const void* c_in, const void* c_out, size_t nc) {
+    return overlaps(o, no, s_in, ns) || overlaps(o, no, s_out, ns) || overlaps(o, no, c_in, nc) ||
+           overlaps(o, no, c_out, nc);
+}
+
 gdn_status check_layer(const gdn_layer* L, bool prefill) {
     if (!L) return fail(GDN_ERR_INVALID_ARGUMENT, "layer is NULL");
     if (L->Hk <= 0 || L->Hv <= 0 || L->dk <= 0 || L->dv <= 0)
@@ -206,6 +221,11 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
         return fail(GDN_ERR_INVALID_ARGUMENT, "out overlaps core_out");
     if (io->core_out && static_cast<const void*>(io->out) == static_cast<const void*>(io->core_out) && T > 0)
         return fail(GDN_ERR_INVALID_ARGUMENT, "out and core_out must be different buffers");
+    if (output_hits_state(io->out, out_bytes, io->initial_state, io->final_state, state_bytes,
+                          io->conv_state_in, io->conv_state_out, conv_bytes) ||
+        output_hits_state(io->core_out, size_t(T) * Hv * dv * 4, io->initial_state, io->final_state,
+                          state_bytes, io->conv_state_in, io->conv_state_out, conv_bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "out or core_out overlaps a state");
 
     WsLayout w;
     st = fit_workspace(L, N, T, io->core_out == nullptr, ws, ws_bytes, &w);
@@ -277,11 +297,6 @@ gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void*
     return prefill_impl(L, io, ws, ws_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
-static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    if (!a || !b || na == 0 || nb == 0) return false;
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + nb && y < x + na;
-}
 
 // Ts = 0: one token per sequence (gdn_decode); Ts >= 1: the multi-token kernel.
 static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32_t Ts, float* snap,
@@ -323,6 +338,15 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
         return fail(GDN_ERR_INVALID_ARGUMENT, "conv_state_out partially overlaps conv_state_in");
     if (static_cast<int64_t>(B) * Hk >= (int64_t(1) << 31) || static_cast<int64_t>(B) * Ts >= (int64_t(1) << 31))
         return fail(GDN_ERR_INVALID_ARGUMENT, "B * Hk or B * tokens too large");
+    {
+        const size_t rows = size_t(B) * (Ts > 0 ? Ts : 1);
+        const size_t ob = rows * Hv * dv * (L->out_dtype == GDN_DTYPE_BF16 ? 2 : 4);
+        if (output_hits_state(io->out, ob, io->state_in, io->state_out, state_bytes, io->conv_state_in,
+                              io->conv_state_out, conv_bytes) ||
+            output_hits_state(io->core_out, rows * Hv * dv * 4, io->state_in, io->state_out, state_bytes,
+                              io->conv_state_in, io->conv_state_out, conv_bytes))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "out or core_out overlaps a state");
+    }
     if (snap) {
         const size_t snap_bytes = size_t(B) * Ts * Hv * dk * dv * 4;
         if (!aligned(snap, 16)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_snapshots must be 16-byte aligned");

@@ -140,6 +140,23 @@ def test_decode_rejects(kw, status):
     assert gdn.lib().gdn_last_error()
 
 
+def test_outputs_may_not_overlap_a_state():
+    """out or core_out sharing bytes with a recurrent or conv state is refused
+    on the host (the kernels would write one over the other)."""
+    far = FAKE + (1 << 34)
+    base = dict(out=far, state_in=FAKE, state_out=FAKE, conv_state_in=FAKE + (1 << 30),
+                conv_state_out=FAKE + (1 << 30))
+    for over in (dict(out=FAKE + 4096), dict(out=FAKE + (1 << 30) + 256),
+                 dict(core_out=FAKE + (1 << 20))):
+        kw = dict(base, **over)
+        st = gdn.lib().gdn_decode(ctypes.byref(_full_layer()), ctypes.byref(_dio(**kw)), None)
+        assert st == gdn.GDN_ERR_INVALID_ARGUMENT
+        assert b"overlaps a state" in gdn.lib().gdn_last_error()
+    io = _pio(out=FAKE + 4096, final_state=FAKE, N=1, T_total=64)
+    assert _prefill(_full_layer(), io) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert b"overlaps a state" in gdn.lib().gdn_last_error()
+
+
 def test_decode_zero_batch_is_a_no_op():
     assert gdn.lib().gdn_decode(ctypes.byref(_full_layer()), ctypes.byref(_dio(B=0)), None) == 0
 
