@@ -633,7 +633,9 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
         v.y = f32_to_bf16_bits(y[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(y[3])) << 16);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * DV + 4 * lr) = v;
     } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row * DV + 4 * lr) = f32x4{y[0], y[1], y[2], y[3]};
+        // out is not read again here: streamed past the caches
+        __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]},
+                                    reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row * DV + 4 * lr));
     }
 }
 
