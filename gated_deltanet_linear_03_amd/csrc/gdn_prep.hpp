@@ -78,12 +78,14 @@ __device__ __forceinline__ void load_rows(const PrefillParams& p, int slot, int6
     const T* row = static_cast<const T*>(src) + (t0 + r0 - 3) * rs + col;   // row j at row + j rs
     const int hist = static_cast<int>(min(t0 - start, static_cast<int64_t>(3)));  // sequence rows before the chunk, up to 3
     if (r0 - 3 + hist >= 0 && r0 + 3 < valid) {
-        // the common case: all seven rows inside the chunk's sequence rows
+        // the common case: all seven rows inside the chunk's sequence rows,
+        // read non-temporally (used once: they should not push the window's
+        // operand blocks or the pre-norm output out of the caches)
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
             const u32x4* q = reinterpret_cast<const u32x4*>(row + j * rs);
 #pragma unroll
-            for (int w = 0; w < W; ++w) raw.r[j][w] = q[w];
+            for (int w = 0; w < W; ++w) raw.r[j][w] = __builtin_nontemporal_load(q + w);
         }
         return;
     }
