@@ -152,6 +152,9 @@ def test_single_token_closed_form():
     x = _inputs(d, 1, 11)
     p = _params(d, 11)
     r = _run(d, [0, 1], x, p)
+    d0 = _dims(Hk=1, Hv=2, dk=16, dv=8, scale=0.3)
+    d0.eps_rms = 0.0
+    r0 = _run(d0, [0, 1], x, p)
     conv_last = p["conv_w"][:, -1]
     def act(raw, ch0):
         y = raw * conv_last[ch0:ch0 + raw.size]
@@ -166,6 +169,15 @@ def test_single_token_closed_form():
         o = beta * float(kh @ qh) * vh
         assert np.allclose(r["core_out"][0, h], o, atol=1e-14)
         assert np.allclose(r["final_state"][0, h], beta * np.outer(kh, vh), atol=1e-14)
+        # the gated output: norm_w (.) o / sqrt(mean(o^2) + eps) (.) SiLU(z),
+        # with the layer's non-uniform norm_w applied entry by entry
+        zz = x["z"][0, h]
+        y = p["norm_w"] * o / math.sqrt(float(np.mean(o * o)) + d.eps_rms) * zz / (1 + np.exp(-zz))
+        assert np.allclose(r["out"][0, h], y, rtol=1e-13, atol=1e-15)
+        # with eps_rms = 0 it is sign(beta k^.q^) w (.) v^/rms(v^) (.) SiLU(z)
+        s = math.copysign(1.0, beta * float(kh @ qh))
+        y0 = s * p["norm_w"] * vh / math.sqrt(float(np.mean(vh * vh))) * zz / (1 + np.exp(-zz))
+        assert np.allclose(r0["out"][0, h], y0, rtol=1e-12, atol=0)
 
 
 @pytest.mark.parametrize("T1", [0, 1, 2, 5, 13])

@@ -108,6 +108,32 @@ def test_rmsnorm_gate_closed_forms():
     assert np.all(oracle.rmsnorm_gate(o, np.zeros(64), w2, eps) == 0.0)
 
 
+def test_rmsnorm_gate_weight_is_elementwise():
+    """The norm weight scales each output element by its own entry: the
+    output is linear in w element by element, y(w) = w (.) y(1), so dropping
+    w, broadcasting one entry, or shifting its index all fail here."""
+    n = 48
+    o = _rng(4).standard_normal(n)
+    z = _rng(5).standard_normal(n)
+    eps = 1e-6
+    y1 = oracle.rmsnorm_gate(o, z, np.ones(n), eps)
+    # a non-uniform weight, every entry distinct and of both signs
+    w = np.linspace(-1.5, 2.5, n)
+    yw = oracle.rmsnorm_gate(o, z, w, eps)
+    assert np.allclose(yw, w * y1, rtol=1e-15, atol=0)
+    # a one-hot weight keeps exactly one element, the others are exactly 0
+    for j in (0, 17, n - 1):
+        e = np.zeros(n)
+        e[j] = 3.0
+        ye = oracle.rmsnorm_gate(o, z, e, eps)
+        assert np.all(ye[np.arange(n) != j] == 0.0)
+        assert ye[j] == pytest.approx(3.0 * y1[j], rel=1e-15)
+    # the closed form for w = 1, elementwise: o / rms(o) * SiLU(z)
+    rms = math.sqrt(float(np.mean(o * o)) + eps)
+    silu_z = z / (1.0 + np.exp(-z))
+    assert np.allclose(y1, o / rms * silu_z, rtol=1e-14, atol=0)
+
+
 # ---- the recurrence -------------------------------------------------------
 
 def test_beta0_g0_leaves_state_unchanged():
