@@ -206,9 +206,12 @@ def _ptr(t) -> int | None:
 def _need(t, name, rows, row_elems, esize=None, whole=False):
     """Raise ValueError unless t (None passes) is a device tensor of at least
     `rows` rows, each of at least `row_elems` elements stored densely, with
-    element size `esize`; with whole=True the rows must also be packed
-    back to back.  The library trusts the sizes it is given, so buffers are
-    measured here, before any launch, rather than read out of bounds."""
+    element size `esize`.  whole=True is for buffers the library addresses
+    as packed rows of exactly `row_elems` elements (it takes no row stride
+    for them): each row must then hold exactly that many elements and the
+    rows must follow each other with no gap.  The library trusts the sizes
+    it is given, so buffers are measured here, before any launch, rather
+    than read or written out of bounds or at the wrong place."""
     if t is None:
         return
     if not getattr(t, "is_cuda", False):
@@ -218,13 +221,19 @@ def _need(t, name, rows, row_elems, esize=None, whole=False):
     if t.is_contiguous() and (esize is None or t.element_size() == esize):
         # the common case, in a few calls: dense rows packed back to back
         n0 = int(t.shape[0])
-        if n0 == 0 or t.numel() // n0 >= row_elems:
+        if n0 == 0:
+            return
+        per = t.numel() // n0
+        if per == row_elems or (per > row_elems and not whole):
             return
     per_row = 1
     for d in t.shape[1:]:
         per_row *= int(d)
     if per_row < row_elems:
         raise ValueError(f"{name}: rows of {row_elems} elements needed, shape is {tuple(t.shape)}")
+    if whole and per_row != row_elems:
+        raise ValueError(f"{name}: rows of exactly {row_elems} elements needed (the library takes "
+                         f"no row stride for it), shape is {tuple(t.shape)}")
     if esize is not None and t.element_size() != esize:
         raise ValueError(f"{name}: {esize}-byte elements needed, not {t.element_size()}")
     step = 1

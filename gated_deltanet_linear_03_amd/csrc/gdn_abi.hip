@@ -517,13 +517,15 @@ gdn_status gdn_layer_prefill(const gdn_layer* L, const gdn_proj* pr, const gdn_l
     if (st != GDN_OK) return st;
     if (T == 0) return prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // the tiled kernel at every T: a sequence's bits do not depend on how
+    // many tokens share the call
     hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, T, w.P,
-                                            pr->hidden, s);
+                                            pr->hidden, s, gdn::kGemmTiled);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
     st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
     if (st != GDN_OK) return st;
     e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, T,
-                                 pr->hidden, HD, s);
+                                 pr->hidden, HD, s, gdn::kGemmTiled);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }
@@ -582,13 +584,15 @@ gdn_status gdn_layer_decode(const gdn_layer* L, const gdn_proj* pr, const gdn_la
     st = decode_impl(&Lg, &dio, 0, nullptr, stream, false);
     if (st != GDN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // the few-row kernel at every B: a sequence's bits do not depend on the
+    // batch size
     hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, B, w.P,
-                                            pr->hidden, s);
+                                            pr->hidden, s, gdn::kGemmSkinny);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
     st = decode_impl(&Lg, &dio, 0, nullptr, stream);
     if (st != GDN_OK) return st;
     e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, B,
-                                 pr->hidden, HD, s);
+                                 pr->hidden, HD, s, gdn::kGemmSkinny);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }

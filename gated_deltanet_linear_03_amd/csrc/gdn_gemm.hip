@@ -302,7 +302,8 @@ hipError_t launch_gemm_t(const uint16_t* a, int64_t lda, const uint16_t* b, int6
 // 256-byte runs.  Every pair of the MT 16-row tiles of A and the NTW B tiles
 // is multiplied; the waves' partial tiles are summed in LDS in wave order.
 // Each output depends on its A row, B row, K and NWV only, never on M or on
-// the other rows.
+// the other rows.  More than 64 rows run as 64-row blocks over the grid's
+// second dimension.
 constexpr int kSkinnyMax = 64;
 constexpr int kSkinnyStep = 128;
 
@@ -311,6 +312,14 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_skinny_kernel(
         const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
         void* __restrict__ Cv, int64_t ldc, int64_t M, int64_t N, int64_t K) {
     __shared__ f32x4 part[NWV][MT * NTW][kWave];
+    // this work-group's block of (at most kSkinnyMax) rows
+    A += static_cast<int64_t>(blockIdx.y) * kSkinnyMax * lda;
+    M -= static_cast<int64_t>(blockIdx.y) * kSkinnyMax;
+    if (M > kSkinnyMax) M = kSkinnyMax;
+    if constexpr (OUT_BF16)
+        Cv = static_cast<uint16_t*>(Cv) + static_cast<int64_t>(blockIdx.y) * kSkinnyMax * ldc;
+    else
+        Cv = static_cast<float*>(Cv) + static_cast<int64_t>(blockIdx.y) * kSkinnyMax * ldc;
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
@@ -396,7 +405,9 @@ __global__ __launch_bounds__(NWV * kWave) void gemm_skinny_kernel(
 template <int MT, int NTW, int NWV>
 hipError_t launch_skinny_t(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, void* C,
                            int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>((N + 16 * NTW - 1) / (16 * NTW))), block(NWV * kWave);
+    const dim3 grid(static_cast<unsigned>((N + 16 * NTW - 1) / (16 * NTW)),
+                    static_cast<unsigned>((M + kSkinnyMax - 1) / kSkinnyMax)),
+        block(NWV * kWave);
     if (out_bf16)
         hipLaunchKernelGGL((gemm_skinny_kernel<MT, NTW, NWV, true>), grid, block, 0, s, a, lda, b, ldb, C, ldc, M, N, K);
     else
@@ -408,7 +419,7 @@ hipError_t launch_skinny_t(const uint16_t* a, int64_t lda, const uint16_t* b, in
 
 hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                                int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K,
-                               hipStream_t s) {
+                               hipStream_t s, GemmPath path) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const auto a = static_cast<const uint16_t*>(A);
     const auto b = static_cast<const uint16_t*>(B);
@@ -417,7 +428,7 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (M <= kSkinnyMax) {
+    if (path == kGemmSkinny || (path == kGemmAuto && M <= kSkinnyMax)) {
         // few rows (A rows and lda are 16-byte aligned, K a multiple of 8)
         // With n tiles to spare (at least two per compute unit) K is split
         // over 4 waves and, past 16 rows, a work-group takes 4 n tiles so
@@ -425,7 +436,7 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
         // waves, one n tile each.  The split depends on N only, so a row's
         // bits do not depend on M.
         const bool many = (N + 15) / 16 >= 2ll * cus;
-        const int mt = static_cast<int>((M + 15) / 16);
+        const int mt = static_cast<int>(((M < kSkinnyMax ? M : kSkinnyMax) + 15) / 16);
 #define GDN_SKINNY(MT_, NTW_, NWV_) \
     return launch_skinny_t<MT_, NTW_, NWV_>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s)
         if (many) {

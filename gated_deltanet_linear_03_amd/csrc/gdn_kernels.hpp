@@ -122,9 +122,19 @@ hipError_t launch_prefill(int DK, int DV, int C, bool bf16, const PrefillParams&
 bool prefill_shape_supported(int DK, int DV, int C);
 bool decode_shape_supported(int DK, int DV);
 hipError_t launch_selftest_mfma(const float* A, const float* B, float* C, hipStream_t s);
+// Which GEMM kernel family computes a product.  Each family sums every
+// output element in an order that depends on K (and, for the few-row one,
+// on N) but never on M, so a row's bits are independent of the other rows
+// as long as the family is fixed:
+//   kGemmAuto    the few-row kernel up to 64 rows, else the tiled one
+//   kGemmTiled   always the tiled kernel (the layer's prefill projections)
+//   kGemmSkinny  always the few-row kernel, over 64-row blocks (the layer's
+//                decode projections, at any batch size)
+enum GemmPath { kGemmAuto = 0, kGemmTiled = 1, kGemmSkinny = 2 };
+
 // C[M][N] = A[M][K] B[N][K]^T, bf16 in, fp32 accumulation, bf16 or fp32 out
 hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                                int64_t ldc, bool out_bf16, int64_t M, int64_t N, int64_t K,
-                               hipStream_t s);
+                               hipStream_t s, GemmPath path = kGemmAuto);
 
 }  // namespace gdn

@@ -112,6 +112,31 @@ def proj_weights(shape: LayerShape, hidden: int, seed: int):
     return w_in, w_out
 
 
+def proj_weights_floored(shape: LayerShape, hidden: int, seed: int, floor: float = 2.0 ** -10):
+    """proj_weights with every |w_in| raised to at least `floor` (sign
+    kept): dense N(0, 1/fan_in) weights whose magnitudes span at most ~8
+    binades, so that with sparse_hidden_inputs every in_proj sum is exact
+    in fp32."""
+    w_in, w_out = proj_weights(shape, hidden, seed)
+    w_in = np.where(np.abs(w_in) < floor, np.where(w_in < 0, -floor, floor), w_in).astype(np.float32)
+    return w_in, w_out
+
+
+def sparse_hidden_inputs(T: int, hidden: int, seed: int, nnz: int = 8):
+    """x [T, hidden] with nnz nonzeros per row at random columns, each one
+    of +-1/2, +-1, +-2.  Against bf16 weights of magnitude in [2^-10, 1)
+    each product has at most 9 significant bits and every partial sum of a
+    row fits in 24 bits, so in_proj is exact in fp32 in any summation
+    order: both sides of a parity test see the same projection bits."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 9])))
+    x = np.zeros((T, hidden), dtype=np.float32)
+    vals = np.array([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], dtype=np.float32)
+    for t in range(T):
+        cols = rng.choice(hidden, nnz, replace=False)
+        x[t, cols] = rng.choice(vals, nnz)
+    return x
+
+
 def proj_weights_exact(shape: LayerShape, hidden: int, seed: int):
     """w_in with one nonzero per row, +-1 or +-1/2 at a random column, so a
     projection of bf16 inputs is exact in bf16 whatever the summation order

@@ -230,7 +230,12 @@ gdn_status gdn_decode_multi(const gdn_layer* layer, const gdn_decode_io* io,
 /* C[M][N] = A[M][K] * B[N][K]^T: A, B bf16 (k contiguous, leading dims lda,
  * ldb in elements), C in c_dtype (GDN_DTYPE_BF16 or GDN_DTYPE_FP32, leading
  * dim ldc), fp32 accumulation.  K, lda, ldb multiples of 8 and A, B 16-byte
- * aligned; M, N, K >= 0.  Enqueued on `stream`. */
+ * aligned; M, N, K >= 0.  Enqueued on `stream`.  Up to 64 rows run on a
+ * weight-streaming few-row kernel, more on a tiled one; each sums an output
+ * in an order that depends on K and N only, but the two orders differ, so
+ * a row's bits may change when M crosses 64.  gdn_layer_prefill and
+ * gdn_layer_decode each keep to one kernel family at every size, so their
+ * results do not depend on the batch. */
 gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
                          void* C, int64_t ldc, int32_t c_dtype, int64_t M,
                          int64_t N, int64_t K, void* stream);

@@ -149,6 +149,28 @@ def state_errors(got, ref):
     return max(rel_err(got[n], ref[n]) for n in range(got.shape[0])) if got.shape[0] else 0.0
 
 
+def oracle_layer(sh, params, cu, x, S0=None, C0=None, nthreads=0):
+    """fp64 oracle over numpy token inputs x (dict q, k, v, z, a, b) with
+    per-sequence states S0 [N, Hv, dk, dv] and C0 [N, K-1, Cc] (None =
+    zeros)."""
+    return oracle.gdn_forward(dims(sh), cu, x["q"], x["k"], x["v"], x["z"], x["a"], x["b"],
+                              params["conv_w"], params["A_log"], params["dt_bias"],
+                              params["norm_w"], S0, C0, nthreads=nthreads)
+
+
+def check_against_oracle(cu, ref, out, core=None, state=None, conv=None, tol=TOL, label=""):
+    """Per-sequence metric of out (and core_out, final states) against the
+    oracle's dict; conv states exact.  Arrays are numpy, rows as in ref."""
+    e_out = per_seq_errors(cu, np.asarray(out, dtype=np.float64), ref["out"])
+    e_core = 0.0 if core is None else per_seq_errors(cu, core, ref["core_out"])
+    e_state = 0.0 if state is None else state_errors(state, ref["final_state"])
+    print(f"{label} vs oracle: out {e_out:.3e} core {e_core:.3e} state {e_state:.3e}", flush=True)
+    assert e_out < tol and e_core < tol and e_state < tol, (label, e_out, e_core, e_state)
+    if conv is not None:
+        assert np.array_equal(np.asarray(conv, dtype=np.float64), ref["conv_state_out"]), label
+    return e_out, e_core, e_state
+
+
 def check_prefill(case, res, ref, tol=TOL, heads=None, label=""):
     cu = case.cu_seqlens
     sel = slice(None) if heads is None else heads

@@ -215,12 +215,12 @@ def test_binding_marshals_to_the_abi_and_raises():
     """The Python wrappers reach the C ABI and turn its status into GdnError
     (validation fails on the host before anything touches a device)."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     t = _fake_act(FAKE, 16 * 128)
     kw = dict(N=1, T_total=64, cu_seqlens=_FakeTensor(FAKE), q=t, k=t,
               v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
-              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE, 32 * 128),
               stream=_FakeStream())
     with pytest.raises(gdn.GdnError) as ei:
         gdn.prefill_raw(lay, workspace=None, **kw)
@@ -241,9 +241,9 @@ def test_binding_marshals_to_the_abi_and_raises():
     with pytest.raises(gdn.GdnError):
         gdn.decode_raw(lay, B=2, q=t, k=t, v=_fake_act(FAKE, 32 * 128),
                        z=_fake_act(FAKE, 32 * 128), a=_fake_act(FAKE, 32),
-                       b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE + 4),
-                       state_in=None, state_out=_FakeTensor(FAKE),
-                       conv_state_in=None, conv_state_out=_fake_act(FAKE),
+                       b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE + 4, 32 * 128),
+                       state_in=None, state_out=_FakeTensor(FAKE, 32 * 128 * 128),
+                       conv_state_in=None, conv_state_out=_fake_act(FAKE, 3 * 8192),
                        stream=_FakeStream())
     assert gdn.prefill_workspace_bytes(lay, 1, 4096) > 0
 
@@ -255,8 +255,8 @@ def test_prefill_windows_follow_the_workspace():
     needed, a smaller workspace more windows, down to one chunk slot; below
     that the call is refused."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     # -W, Q_G, K_d^T, P as fp16 fragments and U~ as fp32, for 32 value heads
     slot = 32 * (2 * 64 * 128 + 4 * 64 * 128 + 2 * 128 * 64 + 4 * 64 * 64 + 4 * 64 * 128)
 
@@ -298,13 +298,13 @@ def test_decode_multi_rejects_token_counts():
     """gdn_decode_multi takes 1..GDN_MAX_VERIFY_TOKENS tokens per sequence and
     refuses snapshot buffers that overlap a state (host-side checks)."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     t = _fake_act(FAKE, 16 * 128)
     kw = dict(B=2, q=t, k=t, v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
-              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE + 4096),
-              state_in=_FakeTensor(FAKE + (1 << 24)), state_out=_FakeTensor(FAKE + (1 << 24)),
-              conv_state_in=None, conv_state_out=_fake_act(FAKE + (1 << 26)),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE + 4096, 32 * 128),
+              state_in=_FakeTensor(FAKE + (1 << 24), 32 * 128 * 128), state_out=_FakeTensor(FAKE + (1 << 24), 32 * 128 * 128),
+              conv_state_in=None, conv_state_out=_fake_act(FAKE + (1 << 26), 3 * 8192),
               stream=_FakeStream())
     for bad in (0, gdn.MAX_VERIFY_TOKENS + 1):
         with pytest.raises(gdn.GdnError) as ei:
@@ -312,26 +312,26 @@ def test_decode_multi_rejects_token_counts():
         assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT
         assert b"tokens" in gdn.lib().gdn_last_error()
     with pytest.raises(gdn.GdnError) as ei:
-        gdn.decode_multi_raw(lay, tokens=4, state_snapshots=_FakeTensor(FAKE + (1 << 24) + 4096), **kw)
+        gdn.decode_multi_raw(lay, tokens=4, state_snapshots=_FakeTensor(FAKE + (1 << 24) + 4096, 4 * 32 * 128 * 128), **kw)
     assert b"snapshots" in gdn.lib().gdn_last_error()
 
 
 def _verify_kw(**over):
     t = _fake_act(FAKE, 16 * 128)
     kw = dict(B=8, tokens=4, q=t, k=t, v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
-              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE),
-              state_in=_FakeTensor(FAKE), state_out=_FakeTensor(FAKE),
-              conv_state_in=_fake_act(FAKE), conv_state_out=_fake_act(FAKE), stream=_FakeStream())
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE, 32 * 128),
+              state_in=_FakeTensor(FAKE, 32 * 128 * 128), state_out=_FakeTensor(FAKE, 32 * 128 * 128),
+              conv_state_in=_fake_act(FAKE, 3 * 8192), conv_state_out=_fake_act(FAKE, 3 * 8192), stream=_FakeStream())
     kw.update(over)
     return kw
 
 
 @pytest.mark.parametrize("over, name", [
     # a pool of 3 states handed to an 8-sequence verify
-    (dict(state_in=_FakeTensor(FAKE, rows=3)), "state_in"),
-    (dict(state_out=_FakeTensor(FAKE, rows=3)), "state_out"),
+    (dict(state_in=_FakeTensor(FAKE, 32 * 128 * 128, rows=3)), "state_in"),
+    (dict(state_out=_FakeTensor(FAKE, 32 * 128 * 128, rows=3)), "state_out"),
     (dict(conv_state_out=_fake_act(FAKE, 8192)), "conv_state_out"),       # rows of 1 tap
-    (dict(out=_FakeTensor(FAKE, rows=31)), "out"),                      # 8 x 4 token rows
+    (dict(out=_FakeTensor(FAKE, 32 * 128, rows=31)), "out"),                      # 8 x 4 token rows
     (dict(q=_fake_act(FAKE, 16 * 64)), "q"),                            # half a row
     (dict(v=_FakeTensor(FAKE, 32 * 128)), "v"),                         # fp32, layer is bf16
     (dict(state_snapshots=_FakeTensor(FAKE, 4 * 32 * 128 * 128, rows=7)), "state_snapshots"),
@@ -341,8 +341,8 @@ def test_binding_refuses_short_buffers(over, name):
     library (which trusts them) and refuses a short or mistyped one before
     anything is launched."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     with pytest.raises(ValueError, match=name):
         gdn.decode_multi_raw(lay, **_verify_kw(**over))
 
@@ -352,8 +352,8 @@ def test_binding_refuses_padded_state_rows():
     between its rows is refused, token inputs may have it (their token
     stride is passed on)."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     padded_state = _FakeTensor(FAKE, 32 * 128 * 128, rows=8, pad=64)
     with pytest.raises(ValueError, match="state_out: rows must be packed"):
         gdn.decode_multi_raw(lay, **_verify_kw(state_out=padded_state))
@@ -365,26 +365,46 @@ def test_binding_refuses_padded_state_rows():
                       None, None, None, None)
 
 
+@pytest.mark.parametrize("over, name", [
+    # a pool laid out with one extra head per entry
+    (dict(state_out=_FakeTensor(FAKE, 33 * 128 * 128, rows=8)), "state_out"),
+    (dict(state_in=_FakeTensor(FAKE, 32 * 128 * 129, rows=8)), "state_in"),
+    (dict(out=_FakeTensor(FAKE, 32 * 128 + 8, rows=32)), "out"),
+    (dict(conv_state_out=_FakeTensor(FAKE, 3 * 8192 + 8, esize=2, rows=8)), "conv_state_out"),
+    (dict(state_snapshots=_FakeTensor(FAKE, 4 * 32 * 128 * 128 + 64, rows=8)), "state_snapshots"),
+])
+def test_binding_refuses_wider_packed_rows(over, name):
+    """Buffers the library addresses as packed rows with no stride (states,
+    conv states, out, snapshots) must have rows of exactly the library's
+    width: a contiguous tensor with wider rows would be read and written at
+    the wrong places, so it is refused."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
+    with pytest.raises(ValueError, match=f"{name}: rows of exactly"):
+        gdn.decode_multi_raw(lay, **_verify_kw(**over))
+
+
 def test_binding_refuses_short_prefill_buffers():
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                    conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                    dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                    conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                    dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     t = _fake_act(FAKE, 16 * 128)
     kw = dict(N=2, T_total=64, cu_seqlens=_FakeTensor(FAKE), q=t, k=t,
               v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
-              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE, 32 * 128),
               stream=_FakeStream())
     with pytest.raises(ValueError, match="cu_seqlens"):
         gdn.prefill_raw(lay, **dict(kw, cu_seqlens=_FakeTensor(FAKE, 1, rows=2)))
     with pytest.raises(ValueError, match="final_state"):
-        gdn.prefill_raw(lay, final_state=_FakeTensor(FAKE, rows=1), **kw)
+        gdn.prefill_raw(lay, final_state=_FakeTensor(FAKE, 32 * 128 * 128, rows=1), **kw)
     with pytest.raises(ValueError, match="initial_state"):     # a pool of 4 entries, 5 claimed
-        gdn.prefill_raw(lay, initial_state=_FakeTensor(FAKE, rows=4),
+        gdn.prefill_raw(lay, initial_state=_FakeTensor(FAKE, 32 * 128 * 128, rows=4),
                         state_slots=_FakeTensor(FAKE, 1, rows=2), num_slots=5, **kw)
     with pytest.raises(ValueError, match="conv_w"):
         bad = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64,
-                        conv_w=_FakeTensor(FAKE, 4, rows=8191), A_log=_FakeTensor(FAKE),
-                        dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+                        conv_w=_FakeTensor(FAKE, 4, rows=8191), A_log=_FakeTensor(FAKE, 1),
+                        dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
         gdn.prefill_raw(bad, **kw)
 
 
@@ -454,8 +474,8 @@ def _host_snapshot(Hk=2, Hv=4, dk=32, dv=32, act=gdn.GDN_DTYPE_FP32, seed=0):
 
 
 def test_snapshot_size_and_inspect():
-    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
-                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE, 4),
+                    A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     Cc = 2 * 16 * 128 + 32 * 128
     assert gdn.snapshot_bytes(lay) == 64 + 32 * 128 * 128 * 4 + 3 * Cc * 2
     buf = _host_snapshot()
@@ -484,18 +504,18 @@ def test_snapshot_restore_rejects_another_layer():
     buf = _host_snapshot(Hk=2, Hv=4, dk=32, dv=32, act=gdn.GDN_DTYPE_FP32)
     for kw in (dict(Hk=2, Hv=4, dk=32, dv=64), dict(Hk=1, Hv=4, dk=32, dv=32),
                dict(Hk=2, Hv=4, dk=32, dv=32, act_dtype=gdn.GDN_DTYPE_BF16)):
-        lay = gdn.Layer(chunk=16, conv_w=_FakeTensor(FAKE), A_log=_FakeTensor(FAKE),
-                        dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE), **kw)
-        conv = _FakeTensor(FAKE, esize=2 if lay.act_dtype == gdn.GDN_DTYPE_BF16 else 4)
+        lay = gdn.Layer(chunk=16, conv_w=_FakeTensor(FAKE, 4), A_log=_FakeTensor(FAKE, 1),
+                        dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1), **kw)
+        conv = _FakeTensor(FAKE, 3 * lay.Cc, esize=2 if lay.act_dtype == gdn.GDN_DTYPE_BF16 else 4)
         with pytest.raises(gdn.GdnError) as ei:
-            gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), conv, slot=0,
+            gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE, lay.Hv * lay.dk * lay.dv), conv, slot=0,
                                  num_slots=1, stream=_FakeStream())
         assert "does not fit this layer" in ei.value.detail
-    lay = gdn.Layer(Hk=2, Hv=4, dk=32, dv=32, chunk=16, conv_w=_FakeTensor(FAKE),
-                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE),
+    lay = gdn.Layer(Hk=2, Hv=4, dk=32, dv=32, chunk=16, conv_w=_FakeTensor(FAKE, 4),
+                    A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1),
                     act_dtype=gdn.GDN_DTYPE_FP32)
     with pytest.raises(gdn.GdnError) as ei:
-        gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE), _FakeTensor(FAKE), slot=3,
+        gdn.snapshot_restore(lay, buf, _FakeTensor(FAKE, 4 * 32 * 32), _FakeTensor(FAKE, 3 * 256), slot=3,
                              num_slots=3, stream=_FakeStream())
     assert "outside" in ei.value.detail
 
@@ -522,16 +542,16 @@ def test_layer_workspace_and_rejects():
     """The layer workspace is the bf16 projection [T][P], the bf16 gated
     output [T][Hv dv] (each 256-byte rounded) and gdn_prefill's workspace;
     fp32 activations are refused (the projection is handed over in bf16)."""
-    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
-                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
-    proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE), w_out=_FakeTensor(FAKE))
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE, 4),
+                    A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
+    proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE, 2048), w_out=_FakeTensor(FAKE, 4096))
     T = 4096
     P = 2 * 16 * 128 + 2 * 32 * 128 + 2 * 32
     rnd = lambda n: -(-n // 256) * 256
     assert gdn.layer_prefill_workspace_bytes(lay, proj, 1, T) == (
         rnd(2 * T * P) + rnd(2 * T * 32 * 128) + gdn.prefill_workspace_bytes(lay, 1, T))
-    lay32 = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
-                      A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE),
+    lay32 = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE, 4),
+                      A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1),
                       act_dtype=gdn.GDN_DTYPE_FP32)
     with pytest.raises(gdn.GdnError) as ei:
         gdn.layer_prefill_workspace_bytes(lay32, proj, 1, T)
@@ -543,9 +563,9 @@ def test_layer_workspace_and_rejects():
 def test_layer_decode_workspace():
     """The decode layer's workspace: the bf16 projection [B][P] and gated
     output [B][Hv dv], each 256-byte rounded."""
-    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE),
-                    A_log=_FakeTensor(FAKE), dt_bias=_FakeTensor(FAKE), norm_w=_FakeTensor(FAKE))
-    proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE), w_out=_FakeTensor(FAKE))
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE, 4),
+                    A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
+    proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE, 2048), w_out=_FakeTensor(FAKE, 4096))
     P = 2 * 16 * 128 + 2 * 32 * 128 + 2 * 32
     rnd = lambda n: -(-n // 256) * 256
     for B in (1, 3, 64):

@@ -208,10 +208,12 @@ def _gpu_decode(sh, params, x, S0, C0, in_place=True):
     return res
 
 
-@pytest.mark.parametrize("shape_name,B", [("full", 3), ("full", 64), ("tiny", 5)])
+@pytest.mark.parametrize("shape_name,B", [("full", 3), ("full", 64), ("tiny", 5), ("d64", 4)])
 def test_decode_parity(shape_name, B):
-    sh = synth.FULL if shape_name == "full" else synth.TINY
-    params = synth.layer_params(sh, 21)
+    """d64: the dk = dv = 64 instantiation, with a non-uniform norm weight."""
+    sh = {"full": synth.FULL, "tiny": synth.TINY,
+          "d64": synth.LayerShape(Hk=2, Hv=4, dk=64, dv=64, chunk=16, act_dtype="bf16")}[shape_name]
+    params = synth.layer_params(sh, 21, norm_w_jitter=shape_name == "d64")
     x, S0, C0 = _decode_case(sh, B, 22)
     res = _gpu_decode(sh, params, x, S0, C0)
     import oracle

@@ -1,7 +1,9 @@
 """State pools (state_slots) and the mixed serving step (gdn_step): results
-through a pool are bit-identical to the dense layout, pool entries nobody
-names stay untouched, and one gdn_step equals the separate decode and
-prefill calls."""
+through a pool match the fp64 oracle run on the pool entries' states and are
+bit-identical to the dense layout, pool entries nobody names stay untouched,
+and one gdn_step matches the oracle and equals the separate decode and
+prefill calls (llmxabe README, status paragraph: prefill and decode batched
+across parallel sequences)."""
 import numpy as np
 import pytest
 import torch
@@ -11,13 +13,21 @@ from gated_deltanet_linear_03_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-from gpu_helpers import act_dtype, make_layer, to_dev, workspace_for_window  # noqa: E402
+from gpu_helpers import (act_dtype, check_against_oracle, make_layer, oracle_layer,  # noqa: E402
+                         to_dev, workspace_for_window)
+
+
+def _pool_np(sh, S, seed):
+    return synth.initial_states(sh, S, seed), synth.conv_states(sh, S, seed + 1)
 
 
 def _pool(sh, S, seed, ad):
-    st = to_dev(synth.initial_states(sh, S, seed))
-    cs = to_dev(synth.conv_states(sh, S, seed + 1), ad)
-    return st, cs
+    st, cs = _pool_np(sh, S, seed)
+    return to_dev(st), to_dev(cs, ad)
+
+
+def _np(t):
+    return t.float().cpu().numpy()
 
 
 def test_decode_through_a_pool_bitwise():
@@ -27,7 +37,8 @@ def test_decode_through_a_pool_bitwise():
     S, slots = 9, [7, 2, 5, 0]
     B = len(slots)
     pst, pcs = _pool(sh, S, 402, ad)
-    t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, B, 403).items()}
+    tn = synth.token_inputs(sh, B, 403)
+    t = {k: to_dev(v, ad) for k, v in tn.items()}
     idx = torch.tensor(slots, device="cuda")
     dense = gdn.decode(layer, *(t[n] for n in "qkvzab"), pst[idx].clone(), pcs[idx].clone(),
                        in_place=True, want_core=True)
@@ -44,6 +55,11 @@ def test_decode_through_a_pool_bitwise():
     assert torch.equal(pcs[idx], dense["conv_state_out"])
     rest = [i for i in range(S) if i not in slots]
     assert torch.equal(pst[rest], before_st[rest]) and torch.equal(pcs[rest], before_cs[rest])
+    # the oracle on the named entries' states, one token per sequence
+    S_np, C_np = _pool_np(sh, S, 402)
+    ref = oracle_layer(sh, synth.layer_params(sh, 401), np.arange(B + 1), tn, S_np[slots], C_np[slots])
+    check_against_oracle(np.arange(B + 1), ref, _np(out), _np(core), _np(pst[idx]), _np(pcs[idx]),
+                         label="pool decode")
 
 
 @pytest.mark.parametrize("window_slots", [None, 1])
@@ -78,6 +94,10 @@ def test_prefill_through_a_pool_bitwise(window_slots):
     assert torch.equal(pcs[idx], dense["conv_state_out"])
     rest = [i for i in range(S) if i not in slots]
     assert torch.equal(pst[rest], before_st[rest]) and torch.equal(pcs[rest], before_cs[rest])
+    S_np, C_np = _pool_np(sh, S, 405)
+    ref = oracle_layer(sh, case.params, case.cu_seqlens, case.inputs, S_np[slots], C_np[slots])
+    check_against_oracle(case.cu_seqlens, ref, _np(out), None, _np(pst[idx]), _np(pcs[idx]),
+                         label=f"pool prefill w={window_slots}")
 
 
 def test_step_mixed_equals_separate_calls():
@@ -93,7 +113,8 @@ def test_step_mixed_equals_separate_calls():
     x = {k: to_dev(v, ad) for k, v in pcase.inputs.items()}
     cu = to_dev(pcase.cu_seqlens)
     T = int(pcase.cu_seqlens[-1])
-    t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, len(dslots), 408).items()}
+    tn = synth.token_inputs(sh, len(dslots), 408)
+    t = {k: to_dev(v, ad) for k, v in tn.items()}
     pst0, pcs0 = _pool(sh, S, 409, ad)
     ws = torch.empty(gdn.prefill_workspace_bytes(layer, len(lens), T), dtype=torch.uint8, device="cuda")
 
@@ -123,3 +144,13 @@ def test_step_mixed_equals_separate_calls():
     assert torch.equal(a_st, b_st) and torch.equal(a_cs, b_cs)
     untouched = [i for i in range(S) if i not in pslots + dslots]
     assert torch.equal(a_st[untouched], pst0[untouched])
+    # both halves of the step against the oracle on the entries' states
+    params = synth.layer_params(sh, 406)
+    S_np, C_np = _pool_np(sh, S, 409)
+    ref_p = oracle_layer(sh, params, pcase.cu_seqlens, pcase.inputs, S_np[pslots], C_np[pslots])
+    check_against_oracle(pcase.cu_seqlens, ref_p, _np(pa), None, _np(a_st[pslots]),
+                         _np(a_cs[pslots]), label="step prefill")
+    B = len(dslots)
+    ref_d = oracle_layer(sh, params, np.arange(B + 1), tn, S_np[dslots], C_np[dslots])
+    check_against_oracle(np.arange(B + 1), ref_d, _np(da), None, _np(a_st[dslots]),
+                         _np(a_cs[dslots]), label="step decode")

@@ -1,6 +1,9 @@
 """Session snapshots: park a sequence's state in host memory, clobber the
 device copy, restore it (into another pool entry) and continue -- the
-continuation must be bit-identical to the run that never stopped."""
+continuation must be bit-identical to the run that never stopped (skindeep.ai
+"Our own inference runtime", "Session swap": restart-and-continue reproduces
+the output exactly), and match the fp64 oracle's uninterrupted run over both
+segments."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +13,7 @@ from gated_deltanet_linear_03_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-from gpu_helpers import act_dtype, make_layer, to_dev  # noqa: E402
+from gpu_helpers import act_dtype, check_against_oracle, make_layer, oracle_layer, to_dev  # noqa: E402
 
 
 @pytest.mark.parametrize("shape", ["full", "tiny"])
@@ -23,8 +26,10 @@ def test_restart_and_continue_bitwise(shape):
     case_b = synth.prefill_case(sh, lens_b, seed=502)
     layer = make_layer(sh, case_a.params)
     S = 4
-    pst0 = to_dev(synth.initial_states(sh, S, 503))
-    pcs0 = to_dev(synth.conv_states(sh, S, 504), ad)
+    S_np = synth.initial_states(sh, S, 503)
+    C_np = synth.conv_states(sh, S, 504)
+    pst0 = to_dev(S_np)
+    pcs0 = to_dev(C_np, ad)
 
     def run(case, pst, pcs, slot):
         x = {k: to_dev(v, ad) for k, v in case.inputs.items()}
@@ -59,6 +64,17 @@ def test_restart_and_continue_bitwise(shape):
     out = run(case_b, st, cs, 1)
     assert torch.equal(out, out_ref)
     assert torch.equal(st[1], ref_st[2]) and torch.equal(cs[1], ref_cs[2])
+
+    # the oracle without interruption: one sequence of both segments from
+    # entry 2's original states; the resumed segment's outputs and the
+    # states after it must match its tail
+    La, Lb = lens_a[0], lens_b[0]
+    xab = {k: np.concatenate([case_a.inputs[k], case_b.inputs[k]]) for k in case_a.inputs}
+    ref = oracle_layer(sh, case_a.params, np.array([0, La + Lb]), xab, S_np[2:3], C_np[2:3])
+    tail = {"out": ref["out"][La:], "core_out": ref["core_out"][La:],
+            "final_state": ref["final_state"], "conv_state_out": ref["conv_state_out"]}
+    check_against_oracle(np.array([0, Lb]), tail, out.cpu().numpy(), None, st[1:2].cpu().numpy(),
+                         cs[1:2].float().cpu().numpy(), label=f"snapshot resume {shape}")
 
     # and a decode step from the restored entry matches one from the original
     t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, 1, 505).items()}
