@@ -34,7 +34,8 @@ EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_step", "gdn_snapshot_bytes", "gdn_snapshot_save", "gdn_snapshot_inspect",
            "gdn_snapshot_restore", "gdn_gemm_bf16", "gdn_layer_prefill_workspace_bytes",
            "gdn_layer_prefill", "gdn_layer_decode_workspace_bytes", "gdn_layer_decode",
-           "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma")
+           "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma", "gdn_prefill_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20       # GDN_NOALLOC_SCRATCH_BYTES
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
 PREFILL_KERNELS = ("prep", "scan", "epi")
@@ -136,6 +137,9 @@ def lib():
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_prefill.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_prefill_noalloc.restype = ctypes.c_int
+        L.gdn_prefill_noalloc.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
+                                          ctypes.c_void_p]
         L.gdn_step.restype = ctypes.c_int
         L.gdn_step.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                ctypes.POINTER(CDecodeIO), ctypes.c_void_p, ctypes.c_size_t,
@@ -408,6 +412,18 @@ def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
         _check(lib().gdn_prefill_timed(ctypes.byref(cl), ctypes.byref(io), _ptr(workspace),
                                        int(workspace_bytes), _stream(stream), arr,
                                        len(events)))
+
+
+def prefill_noalloc_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b, out,
+                        core_out=None, initial_state=None, final_state=None,
+                        conv_state_in=None, conv_state_out=None, stream=None,
+                        state_slots=None, num_slots=0):
+    """Call ``gdn_prefill_noalloc``: gdn_prefill on caller-provided buffers
+    with the library's static device scratch as the workspace."""
+    cl = layer.c()
+    io = _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
+                     final_state, conv_state_in, conv_state_out, state_slots, num_slots)
+    _check(lib().gdn_prefill_noalloc(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
 
 
 def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,

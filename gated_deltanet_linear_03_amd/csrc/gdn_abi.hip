@@ -6,8 +6,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gdn.h"
 #include "gdn_kernels.hpp"
+
+// Device scratch of gdn_prefill_noalloc, one copy per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -264,6 +272,51 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
 gdn_status gdn_prefill(const gdn_layer* L, const gdn_prefill_io* io, void* ws, size_t ws_bytes,
                        void* stream) {
     return prefill_impl(L, io, ws, ws_bytes, stream, nullptr);
+}
+
+// Device address of `scratch` on the stream's device, looked up with that
+// device current on the first call there and kept per device.
+static gdn_status noalloc_scratch(void* stream, void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (stream) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+        if (static_cast<int>(sd) != cur)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "the stream belongs to device %d, device %d is current: "
+                        "make the stream's device current", static_cast<int>(sd), cur);
+    }
+    if (cur < 0 || cur >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device index %d >= %d", cur, kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[cur]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        addr[cur] = ptr;
+    }
+    *out = addr[cur];
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_noalloc(const gdn_layer* L, const gdn_prefill_io* io, void* stream) {
+    g_err[0] = 0;
+    void* ws = nullptr;
+    gdn_status st = noalloc_scratch(stream, &ws);
+    if (st != GDN_OK) return st;
+    st = prefill_impl(L, io, ws, GDN_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+    if (st == GDN_ERR_WORKSPACE) {
+        char detail[sizeof g_err];
+        memcpy(detail, g_err, sizeof detail);
+        return fail(GDN_ERR_WORKSPACE, "gdn_prefill_noalloc: its %llu-byte scratch is too small for these "
+                    "sizes (%s)", static_cast<unsigned long long>(GDN_NOALLOC_SCRATCH_BYTES), detail);
+    }
+    return st;
 }
 
 int64_t gdn_prefill_launches(const gdn_layer* L, int32_t N, int64_t T, size_t ws_bytes) {

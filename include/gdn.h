@@ -166,6 +166,29 @@ size_t gdn_prefill_workspace_bytes(const gdn_layer* layer, int32_t N,
 gdn_status gdn_prefill(const gdn_layer* layer, const gdn_prefill_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device scratch array behind gdn_prefill_noalloc. */
+#define GDN_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+/* gdn_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The caller passes the inputs and outputs as for gdn_prefill but no
+ * workspace: the library uses a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES instead, one per device, allocated when the
+ * library's device code is loaded and held until the process ends (its
+ * address is looked up on the first call on each device).  It calls no
+ * allocating routine.  Same kernels and bit-identical results as
+ * gdn_prefill with a workspace of that size.  Sizes whose workspace does not
+ * fit that array (the fixed parts plus one chunk slot of operand blocks,
+ * plus T_total*Hv*dv*4 bytes of pre-norm output when core_out is NULL) are
+ * refused with GDN_ERR_WORKSPACE before anything is enqueued.  The stream's
+ * device must be the current device (else GDN_ERR_INVALID_ARGUMENT).  All
+ * calls on one device share its array: calls that overlap in time on one
+ * device (other streams, other threads) race and must not be made; calls
+ * in one stream's order are safe (nothing in the array needs to start at
+ * zero: every byte a kernel reads was written earlier in the same call). */
+gdn_status gdn_prefill_noalloc(const gdn_layer* layer, const gdn_prefill_io* io,
+                               void* stream);
+
 /* Number of kernels gdn_prefill enqueues for these sizes and this
  * workspace size, in order: per window prep (chunk-parallel operands; the
  * first one also builds the chunk table) and scan (sequential state
