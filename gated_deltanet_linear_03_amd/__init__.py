@@ -34,7 +34,8 @@ EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_step", "gdn_snapshot_bytes", "gdn_snapshot_save", "gdn_snapshot_inspect",
            "gdn_snapshot_restore", "gdn_gemm_bf16", "gdn_layer_prefill_workspace_bytes",
            "gdn_layer_prefill", "gdn_layer_decode_workspace_bytes", "gdn_layer_decode",
-           "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma", "gdn_prefill_noalloc")
+           "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma", "gdn_prefill_noalloc",
+           "gdn_prefill_window_slots")
 NOALLOC_SCRATCH_BYTES = 128 << 20       # GDN_NOALLOC_SCRATCH_BYTES
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
@@ -149,7 +150,10 @@ def lib():
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.gdn_prefill_launches.restype = ctypes.c_int64
         L.gdn_prefill_launches.argtypes = [ctypes.POINTER(CLayer), ctypes.c_int32,
-                                           ctypes.c_int64, ctypes.c_size_t]
+                                           ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32]
+        L.gdn_prefill_window_slots.restype = ctypes.c_int64
+        L.gdn_prefill_window_slots.argtypes = [ctypes.POINTER(CLayer), ctypes.c_int32,
+                                               ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32]
         L.gdn_prefill_timed.restype = ctypes.c_int
         L.gdn_prefill_timed.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -348,17 +352,34 @@ def prefill_workspace_bytes(layer: Layer, N: int, T_total: int) -> int:
     return int(n)
 
 
-def prefill_launches(layer: Layer, N: int, T_total: int, workspace_bytes: int | None = None):
+def prefill_launches(layer: Layer, N: int, T_total: int, workspace_bytes: int | None = None,
+                     with_core_out: bool = False):
     """Names of the kernels gdn_prefill enqueues, in order, for these sizes
-    and workspace size (default: gdn_prefill_workspace_bytes): prep and
-    scan per window of chunks, then epi."""
+    and workspace size (default: gdn_prefill_workspace_bytes), with or
+    without core_out: prep and scan per window of chunks, then epi."""
     if workspace_bytes is None:
         workspace_bytes = prefill_workspace_bytes(layer, N, T_total)
     cl = layer.c()
-    n = lib().gdn_prefill_launches(ctypes.byref(cl), int(N), int(T_total), int(workspace_bytes))
+    n = lib().gdn_prefill_launches(ctypes.byref(cl), int(N), int(T_total), int(workspace_bytes),
+                                   int(bool(with_core_out)))
     if n < 0:
         raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
     return ["prep", "scan"] * ((n - 1) // 2) + ["epi"]
+
+
+def prefill_window_slots(layer: Layer, N: int, T_total: int, workspace_bytes: int | None = None,
+                         with_core_out: bool = False) -> int:
+    """Chunk slots per window gdn_prefill runs with for these sizes and
+    workspace size (default: gdn_prefill_workspace_bytes), with or without
+    core_out."""
+    if workspace_bytes is None:
+        workspace_bytes = prefill_workspace_bytes(layer, N, T_total)
+    cl = layer.c()
+    n = lib().gdn_prefill_window_slots(ctypes.byref(cl), int(N), int(T_total), int(workspace_bytes),
+                                       int(bool(with_core_out)))
+    if n < 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return int(n)
 
 
 def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,

@@ -319,18 +319,31 @@ gdn_status gdn_prefill_noalloc(const gdn_layer* L, const gdn_prefill_io* io, voi
     return st;
 }
 
-int64_t gdn_prefill_launches(const gdn_layer* L, int32_t N, int64_t T, size_t ws_bytes) {
+// The layout gdn_prefill fits into a workspace of ws_bytes (which depends
+// only on its size, not on where it is), or -1.
+static int64_t planned_layout(const gdn_layer* L, int32_t N, int64_t T, size_t ws_bytes, int32_t with_core,
+                              WsLayout* w) {
     g_err[0] = 0;
     if (check_layer(L, true) != GDN_OK) return -1;
     if (N < 0 || T < 0) {
         fail(GDN_ERR_INVALID_ARGUMENT, "N and T_total must be >= 0");
         return -1;
     }
-    // the fit does not depend on where the workspace is, only on its size
-    WsLayout w;
     static const uint8_t probe[256] __attribute__((aligned(256))) = {0};
-    if (fit_workspace(L, N, T, true, probe, ws_bytes, &w) != GDN_OK) return -1;
+    if (fit_workspace(L, N, T, with_core == 0, probe, ws_bytes, w) != GDN_OK) return -1;
+    return 0;
+}
+
+int64_t gdn_prefill_launches(const gdn_layer* L, int32_t N, int64_t T, size_t ws_bytes, int32_t with_core) {
+    WsLayout w;
+    if (planned_layout(L, N, T, ws_bytes, with_core, &w) < 0) return -1;
     return gdn::prefill_launches(w.max_chunks, w.win_slots);
+}
+
+int64_t gdn_prefill_window_slots(const gdn_layer* L, int32_t N, int64_t T, size_t ws_bytes, int32_t with_core) {
+    WsLayout w;
+    if (planned_layout(L, N, T, ws_bytes, with_core, &w) < 0) return -1;
+    return w.win_slots;
 }
 
 gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void* ws,

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef enum {
     GDN_OK = 0,
@@ -192,15 +192,27 @@ gdn_status gdn_prefill_noalloc(const gdn_layer* layer, const gdn_prefill_io* io,
 /* Number of kernels gdn_prefill enqueues for these sizes and this
  * workspace size, in order: per window prep (chunk-parallel operands; the
  * first one also builds the chunk table) and scan (sequential state
- * passing), then epi (gated RMSNorm): 1 + 2 * windows.  -1 on an invalid layer, sizes or a
- * too small workspace (detail in gdn_last_error()). */
+ * passing), then epi (gated RMSNorm): 1 + 2 * windows.  with_core_out:
+ * nonzero if the call passes core_out (the workspace then holds no pre-norm
+ * output, so more chunk slots fit in a given size).  -1 on an invalid
+ * layer, sizes or a too small workspace (detail in gdn_last_error()). */
 int64_t gdn_prefill_launches(const gdn_layer* layer, int32_t N,
-                             int64_t T_total, size_t workspace_bytes);
+                             int64_t T_total, size_t workspace_bytes,
+                             int32_t with_core_out);
+
+/* Chunk slots per window gdn_prefill runs with for these sizes, this
+ * workspace size and with or without core_out (operand blocks of that many
+ * chunks of every value head fit the workspace at once); -1 as for
+ * gdn_prefill_launches. */
+int64_t gdn_prefill_window_slots(const gdn_layer* layer, int32_t N,
+                                 int64_t T_total, size_t workspace_bytes,
+                                 int32_t with_core_out);
 
 /* gdn_prefill that also records caller-created timing events (hipEvent_t
  * handles) on `stream`: events[0] before the first kernel and events[i]
  * after kernel i-1 (numbering as in gdn_prefill_launches), so consecutive
- * events bracket each kernel.  n_events must be gdn_prefill_launches() + 1.
+ * events bracket each kernel.  n_events must be gdn_prefill_launches() + 1
+ * (with with_core_out set as io->core_out is given).
  * Same results as gdn_prefill; meant for per-kernel timing. */
 gdn_status gdn_prefill_timed(const gdn_layer* layer, const gdn_prefill_io* io,
                              void* workspace, size_t workspace_bytes,

@@ -52,25 +52,22 @@ def chunk_slot_bytes(Hv, dk, dv, C):
     return Hv * (2 * C * dk + 4 * C * dk + 2 * dk * CK + 4 * C * CK + 4 * C * dv)
 
 
-def default_window_slots(layer, N, T):
-    """Chunk slots per window gdn_prefill uses with a full workspace: as many
-    as ~144 MiB of operand blocks hold for one sequence (4 GiB for several),
-    evened out over the windows that takes."""
-    slot = chunk_slot_bytes(layer.Hv, layer.dk, layer.dv, layer.chunk)
-    target = (144 << 20) if N == 1 else (4 << 30)
-    mc = max((T + N * (layer.chunk - 1)) // layer.chunk, 1)
-    w = min(max(1, target // slot), mc)
-    nwin = -(-mc // w)
-    return -(-mc // nwin)
-
-
-def workspace_for_window(layer, N, T, window_slots):
+def workspace_for_window(layer, N, T, window_slots, with_core_out=True):
     """Workspace bytes that make gdn_prefill run windows of window_slots
-    chunk slots (fewer, if that is more than the default)."""
+    chunk slots (fewer, if that is more than the default), asking the
+    library for the window each size gives: the default workspace less the
+    slots beyond those, less more slots while the call's window (with core_out,
+    the pre-norm output's share of the workspace is free for slots) is still
+    wider."""
     slot = chunk_slot_bytes(layer.Hv, layer.dk, layer.dv, layer.chunk)
     full = gdn.prefill_workspace_bytes(layer, N, T)
-    default = default_window_slots(layer, N, T)
-    return full - (default - min(window_slots, default)) * slot
+    default = gdn.prefill_window_slots(layer, N, T, full)
+    want = min(window_slots, default)
+    nb = full - (default - want) * slot
+    while gdn.prefill_window_slots(layer, N, T, nb, with_core_out) > want:
+        nb -= slot
+    assert gdn.prefill_window_slots(layer, N, T, nb, with_core_out) == want
+    return nb
 
 
 def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=False,
@@ -87,7 +84,7 @@ def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=Fal
     ws = None
     if window_slots is not None:
         N, T = len(case.cu_seqlens) - 1, int(case.cu_seqlens[-1])
-        ws = torch.empty(workspace_for_window(layer, N, T, window_slots), dtype=torch.uint8,
+        ws = torch.empty(workspace_for_window(layer, N, T, window_slots, want_core), dtype=torch.uint8,
                          device="cuda")
     res = gdn.prefill(layer, x["q"], x["k"], x["v"], x["z"], x["a"], x["b"], cu,
                       initial_state=S0, conv_state_in=C0, want_core=want_core,

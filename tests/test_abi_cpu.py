@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 8
+    assert L.gdn_abi_version() == 9
 
 
 def test_status_strings():
@@ -290,8 +290,37 @@ def test_prefill_windows_follow_the_workspace():
     # the smallest workspace holds one slot: a window per chunk slot
     floor = nb - (win - 1) * slot
     assert len(gdn.prefill_launches(lay, 1, T, floor)) == 1 + 2 * n_chunks
+    assert gdn.prefill_window_slots(lay, 1, T, floor) == 1
     with pytest.raises(gdn.GdnError):
         gdn.prefill_launches(lay, 1, T, floor - 256)
+    # with core_out the pre-norm output needs no workspace: the same size
+    # then holds that many more chunk slots
+    pre_norm = T * 32 * 128 * 4
+    extra = pre_norm // slot
+    assert gdn.prefill_window_slots(lay, 1, T, floor, with_core_out=True) == 1 + extra
+    assert (len(gdn.prefill_launches(lay, 1, T, floor, with_core_out=True))
+            == 1 + 2 * -(-n_chunks // (1 + extra)))
+    with pytest.raises(gdn.GdnError):
+        gdn.prefill_launches(lay, 1, T, floor - pre_norm - 256, with_core_out=True)
+    assert len(gdn.prefill_launches(lay, 1, T, floor - pre_norm, with_core_out=True)) == 1 + 2 * n_chunks
+    # gdn_prefill_timed expects the count for the call as made: with core_out
+    # at this size, the with-core_out count (NULL handles: refused before
+    # any launch), not the one without
+    t = _fake_act(FAKE, 16 * 128)
+    kw = dict(N=1, T_total=T, cu_seqlens=_FakeTensor(FAKE), q=t, k=t,
+              v=_fake_act(FAKE, 32 * 128), z=_fake_act(FAKE, 32 * 128),
+              a=_fake_act(FAKE, 32), b=_fake_act(FAKE, 32), out=_FakeTensor(FAKE, 32 * 128),
+              core_out=_FakeTensor(FAKE + (1 << 30), 32 * 128), stream=_FakeStream(),
+              workspace=_FakeTensor(FAKE, numel=floor, esize=1))
+    n_core = len(gdn.prefill_launches(lay, 1, T, floor, with_core_out=True)) + 1
+    n_plain = len(gdn.prefill_launches(lay, 1, T, floor)) + 1
+    assert n_core < n_plain
+    with pytest.raises(gdn.GdnError):
+        gdn.prefill_raw(lay, events=[_FakeEvent()] * n_plain, **kw)
+    assert b"timing events" in gdn.lib().gdn_last_error()
+    with pytest.raises(gdn.GdnError):
+        gdn.prefill_raw(lay, events=[_FakeEvent()] * n_core, **kw)
+    assert b"is NULL" in gdn.lib().gdn_last_error()
 
 
 def test_decode_multi_rejects_token_counts():

@@ -77,7 +77,7 @@ def test_prefill_through_a_pool_bitwise(window_slots):
     T = int(case.cu_seqlens[-1])
     idx = torch.tensor(slots, device="cuda")
     ws_bytes = (gdn.prefill_workspace_bytes(layer, N, T) if window_slots is None
-                else workspace_for_window(layer, N, T, window_slots))
+                else workspace_for_window(layer, N, T, window_slots, with_core_out=False))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     dense = gdn.prefill(layer, *(x[n] for n in "qkvzab"), cu, initial_state=pst[idx].clone(),
                         conv_state_in=pcs[idx].clone(), want_core=True, workspace=ws)
