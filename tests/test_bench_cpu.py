@@ -39,3 +39,26 @@ def test_decode_bytes_per_sequence():
     assert state == 2 * 32 * 128 * 128 * 4 == 4_194_304
     assert total == state + 2 * 3 * 8192 * 2 + (2 * 2048 + 2 * 4096 + 64) * 2 + 4096 * 4
     assert total == 4_333_696
+
+
+def test_prefill_bytes_per_token():
+    """Compulsory bytes per token at the 16/32-head, 128/128 shape with bf16
+    inputs and fp32 out: prep reads q, k (2 x 16 x 128), v (32 x 128), a and
+    b (2 x 32) bf16 values; the epilogue reads z (32 x 128 bf16) and writes
+    out (32 x 128 fp32); the path is both."""
+    b = bench.prefill_bytes_per_token(16, 32, 128, 128)
+    assert b["prep"] == (2 * 16 * 128 + 32 * 128 + 2 * 32) * 2 == 16_512
+    assert b["epi"] == 32 * 128 * (2 + 4) == 24_576
+    assert b["path"] == 41_088
+
+
+def test_binding_roofline_takes_the_larger_ceiling():
+    # 1 GFLOP and 8 MB in 1 ms: the matrix cores need 0.4 us, HBM 1 us
+    r = bench.binding_roofline(1e9, 8e6, 1e-3)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["achieved"] == pytest.approx(8.0) and r["frac"] == pytest.approx(1e-3)
+    assert r["ceiling_ms"] == pytest.approx(1e-3)
+    # 100 GFLOP and 8 MB in 1 ms: the matrix cores need 40 us
+    r = bench.binding_roofline(1e11, 8e6, 1e-3)
+    assert r["bound"] == "mfma" and r["achieved"] == pytest.approx(100.0)
+    assert r["frac"] == pytest.approx(0.04)
