@@ -113,7 +113,10 @@ typedef struct {
     void* conv_state_out;
     void* out;                     /* out_dtype */
     float* core_out;               /* optional */
-    /* optional state pool: device int32 [N], distinct entries in
+    /* optional state pool (a serving engine's bank of per-sequence states,
+     * batched across whichever sequences are ready: llmxabe README,
+     * "Status", batched prefill and decode across parallel sequences):
+     * device int32 [N], distinct entries in
      * [0, num_slots); sequence n's recurrent and conv states are then entry
      * state_slots[n] of initial_state / final_state ([num_slots][Hv][dk][dv])
      * and of conv_state_in / conv_state_out ([num_slots][K-1][Cc]).  NULL:
@@ -222,7 +225,9 @@ gdn_status gdn_prefill_timed(const gdn_layer* layer, const gdn_prefill_io* io,
 gdn_status gdn_decode(const gdn_layer* layer, const gdn_decode_io* io,
                       void* stream);
 
-/* One serving step of a layer over a state pool: the decode batch (one
+/* One serving step of a layer over a state pool (the llmxabe README,
+ * "Status": prefill and decode batched across parallel sequences in one
+ * engine step): the decode batch (one
  * token per sequence; NULL or B = 0 for none) and the prefill batch (NULL or
  * N = 0 for none), each as its own call describes, enqueued on `stream`
  * decode first.  The two batches' sequences must use distinct pool entries
