@@ -57,6 +57,8 @@ def parse(argv=None):
                     help="only this extra workload, no headline and no JSON line (for profiling)")
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--decode-batches", default="64,3,1")
+    ap.add_argument("--decode-compare", action="store_true",
+                    help="also time decode without a workspace (the one-work-group kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="about this much oracle work for the all-threads CPU baseline")
@@ -443,7 +445,13 @@ def main(argv=None):
         dec = {}
         per_seq, state_per_seq = decode_bytes_per_seq(sh.Hk, sh.Hv, sh.dk, sh.dv)
         DK = 20
-        for B in [int(b) for b in args.decode_batches.split(",")]:
+        dws = gdn.decode_workspace(layers[0], Bmax)     # zero-filled once, shared by the layers
+
+        def decode_variant(B, ws):
+            """Eager and graph-replayed 30-layer steps and the kernel time per
+            layer, with the decode workspace `ws` (the library then picks the
+            column-split kernel for small batches) or without (one
+            work-group per sequence and key head)."""
             outs = [torch.empty((B, sh.Hv, sh.dv), dtype=torch.float32, device=dev) for _ in range(L)]
 
             def dstep(events=None):
@@ -454,7 +462,7 @@ def main(argv=None):
                     gdn.decode_raw(layers[l], B=B, q=t["q"][:B], k=t["k"][:B], v=t["v"][:B],
                                    z=t["z"][:B], a=t["a"][:B], b=t["b"][:B], out=outs[l],
                                    state_in=states[l][:B], state_out=states[l][:B],
-                                   conv_state_in=convs[l][:B], conv_state_out=convs[l][:B])
+                                   conv_state_in=convs[l][:B], conv_state_out=convs[l][:B], workspace=ws)
                     if events is not None:
                         events[l][1].record(stream)
             for _ in range(5):
@@ -475,14 +483,6 @@ def main(argv=None):
                 dstep(devs[i])
             torch.cuda.synchronize()
             kms = sum(devs[i][l][0].elapsed_time(devs[i][l][1]) for i in range(DK) for l in range(L)) / (DK * L)
-            kern_gbs = B * per_seq / (kms * 1e-3) / 1e9
-            dec[f"B{B}"] = {"layers": L, "eager_ms_per_step": eager_ms,
-                            "eager_state_GBps": L * B * state_per_seq / (eager_ms * 1e-3) / 1e9,
-                            "kernel_avg_ms": kms,
-                            "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
-                                         "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
-                                         "traffic": measured_traffic(f"decode_b{B}/decode"),
-                                         "bytes_per_launch": B * per_seq}}
             # the same 30-layer step replayed from a HIP graph (launch gaps
             # removed; the states keep advancing exactly as eager steps do)
             g = torch.cuda.CUDAGraph()
@@ -502,6 +502,19 @@ def main(argv=None):
             g1.record(stream)
             torch.cuda.synchronize()
             gms = g0.elapsed_time(g1) / DK
+            del g
+            return eager_ms, kms, gms
+
+        for B in [int(b) for b in args.decode_batches.split(",")]:
+            eager_ms, kms, gms = decode_variant(B, dws)
+            kern_gbs = B * per_seq / (kms * 1e-3) / 1e9
+            dec[f"B{B}"] = {"layers": L, "eager_ms_per_step": eager_ms,
+                            "eager_state_GBps": L * B * state_per_seq / (eager_ms * 1e-3) / 1e9,
+                            "kernel_avg_ms": kms,
+                            "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
+                                         "traffic": measured_traffic(f"decode_b{B}/decode"),
+                                         "bytes_per_launch": B * per_seq}}
             # the step as a serving loop runs it, replayed from a graph: the
             # headline decode figures (the eager loop above also pays the
             # Python binding's per-call cost, which B = 64 no longer hides)
@@ -509,9 +522,14 @@ def main(argv=None):
             dec[f"B{B}"].update({"ms_per_step": gms, "state_GBps": state_gbs,
                                  "all_bytes_GBps": L * B * per_seq / (gms * 1e-3) / 1e9,
                                  "state_frac_hbm": state_gbs / PEAK_HBM_GBS})
-            del g
             log(f"decode B={B}: {gms:.3f} ms/step from a graph ({eager_ms:.3f} eager), state "
                 f"{state_gbs:.1f} GB/s, kernel {kms * 1e3:.1f} us = {kern_gbs:.1f} GB/s")
+            if args.decode_compare:
+                e2, k2, g2 = decode_variant(B, None)
+                dec[f"B{B}"]["without_workspace"] = {"ms_per_step": g2, "eager_ms_per_step": e2,
+                                                     "kernel_avg_ms": k2}
+                log(f"  without a workspace (one work-group per key head): {g2:.3f} ms/step from a graph, "
+                    f"kernel {k2 * 1e3:.1f} us")
         result["decode"] = dec
 
         # multi-token verify: VB sequences x VT draft tokens x the same layers

@@ -35,7 +35,7 @@ EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_snapshot_restore", "gdn_gemm_bf16", "gdn_layer_prefill_workspace_bytes",
            "gdn_layer_prefill", "gdn_layer_decode_workspace_bytes", "gdn_layer_decode",
            "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma", "gdn_prefill_noalloc",
-           "gdn_prefill_window_slots")
+           "gdn_prefill_window_slots", "gdn_decode_workspace_bytes")
 NOALLOC_SCRATCH_BYTES = 128 << 20       # GDN_NOALLOC_SCRATCH_BYTES
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
@@ -115,7 +115,8 @@ class CDecodeIO(ctypes.Structure):
                  ("conv_state_in", ctypes.c_void_p),
                  ("conv_state_out", ctypes.c_void_p),
                  ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p),
-                 ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32)])
+                 ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)])
 
 
 _lib = None
@@ -158,6 +159,8 @@ def lib():
         L.gdn_prefill_timed.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CPrefillIO),
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        L.gdn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_decode_workspace_bytes.argtypes = [ctypes.POINTER(CLayer), ctypes.c_int32]
         L.gdn_decode.restype = ctypes.c_int
         L.gdn_decode.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CDecodeIO),
                                  ctypes.c_void_p]
@@ -399,16 +402,17 @@ def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, 
 
 
 def _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
-               conv_state_out, state_slots, num_slots, tokens=1):
+               conv_state_out, state_slots, num_slots, tokens=1, workspace=None):
     _check_tokens(layer, int(B) * int(tokens), q, k, v, z, a, b, out, core_out)
     _check_index(state_slots, "state_slots", int(B))
     _check_states(layer, int(num_slots) if state_slots is not None else int(B), state_in,
                   state_out, conv_state_in, conv_state_out)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return CDecodeIO(int(B), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b),
                      _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
                      _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
                      _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
-                     _ptr(core_out), _ptr(state_slots), int(num_slots))
+                     _ptr(core_out), _ptr(state_slots), int(num_slots), _ptr(workspace), int(wsb))
 
 
 def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
@@ -485,14 +489,31 @@ def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,
     return res
 
 
+def decode_workspace_bytes(layer: Layer, B: int) -> int:
+    """Bytes of a ``gdn_decode`` workspace for up to B sequences."""
+    n = lib().gdn_decode_workspace_bytes(ctypes.byref(layer.c()), int(B))
+    if n == 0:
+        raise GdnError(GDN_ERR_INVALID_ARGUMENT, lib().gdn_last_error().decode())
+    return int(n)
+
+
+def decode_workspace(layer: Layer, B: int, device="cuda"):
+    """A zero-filled ``gdn_decode`` workspace for up to B sequences (every
+    call leaves it zero-filled where it must be)."""
+    import torch
+    return torch.zeros(decode_workspace_bytes(layer, B), dtype=torch.uint8, device=device)
+
+
 def decode_raw(layer: Layer, *, B, q, k, v, z, a, b, out, state_in, state_out,
                conv_state_in, conv_state_out, core_out=None, stream=None, state_slots=None,
-               num_slots=0):
+               num_slots=0, workspace=None):
     """Call ``gdn_decode`` on caller-provided buffers (no allocation).  With
-    state_slots (device int32 [B]) the states are pools of num_slots entries."""
+    state_slots (device int32 [B]) the states are pools of num_slots entries;
+    with a workspace (``decode_workspace``) a small batch takes the
+    column-split kernel (same bits)."""
     cl = layer.c()
     io = _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
-                    conv_state_out, state_slots, num_slots)
+                    conv_state_out, state_slots, num_slots, workspace=workspace)
     _check(lib().gdn_decode(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
 
 
@@ -511,11 +532,12 @@ def step_raw(layer: Layer, *, prefill=None, decode=None, workspace=None, workspa
                           f["final_state"], f["conv_state_in"], f["conv_state_out"],
                           f["state_slots"], f["num_slots"])
     if decode is not None:
-        f = dict(core_out=None, state_slots=None, num_slots=0)
+        f = dict(core_out=None, state_slots=None, num_slots=0, workspace=None)
         f.update(decode)
         dio = _decode_io(layer, f["B"], f["q"], f["k"], f["v"], f["z"], f["a"], f["b"], f["out"],
                          f["core_out"], f["state_in"], f["state_out"], f["conv_state_in"],
-                         f["conv_state_out"], f["state_slots"], f["num_slots"])
+                         f["conv_state_out"], f["state_slots"], f["num_slots"],
+                         workspace=f["workspace"])
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_step(ctypes.byref(cl), ctypes.byref(pio) if pio is not None else None,
@@ -568,7 +590,7 @@ def decode_multi(layer: Layer, q, k, v, z, a, b, state, conv_state, tokens, in_p
 
 
 def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
-           want_core=False, stream=None):
+           want_core=False, stream=None, workspace=None):
     """One token per sequence: q, k [B, Hk, dk]; v, z [B, Hv, dv]; a, b
     [B, Hv]; state [B, Hv, dk, dv] fp32; conv_state [B, 3, Cc].  Updates
     the states in place by default.  Returns a dict like ``prefill``."""
@@ -581,7 +603,7 @@ def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
     co = conv_state if in_place else torch.empty_like(conv_state)
     decode_raw(layer, B=B, q=q, k=k, v=v, z=z, a=a, b=b, out=out, state_in=state,
                state_out=so, conv_state_in=conv_state, conv_state_out=co,
-               core_out=core, stream=stream)
+               core_out=core, stream=stream, workspace=workspace)
     res = {"out": out, "final_state": so, "conv_state_out": co}
     if want_core:
         res["core_out"] = core

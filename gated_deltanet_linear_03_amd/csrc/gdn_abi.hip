@@ -364,6 +364,30 @@ gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void*
 }
 
 
+// The decode workspace: the arrival counters [B][Hk] uint32 of the
+// one-work-group-per-value-head kernel, rounded up to 256 bytes.  Counter
+// (b, hk) sits at the same place for every B, so a workspace sized for B
+// serves every smaller batch.
+static size_t decode_ws_bytes(const gdn_layer* L, int32_t B) {
+    return (size_t(B) * L->Hk * 4 + 255) / 256 * 256;
+}
+// One work-group per value head spreads a small batch's state stream over
+// twice the compute units; both kernels give the same bits, so the choice
+// is free.
+static bool head_wg_pays(const gdn_layer* L, int32_t B) {
+    return static_cast<int64_t>(B) * L->Hk <= gdn::kDecodeHeadWgMaxGroups;
+}
+
+size_t gdn_decode_workspace_bytes(const gdn_layer* L, int32_t B) {
+    g_err[0] = 0;
+    if (check_layer(L, false) != GDN_OK) return 0;
+    if (B < 0) {
+        fail(GDN_ERR_INVALID_ARGUMENT, "B (%d) must be >= 0", B);
+        return 0;
+    }
+    return B == 0 ? 256 : decode_ws_bytes(L, B);
+}
+
 // Ts = 0: one token per sequence (gdn_decode); Ts >= 1: the multi-token kernel.
 static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32_t Ts, float* snap,
                               void* stream, bool launch = true) {
@@ -413,6 +437,23 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
                               io->conv_state_in, io->conv_state_out, conv_bytes))
             return fail(GDN_ERR_INVALID_ARGUMENT, "out or core_out overlaps a state");
     }
+    const size_t dws_need = decode_ws_bytes(L, B);
+    const bool head_wg = Ts == 0 && io->workspace != nullptr && head_wg_pays(L, B);
+    if (Ts == 0 && io->workspace) {
+        if (!aligned(io->workspace, 256))
+            return fail(GDN_ERR_WORKSPACE, "decode workspace must be 256-byte aligned");
+        if (io->workspace_bytes < dws_need)
+            return fail(GDN_ERR_WORKSPACE, "decode workspace of %zu bytes, B = %d needs %zu", io->workspace_bytes,
+                        B, dws_need);
+        const size_t ob = size_t(B) * Hv * dv * (L->out_dtype == GDN_DTYPE_BF16 ? 2 : 4);
+        if (overlaps(io->workspace, io->workspace_bytes, io->state_in, state_bytes) ||
+            overlaps(io->workspace, io->workspace_bytes, io->state_out, state_bytes) ||
+            overlaps(io->workspace, io->workspace_bytes, io->conv_state_in, conv_bytes) ||
+            overlaps(io->workspace, io->workspace_bytes, io->conv_state_out, conv_bytes) ||
+            overlaps(io->workspace, io->workspace_bytes, io->out, ob) ||
+            overlaps(io->workspace, io->workspace_bytes, io->core_out, size_t(B) * Hv * dv * 4))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "decode workspace overlaps a state or an output");
+    }
     if (snap) {
         const size_t snap_bytes = size_t(B) * Ts * Hv * dk * dv * 4;
         if (!aligned(snap, 16)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_snapshots must be 16-byte aligned");
@@ -432,6 +473,7 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
     p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16; p.core_out = io->core_out;
     p.Ts = Ts; p.snap = snap;     // Ts = 0: the one-token kernel
     p.slots = io->state_slots;
+    if (head_wg) p.arrive = static_cast<uint32_t*>(io->workspace);
     if (!launch) return GDN_OK;
     bool supported = false;
     hipError_t e = gdn::launch_decode(dk, dv, L->act_dtype == GDN_DTYPE_BF16, p,
@@ -454,6 +496,8 @@ gdn_status gdn_step(const gdn_layer* L, const gdn_prefill_io* prefill, const gdn
     gdn_status st = GDN_OK;
     if (has_d && (st = decode_impl(L, decode, 0, nullptr, stream, false)) != GDN_OK) return st;
     if (has_p && (st = prefill_impl(L, prefill, ws, ws_bytes, stream, nullptr, false)) != GDN_OK) return st;
+    if (has_d && has_p && decode->workspace && overlaps(decode->workspace, decode->workspace_bytes, ws, ws_bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "the decode and prefill workspaces overlap");
     if (has_d && (st = decode_impl(L, decode, 0, nullptr, stream)) != GDN_OK) return st;
     if (has_p && (st = prefill_impl(L, prefill, ws, ws_bytes, stream, nullptr)) != GDN_OK) return st;
     return GDN_OK;

@@ -81,11 +81,15 @@ __device__ __forceinline__ float conv4_silu(const f32x4& w, float t0, float t1, 
 // sums entries l, l + 64, ... in order, then the wave sum (every lane of the
 // wave takes part)
 template <int DK>
-__device__ __forceinline__ float l2_scale(const float* src, int lane, float num, float eps) {
+__device__ __forceinline__ float l2_sumsq(const float* src, int lane) {
     float ss = 0.f;
     for (int i = lane; i < DK; i += kWave) ss = fmaf(src[i], src[i], ss);
-    ss = wave_sum(ss);
-    return num / sqrtf(ss + eps);
+    return ss;
+}
+__device__ __forceinline__ float l2_finish(float ss, float num, float eps) { return num / sqrtf(ss + eps); }
+template <int DK>
+__device__ __forceinline__ float l2_scale(const float* src, int lane, float num, float eps) {
+    return l2_finish(wave_sum(l2_sumsq<DK>(src, lane)), num, eps);
 }
 
 // k^ . q^ over DK values in LDS, in the same lane order
@@ -96,27 +100,56 @@ __device__ __forceinline__ float dot_wave(const float* a, const float* b, int la
     return wave_sum(d);
 }
 
-template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams p) {
+// One-token step.  A work-group holds HPW value heads of one key head (256
+// threads per value head):
+//   HPW = 2  one work-group per (sequence, key head); the key head's value
+//            heads two at a time.  It alone reads and rewrites the key head's
+//            q/k conv channels.
+//   HPW = 1  one work-group per (sequence, value head), so a small batch
+//            spreads its state stream over twice as many compute units.  The
+//            G work-groups of a key head all read its q/k conv history; the
+//            last of them to count itself in on a per-(sequence, key head)
+//            arrival counter (decode workspace) writes the new history and
+//            puts the counter back to zero.  Nothing waits on another
+//            work-group, and no result passes between them.
+// Both compute each value head with the same operations in the same order,
+// so they give the same bits.  With HPW = 1 the conv and gate inputs are
+// loaded before the state stream (loads complete in issue order), so the
+// conv, the gates and the L2 norms run while the state arrives.
+template <int DK, int DV, bool BF16, int HPW>
+__global__ __launch_bounds__(HPW * kDecodeHalf, 4) void decode_kernel(DecodeParams p) {
     using A = Act<BF16>;
     using T = typename A::T;
     constexpr int NT = kDecodeHalf;
+    constexpr int NTH = HPW * NT;
     constexpr int CG = DV / 4;          // float4 column groups
     constexpr int RG = NT / CG;         // row groups
     constexpr int RPT = DK / RG;        // rows per thread
     static_assert(CG <= 64 && NT % CG == 0 && DK % RG == 0 && RPT >= 1, "shape");
-    static_assert(2 * DK <= kDecodeThreads, "one thread per q/k channel");
+    static_assert(HPW == 1 || HPW == 2, "one or two value heads per work-group");
 
-    __shared__ float sq[DK], sk[DK], sv[2][DV], sz[2][DV];
-    __shared__ f32x4 red_k[2][RG][CG], red_q[2][RG][CG];
-    __shared__ float s_r[2], s_kq, s_eg[2], s_beta[2];
+    __shared__ float sq[DK], sk[DK], sv[HPW][DV], sz[HPW][DV];
+    __shared__ f32x4 red_k[HPW][RG][CG], red_q[HPW][RG][CG];
+    __shared__ float s_eg[HPW], s_beta[HPW];
+    __shared__ T s_tap[HPW == 1 ? 3 : 1][HPW == 1 ? 2 * DK : 1];   // new q/k history (HPW = 1)
 
-    const int b = blockIdx.x / p.Hk;
-    const int hk = blockIdx.x % p.Hk;
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
+    int b, hk, gfirst, gend;
+    if constexpr (HPW == 1) {
+        b = blockIdx.x / p.Hv;
+        const int h = blockIdx.x % p.Hv;
+        hk = h / p.G;
+        gfirst = h % p.G;
+        gend = gfirst + 1;
+    } else {
+        b = blockIdx.x / p.Hk;
+        hk = blockIdx.x % p.Hk;
+        gfirst = 0;
+        gend = p.G;
+    }
     // value head slot (uniform per wave, so the state base lives in SGPRs)
-    const int half = __builtin_amdgcn_readfirstlane(tid / NT);
+    const int half = HPW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / NT);
     const int t = tid % NT;
     const int Cc = 2 * p.Hk * DK + p.Hv * DV;
     const T* cin = static_cast<const T*>(p.conv_in);
@@ -124,143 +157,177 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
     const int sb = state_slot(p.slots, b);                // pool entry of the states
     const size_t crow = static_cast<size_t>(sb) * 3 * Cc;
 
+    // ---- conv and gate inputs ----
+    // Each thread takes at most one q/k channel (threads [0, 2 DK)) and one
+    // v channel (threads [VOFF, VOFF + HPW DV)).  The loads are issued
+    // unconditionally from clamped indices and the raw values kept until
+    // the conv, so that issuing them never waits on memory; with no conv
+    // history the tap loads read channel 0 of q instead and are zeroed at use.
+    constexpr int VOFF = NTH >= 2 * DK + HPW * DV ? 2 * DK : 0;
+    static_assert(VOFF + HPW * DV <= NTH && 2 * DK <= NTH, "one q/k and one v channel per thread");
+    const bool has_qk = tid < 2 * DK;
+    const int qc = has_qk ? tid : 0;
+    // whether the channel is a k channel: wave-uniform when DK is a multiple
+    // of the wave, so the choice of source is a scalar select
+    const bool isk = DK % kWave == 0 ? __builtin_amdgcn_readfirstlane(qc >= DK) != 0 : qc >= DK;
+    const int qi = qc - (isk ? DK : 0);
+    const int c_qk = (isk ? p.Hk * DK : 0) + hk * DK + qi;
+    const T* const hist = cin ? cin : static_cast<const T*>(p.q);
+    // all-ones with a conv history, else zero: tap indices collapse to 0
+    const size_t hmask = cin ? ~size_t(0) : size_t(0);
+    T xqk, tqk0, tqk1, tqk2, xv, tv0, tv1, tv2, zv, av, bv;
+    f32x4 wqk, wv;
+    float alog, dtb;
+    auto conv_loads = [&](int g0, bool with_qk) {
+        if (with_qk) {
+            const T* src = isk ? static_cast<const T*>(p.k) + b * p.ks : static_cast<const T*>(p.q) + b * p.qs;
+            xqk = src[hk * DK + qi];
+            tqk0 = hist[(crow + c_qk) & hmask];
+            tqk1 = hist[(crow + Cc + c_qk) & hmask];
+            tqk2 = hist[(crow + 2 * Cc + c_qk) & hmask];
+            wqk = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c_qk) * 4);
+        }
+        const int vc = min(max(tid - VOFF, 0), HPW * DV - 1);
+        const int vh = vc / DV, j = vc % DV;
+        const int h = hk * p.G + (g0 + vh < gend ? g0 + vh : g0);
+        const int c = 2 * p.Hk * DK + h * DV + j;
+        xv = static_cast<const T*>(p.v)[b * p.vs + h * DV + j];
+        tv0 = hist[(crow + c) & hmask];
+        tv1 = hist[(crow + Cc + c) & hmask];
+        tv2 = hist[(crow + 2 * Cc + c) & hmask];
+        wv = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c) * 4);
+        zv = static_cast<const T*>(p.z)[b * p.zs + h * DV + j];
+        av = static_cast<const T*>(p.a)[b * p.as + h];
+        bv = static_cast<const T*>(p.b)[b * p.bs + h];
+        alog = p.A_log[h];
+        dtb = p.dt_bias[h];
+    };
+    // conv + SiLU into LDS, the gates, and the new conv history (q/k
+    // channels: with HPW = 2 here, by their single owner; with HPW = 1 into
+    // LDS, for the last of the key head's work-groups)
+    auto conv_compute = [&](int g0, bool with_qk) {
+        auto ld = [&](const T& x) { return cin ? A::load(&x) : 0.f; };
+        if (with_qk && has_qk) {
+            const float y = conv4_silu(wqk, ld(tqk0), ld(tqk1), ld(tqk2), A::load(&xqk));
+            (isk ? sk : sq)[qi] = y;
+            const T n0 = cin ? tqk1 : T(0), n1 = cin ? tqk2 : T(0);
+            if constexpr (HPW == 1) {
+                s_tap[0][tid] = n0;
+                s_tap[1][tid] = n1;
+                s_tap[2][tid] = xqk;
+            } else {
+                cout[crow + c_qk] = n0;
+                cout[crow + Cc + c_qk] = n1;
+                cout[crow + 2 * Cc + c_qk] = xqk;
+            }
+        }
+        const int vc = tid - VOFF;
+        const int vh = vc / DV, j = vc % DV;
+        if (vc >= 0 && vc < HPW * DV && g0 + vh < gend) {
+            const int h = hk * p.G + g0 + vh;
+            const int c = 2 * p.Hk * DK + h * DV + j;
+            sv[vh][j] = conv4_silu(wv, ld(tv0), ld(tv1), ld(tv2), A::load(&xv));
+            sz[vh][j] = A::load(&zv);
+            if (j == 0) {
+                const float gg = -expf(alog) * softplus(A::load(&av) + dtb);
+                s_eg[vh] = expf(gg);
+                s_beta[vh] = sigmoid(A::load(&bv));
+            }
+            cout[crow + c] = cin ? tv1 : T(0);
+            cout[crow + Cc + c] = cin ? tv2 : T(0);
+            cout[crow + 2 * Cc + c] = xv;
+        }
+    };
+
     // thread (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 of columns 4cg..4cg+3;
-    // one load instruction still covers whole 512-byte rows.  The first pair
-    // of heads' state stream is issued before anything else so its latency
-    // overlaps the conv and the norms.
+    // one load instruction covers whole 512-byte rows
     const int cg = t % CG, rg = t / CG;
     const uint32_t toff = static_cast<uint32_t>(rg * RPT * DV + 4 * cg);
     f32x4 H[RPT];
+    // Unconditional loads (a branch around them would make every later wait
+    // for the conv inputs also wait for the stream): a slot past the last
+    // head reads the pair's first head, and with no initial state the loads
+    // read state_out (same shape; the values are replaced by zeros at use).
     auto load_state = [&](int g0) {
-        const int g = g0 + half;
-        if (g < p.G && p.state_in) {
-            const float* src = p.state_in + (static_cast<size_t>(sb) * p.Hv + hk * p.G + g) * DK * DV;
+        const int g = g0 + half < gend ? g0 + half : g0;
+        const float* src = (p.state_in ? p.state_in : p.state_out) +
+                           (static_cast<size_t>(sb) * p.Hv + hk * p.G + g) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < RPT; ++m)
-                H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + toff + m * DV));
-        } else {
+        for (int m = 0; m < RPT; ++m)
+            H[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + toff + m * DV));
+    };
+
+    if constexpr (HPW == 1) {
+        conv_loads(gfirst, true);
+        __builtin_amdgcn_sched_barrier(0);      // keep the conv inputs ahead of the stream
+        load_state(gfirst);
+    } else {
+        // (two heads' state leaves no registers to hold the conv inputs
+        // across the stream; at the batch sizes this kernel serves the step
+        // is bound by the state stream anyway)
+        load_state(gfirst);
+        conv_loads(gfirst, true);
+    }
+    conv_compute(gfirst, true);
+    __syncthreads();
+    uint32_t* counter = nullptr;
+    uint32_t prev;      // lane 0 of wave 0 only (no default: a merge would force a wait on the atomic)
+    if constexpr (HPW == 1) {
+        // every q/k history load of this work-group has been consumed: count
+        // it in with a wrapping increment (old >= G - 1 stores 0), so the
+        // last arrival also puts the counter back to zero.  Wave 0 uses the
+        // answer only at its end, so waiting for it (loads complete in order)
+        // costs nothing then.
+        counter = p.arrive + static_cast<size_t>(b) * p.Hk + hk;
+        if (tid == 0)
+            prev = __builtin_amdgcn_atomic_inc32(counter, static_cast<uint32_t>(p.G - 1), __ATOMIC_RELAXED, "agent");
+    }
+    // the key head's norms, computed by every wave from the conv outputs:
+    // q^ = s q~ / |q~|, k^ = k~ / |k~| (scaled as they are read) and k^ . q^
+    // (every lane of a wave holds the same bits: kept as wave-uniform
+    // values); the two sums of squares are reduced side by side
+    float ssq = l2_sumsq<DK>(sq, lane), ssk = l2_sumsq<DK>(sk, lane);
+    ssq = wave_sum(ssq);
+    ssk = wave_sum(ssk);
+    const float rq = uniform_f32(l2_finish(ssq, p.scale, p.eps_l2));
+    const float rk = uniform_f32(l2_finish(ssk, 1.0f, p.eps_l2));
+    float kq;
+    {
+        float d = 0.f;
+        for (int i = lane; i < DK; i += kWave) d = fmaf(sk[i] * rk, sq[i] * rq, d);
+        kq = uniform_f32(wave_sum(d));
+    }
+
+    for (int g0 = gfirst; g0 < gend; g0 += HPW) {
+        const int g = g0 + half;
+        const bool active = g < gend;
+        const int h = hk * p.G + g;
+        const size_t hbase = (static_cast<size_t>(sb) * p.Hv + h) * DK * DV;
+        if (g0 != gfirst) {
+            // the next pair of heads (HPW = 2, G > 2): their v channels and
+            // gates, then their state
+            conv_loads(g0, false);
+            load_state(g0);
+            conv_compute(g0, false);
+            __syncthreads();
+        }
+        if (!p.state_in) {
 #pragma unroll
             for (int m = 0; m < RPT; ++m) H[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    };
-    load_state(0);
-
-    // One conv channel per thread, all loads issued before any arithmetic:
-    // threads [0, 2 DK) take the key head's q and k channels, threads
-    // [NT, NT + 2 DV) the v channels of the first pair of value heads (with
-    // their z and, on each head's first thread, the gate inputs a, b).
-    static_assert(DV <= NT, "one thread per v channel of a head pair");
-    {
-        const bool is_qk = tid < 2 * DK;
-        const int vj = tid - NT;
-        const int vg = vj / DV, vjj = vj - vg * DV;
-        const bool is_v = vj >= 0 && vj < 2 * DV && vg < p.G;
-        int c = 0;
-        const T* src = nullptr;
-        const T* zsrc = nullptr;
-        if (is_qk) {
-            const int isk = tid >= DK;
-            const int i = tid - isk * DK;
-            c = isk * p.Hk * DK + hk * DK + i;
-            src = isk ? static_cast<const T*>(p.k) + b * p.ks + hk * DK + i
-                      : static_cast<const T*>(p.q) + b * p.qs + hk * DK + i;
-        } else if (is_v) {
-            const int h = hk * p.G + vg;
-            c = 2 * p.Hk * DK + h * DV + vjj;
-            src = static_cast<const T*>(p.v) + b * p.vs + h * DV + vjj;
-            zsrc = static_cast<const T*>(p.z) + b * p.zs + h * DV + vjj;
-        }
-        if (is_qk || is_v) {
-            const T x = *src;
-            const T t0 = cin ? cin[crow + c] : T(0);
-            const T t1 = cin ? cin[crow + Cc + c] : T(0);
-            const T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
-            const f32x4 w = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c) * 4);
-            float zz = 0.f, av = 0.f, bv = 0.f;
-            const bool gate = is_v && vjj == 0;
-            if (is_v) zz = A::load(zsrc);
-            if (gate) {
-                const int h = hk * p.G + vg;
-                av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
-                bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
-            }
-            const float y = conv4_silu(w, A::load(&t0), A::load(&t1), A::load(&t2), A::load(&x));
-            if (is_qk) {
-                (tid >= DK ? sk : sq)[tid >= DK ? tid - DK : tid] = y;
-            } else {
-                sv[vg][vjj] = y;
-                sz[vg][vjj] = zz;
-            }
-            if (gate) {
-                const int h = hk * p.G + vg;
-                const float gg = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
-                s_eg[vg] = expf(gg);
-                s_beta[vg] = sigmoid(bv);
-            }
-            cout[crow + c] = t1;
-            cout[crow + Cc + c] = t2;
-            cout[crow + 2 * Cc + c] = x;
-        }
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const float r = l2_scale<DK>(wave == 0 ? sq : sk, lane, wave == 0 ? p.scale : 1.0f, p.eps_l2);
-        if (lane == 0) s_r[wave] = r;
-    }
-    __syncthreads();
-    if (tid < 2 * DK) {
-        if (tid < DK) sq[tid] *= s_r[0];
-        else sk[tid - DK] *= s_r[1];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const float d = dot_wave<DK>(sk, sq, lane);
-        if (lane == 0) s_kq = d;
-    }
-
-    for (int g0 = 0; g0 < p.G; g0 += 2) {
-        const int g = g0 + half;
-        const bool active = g < p.G;
-        const int h = hk * p.G + g;
-        const size_t hbase = (static_cast<size_t>(sb) * p.Hv + h) * DK * DV;
-        if (g0 > 0) load_state(g0);
-        // conv + SiLU of this head's v channels, gate inputs (the first pair
-        // was done in the prologue).
-        if (active && g0 > 0) {
-            for (int j = t; j < DV; j += NT) {
-                const int c = 2 * p.Hk * DK + h * DV + j;
-                T x = static_cast<const T*>(p.v)[b * p.vs + h * DV + j];
-                T t0 = cin ? cin[crow + c] : T(0);
-                T t1 = cin ? cin[crow + Cc + c] : T(0);
-                T t2 = cin ? cin[crow + 2 * Cc + c] : T(0);
-                const f32x4 w = *reinterpret_cast<const f32x4*>(p.conv_w + static_cast<size_t>(c) * 4);
-                sv[half][j] = conv4_silu(w, A::load(&t0), A::load(&t1), A::load(&t2), A::load(&x));
-                sz[half][j] = A::load(static_cast<const T*>(p.z) + b * p.zs + h * DV + j);
-                cout[crow + c] = t1;
-                cout[crow + Cc + c] = t2;
-                cout[crow + 2 * Cc + c] = x;
-            }
-            if (t == 0) {
-                const float av = A::load(static_cast<const T*>(p.a) + b * p.as + h);
-                const float bv = A::load(static_cast<const T*>(p.b) + b * p.bs + h);
-                const float gg = -expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
-                s_eg[half] = expf(gg);
-                s_beta[half] = sigmoid(bv);
-            }
-        }
-        f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
+        f32x4 rkv = {0.f, 0.f, 0.f, 0.f}, rqv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg * RPT + m;
-            const float kk = sk[i], qq = sq[i];
+            const float kk = sk[i] * rk, qq = sq[i] * rq;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                rk[e] = fmaf(H[m][e], kk, rk[e]);
-                rq[e] = fmaf(H[m][e], qq, rq[e]);
+                rkv[e] = fmaf(H[m][e], kk, rkv[e]);
+                rqv[e] = fmaf(H[m][e], qq, rqv[e]);
             }
         }
-        red_k[half][rg][cg] = rk;
-        red_q[half][rg][cg] = rq;
+        red_k[half][rg][cg] = rkv;
+        red_q[half][rg][cg] = rqv;
         __syncthreads();
         if (active) {
             f32x4 RK = red_k[half][0][cg], RQ = red_q[half][0][cg];
@@ -270,7 +337,7 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { RK[e] += a[e]; RQ[e] += c[e]; }
             }
-            const float eg = s_eg[half], beta = s_beta[half], kq = s_kq;
+            const float eg = s_eg[half], beta = s_beta[half];
             f32x4 u, o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -280,7 +347,7 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
             float* so = p.state_out + hbase;
 #pragma unroll
             for (int m = 0; m < RPT; ++m) {
-                const float kk = sk[rg * RPT + m];
+                const float kk = sk[rg * RPT + m] * rk;
                 f32x4 hn;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hn[e] = fmaf(eg, H[m][e], kk * u[e]);
@@ -292,7 +359,19 @@ __global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeParams 
                 gated_rmsnorm_store<DV>(t, o, &sz[half][4 * cg], p.norm_w, p.eps_rms, p.out, p.out_bf16,
                                         p.core_out, (static_cast<size_t>(b) * p.Hv + h) * DV + 4 * cg);
         }
-        __syncthreads();   // LDS (sv, sz, red_*) reused by the next pair of heads
+        if constexpr (HPW == 1) {
+            // the last of the key head's work-groups (wave 0 of it) writes
+            // the key head's q/k history
+            if (wave == 0 && __shfl(prev, 0, kWave) + 1 == static_cast<uint32_t>(p.G)) {
+                for (int ch = lane; ch < 2 * DK; ch += kWave) {
+                    const int c = (ch >= DK ? p.Hk * DK - DK : 0) + hk * DK + ch;
+                    cout[crow + c] = s_tap[0][ch];
+                    cout[crow + Cc + c] = s_tap[1][ch];
+                    cout[crow + 2 * Cc + c] = s_tap[2][ch];
+                }
+            }
+        }
+        if (g0 + HPW < gend) __syncthreads();   // LDS (sv, sz, red_*) reused by the next pair of heads
     }
 }
 
@@ -509,11 +588,16 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
 
 template <int DK, int DV, bool BF16>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-    dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.Hk));
-    if (p.Ts == 0)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, BF16>), grid, dim3(kDecodeThreads), 0, s, p);
+    const unsigned B = static_cast<unsigned>(p.B);
+    if (p.Ts != 0)
+        hipLaunchKernelGGL((verify_kernel<DK, DV, BF16>), dim3(B * static_cast<unsigned>(p.Hk)),
+                           dim3(kDecodeThreads), 0, s, p);
+    else if (p.arrive)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, BF16, 1>), dim3(B * static_cast<unsigned>(p.Hv)),
+                           dim3(kDecodeHalf), 0, s, p);
     else
-        hipLaunchKernelGGL((verify_kernel<DK, DV, BF16>), grid, dim3(kDecodeThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<DK, DV, BF16, 2>), dim3(B * static_cast<unsigned>(p.Hk)),
+                           dim3(kDecodeThreads), 0, s, p);
     return hipGetLastError();
 }
 

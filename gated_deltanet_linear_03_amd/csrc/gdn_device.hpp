@@ -212,6 +212,26 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// A value every lane of the wave holds with the same bits, moved to a
+// scalar register
+__device__ __forceinline__ float uniform_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// A pointer every lane of the wave holds, as a wave-uniform integer
+template <typename P>
+__device__ __forceinline__ uintptr_t uniform_ptr(const P* ptr) {
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// s_waitcnt vmcnt(0): every vector memory access this wave has issued,
+// loads and stores alike, has completed (gfx9 encoding: expcnt and lgkmcnt
+// left at their maxima)
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Deterministic wave-wide sum: rows of 16 on DPP swaps, then the four rows
 // through two xor permutes; every lane ends with the same bits.
 __device__ __forceinline__ float wave_sum(float x) {

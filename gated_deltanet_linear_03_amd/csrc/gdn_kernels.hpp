@@ -25,7 +25,16 @@ struct DecodeParams {
     int Ts;                              // 0: one token (decode); else tokens per sequence (rows b*Ts ..)
     float* snap;                         // [B][Ts][Hv][dk][dv] state after each token, or NULL
     const int32_t* slots;                // [B] pool entry of each sequence's states, or NULL (entry b)
+    // one-token step with one work-group per value head (Ts = 0 only):
+    // arrival counters [B][Hk], zero on entry and left zero.  NULL: one
+    // work-group per key head.
+    uint32_t* arrive;
 };
+
+// Most (sequence, key head) pairs for which gdn_decode, given a workspace,
+// runs one work-group per value head (beyond, one per key head streams as
+// fast with half the work-groups)
+constexpr int64_t kDecodeHeadWgMaxGroups = int64_t(1) << 30;
 
 constexpr int kMaxVerifyTokens = 16;     // tokens per sequence of one multi-token decode
 

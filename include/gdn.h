@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 9
+#define GDN_ABI_VERSION 10
 
 typedef enum {
     GDN_OK = 0,
@@ -127,7 +127,21 @@ typedef struct {
 
 /* One token for each of B sequences.  state_out may equal state_in and
  * conv_state_out may equal conv_state_in (in-place); partial overlap is an
- * error.  state_in NULL means zeros; conv_state_in NULL means zero history. */
+ * error.  state_in NULL means zeros; conv_state_in NULL means zero history.
+ *
+ * workspace (optional, gdn_decode and gdn_step only; gdn_decode_multi
+ * ignores it): device memory of at least gdn_decode_workspace_bytes(layer,
+ * B) bytes, 256-byte aligned, that must hold zeros before its first use.
+ * With it, the step runs one work-group per (sequence, value head), which
+ * spreads a small batch's state stream over twice as many compute units;
+ * the work-groups of a key head share its q/k conv history, and the last of
+ * them to count itself in on a per-(sequence, key head) arrival counter in
+ * the workspace writes the new history and puts the counter back to zero.
+ * So every call leaves the workspace at zero (no fill between calls or
+ * graph replays), results are bit-identical to the call without a
+ * workspace, and a workspace serves one call at a time (calls that may run
+ * concurrently need their own).  NULL: one work-group per (sequence, key
+ * head). */
 typedef struct {
     int32_t B;
     const void *q, *k, *v, *z, *a, *b;   /* one token per sequence */
@@ -140,7 +154,14 @@ typedef struct {
     float* core_out;                     /* optional [B][Hv][dv] fp32 */
     const int32_t* state_slots;          /* optional pool entries, as in gdn_prefill_io */
     int32_t num_slots;
+    void* workspace;                     /* optional, see above */
+    size_t workspace_bytes;
 } gdn_decode_io;
+
+/* Bytes of a gdn_decode workspace for up to B sequences: arrival counters
+ * [B][Hk] uint32, rounded up to 256 bytes; 0 on error.  A workspace sized
+ * for B serves any smaller batch. */
+size_t gdn_decode_workspace_bytes(const gdn_layer* layer, int32_t B);
 
 /* Version of this header's structs and layouts. */
 int gdn_abi_version(void);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 9
+    assert L.gdn_abi_version() == 10
 
 
 def test_status_strings():
@@ -155,6 +155,42 @@ def test_outputs_may_not_overlap_a_state():
     io = _pio(out=FAKE + 4096, final_state=FAKE, N=1, T_total=64)
     assert _prefill(_full_layer(), io) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert b"overlaps a state" in gdn.lib().gdn_last_error()
+
+
+def test_decode_workspace_bytes_and_errors():
+    """The decode workspace: arrival counters [B][Hk] uint32 rounded up to
+    256 bytes; a short, misaligned or overlapping workspace is refused
+    before anything runs."""
+    lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE, 4),
+                    A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
+    rnd = lambda n: (n + 255) // 256 * 256
+    for B in (1, 3, 64):
+        assert gdn.decode_workspace_bytes(lay, B) == rnd(4 * B * 16)
+    cl = _full_layer()
+    far = FAKE + (1 << 36)
+    need = gdn.lib().gdn_decode_workspace_bytes(ctypes.byref(cl), 4)
+    assert need == 256
+    base = dict(out=FAKE + (1 << 34), state_in=FAKE, state_out=FAKE, conv_state_in=FAKE + (1 << 30),
+                conv_state_out=FAKE + (1 << 30))
+    for over, status, msg in ((dict(workspace=far, workspace_bytes=need - 4), gdn.GDN_ERR_WORKSPACE, b"needs"),
+                              (dict(workspace=far + 16, workspace_bytes=need), gdn.GDN_ERR_WORKSPACE,
+                               b"aligned"),
+                              (dict(workspace=FAKE + 4096, workspace_bytes=need), gdn.GDN_ERR_INVALID_ARGUMENT,
+                               b"overlaps"),
+                              (dict(workspace=FAKE + (1 << 34), workspace_bytes=need),
+                               gdn.GDN_ERR_INVALID_ARGUMENT, b"overlaps")):
+        st = gdn.lib().gdn_decode(ctypes.byref(cl), ctypes.byref(_dio(**dict(base, **over))), None)
+        assert st == status, over
+        assert msg in gdn.lib().gdn_last_error(), over
+    # gdn_step refuses a decode workspace that shares bytes with the prefill one
+    pio = _pio(N=1, T_total=64)
+    nb = gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(cl), 1, 64)
+    ws = FAKE + (1 << 40)
+    dio = _dio(workspace=ws + 256, workspace_bytes=need, out=far, state_in=FAKE, state_out=FAKE,
+               conv_state_in=FAKE + (1 << 30), conv_state_out=FAKE + (1 << 30))
+    st = gdn.lib().gdn_step(ctypes.byref(cl), ctypes.byref(pio), ctypes.byref(dio), ctypes.c_void_p(ws),
+                            nb, None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT
 
 
 def test_decode_zero_batch_is_a_no_op():
@@ -450,7 +486,8 @@ def test_binding_structs_match_the_header(tmp_path):
                                                   "initial_state", "core_out", "state_slots",
                                                   "num_slots"]),
               "gdn_decode_io": (gdn.CDecodeIO, ["B", "q", "b_stride", "state_in", "core_out",
-                                                "state_slots", "num_slots"]),
+                                                "state_slots", "num_slots", "workspace",
+                                                "workspace_bytes"]),
               "gdn_snapshot_header": (gdn.CSnapshotHeader, ["magic", "version", "Hk", "dv",
                                                             "act_dtype", "state_bytes",
                                                             "checksum", "reserved"]),

@@ -13,7 +13,11 @@ pytestmark = pytest.mark.gpu
 from gpu_helpers import act_dtype, make_layer, to_dev  # noqa: E402
 
 
-def test_decode_graph_replays_match_eager():
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_decode_graph_replays_match_eager(use_ws):
+    """use_ws: the graph's steps run one work-group per value head with one
+    shared decode workspace (its arrival counters reset themselves, so the
+    graph needs no fill node); the eager reference runs without one."""
     sh = synth.FULL
     L, B, reps = 3, 4, 4
     ad = act_dtype(sh)
@@ -24,13 +28,14 @@ def test_decode_graph_replays_match_eager():
     outs = [torch.empty((B, sh.Hv, sh.dv), dtype=torch.float32, device="cuda") for _ in range(L)]
     st = [s.clone() for s in S0]
     cs = [c.clone() for c in C0]
+    ws = gdn.decode_workspace(layers[0], B)
 
-    def step(state, conv):
+    def step(state, conv, workspace=None):
         for l in range(L):
             t = toks[l]
             gdn.decode_raw(layers[l], B=B, q=t["q"], k=t["k"], v=t["v"], z=t["z"], a=t["a"],
                            b=t["b"], out=outs[l], state_in=state[l], state_out=state[l],
-                           conv_state_in=conv[l], conv_state_out=conv[l])
+                           conv_state_in=conv[l], conv_state_out=conv[l], workspace=workspace)
 
     # eager reference: reps successive steps from S0, C0
     ref_st = [s.clone() for s in S0]
@@ -46,7 +51,7 @@ def test_decode_graph_replays_match_eager():
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g, stream=cap):
-            step(st, cs)
+            step(st, cs, ws if use_ws else None)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
     # capturing did not run the step: restart from S0, C0 and replay

@@ -195,27 +195,34 @@ def _decode_case(sh, B, seed):
     return x, S0, C0
 
 
-def _gpu_decode(sh, params, x, S0, C0, in_place=True):
+def _gpu_decode(sh, params, x, S0, C0, in_place=True, workspace=False, want_core=True):
     from gpu_helpers import act_dtype, make_layer
     ad = act_dtype(sh)
     layer = make_layer(sh, params)
     t = {k: to_dev(v, ad) for k, v in x.items()}
     st = to_dev(S0)
     cs = to_dev(C0, ad)
+    ws = gdn.decode_workspace(layer, int(S0.shape[0])) if workspace else None
     res = gdn.decode(layer, t["q"], t["k"], t["v"], t["z"], t["a"], t["b"], st, cs,
-                     in_place=in_place, want_core=True)
+                     in_place=in_place, want_core=want_core, workspace=ws)
     torch.cuda.synchronize()
     return res
 
 
-@pytest.mark.parametrize("shape_name,B", [("full", 3), ("full", 64), ("tiny", 5), ("d64", 4)])
-def test_decode_parity(shape_name, B):
-    """d64: the dk = dv = 64 instantiation, with a non-uniform norm weight."""
+@pytest.mark.parametrize("shape_name,B,workspace", [
+    ("full", 3, False), ("full", 64, False), ("tiny", 5, False), ("d64", 4, False),
+    ("full", 1, True), ("full", 3, True), ("tiny", 5, True), ("d64", 4, True), ("k32v64", 3, True),
+    ("k32v64", 3, False)])
+def test_decode_parity(shape_name, B, workspace):
+    """d64: the dk = dv = 64 instantiation, with a non-uniform norm weight;
+    k32v64: dk = 32 < dv = 64 and three value heads per key head.
+    workspace: one work-group per value head (else one per key head)."""
     sh = {"full": synth.FULL, "tiny": synth.TINY,
-          "d64": synth.LayerShape(Hk=2, Hv=4, dk=64, dv=64, chunk=16, act_dtype="bf16")}[shape_name]
-    params = synth.layer_params(sh, 21, norm_w_jitter=shape_name == "d64")
+          "d64": synth.LayerShape(Hk=2, Hv=4, dk=64, dv=64, chunk=16, act_dtype="bf16"),
+          "k32v64": synth.LayerShape(Hk=2, Hv=6, dk=32, dv=64, chunk=16, act_dtype="bf16")}[shape_name]
+    params = synth.layer_params(sh, 21, norm_w_jitter=shape_name in ("d64", "k32v64"))
     x, S0, C0 = _decode_case(sh, B, 22)
-    res = _gpu_decode(sh, params, x, S0, C0)
+    res = _gpu_decode(sh, params, x, S0, C0, workspace=workspace)
     import oracle
     from gpu_helpers import dims, rel_err
     ref = oracle.gdn_forward(dims(sh), np.arange(B + 1), x["q"], x["k"], x["v"], x["z"],
@@ -227,6 +234,6 @@ def test_decode_parity(shape_name, B):
     e = [max(rel_err(out[b], ref["out"][b]) for b in range(B)),
          max(rel_err(core[b], ref["core_out"][b]) for b in range(B)),
          max(rel_err(st[b], ref["final_state"][b]) for b in range(B))]
-    print(f"decode {shape_name} B={B} out {e[0]:.3e} core {e[1]:.3e} state {e[2]:.3e}")
+    print(f"decode {shape_name} B={B} workspace={workspace} out {e[0]:.3e} core {e[1]:.3e} state {e[2]:.3e}")
     assert max(e) < TOL
     assert np.array_equal(res["conv_state_out"].float().cpu().numpy(), ref["conv_state_out"])

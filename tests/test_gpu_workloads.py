@@ -196,10 +196,9 @@ def test_decode_batch_invariance():
 
 
 def test_decode_small_batch_core_and_bf16_out():
-    """Small batches split each head's columns over several work-groups and
-    finish the norm in a second kernel, carrying o through core_out (bf16
-    out) or out (fp32 out): the same bits as the one-kernel path at B = 64,
-    for out, core_out and both states."""
+    """Sub-batches of 1, 2 and 4 sequences at any batch position give the
+    bits of the whole batch of 64, for out, core_out and both states, with
+    bf16 and with fp32 out."""
     sh = synth.FULL
     params = synth.layer_params(sh, 65)
     ad = act_dtype(sh)
@@ -218,6 +217,62 @@ def test_decode_small_batch_core_and_bf16_out():
             for j, b in enumerate(sel):
                 for key in ("out", "core_out", "final_state", "conv_state_out"):
                     assert _bits_equal(r[key][j], full[key][b]), (out_dtype, sel, key)
+
+
+@pytest.mark.parametrize("out_dtype", [gdn.GDN_DTYPE_FP32, gdn.GDN_DTYPE_BF16])
+def test_decode_head_workgroups_same_bits(out_dtype):
+    """With a decode workspace the step runs one work-group per value head
+    (the last of a key head's work-groups to arrive on its counter writes
+    the shared q/k conv history).  Its results are the bits of one
+    work-group per key head for out, core_out and both states; the arrival
+    counters are back at zero after every call, so one workspace serves call
+    after call, here at B = 64, 3, 1 and 64 again."""
+    sh = synth.FULL
+    params = synth.layer_params(sh, 81)
+    layer = make_layer(sh, params, out_dtype=out_dtype)
+    ad = act_dtype(sh)
+    Bmax = 64
+    t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, Bmax, 82).items()}
+    st = to_dev(synth.initial_states(sh, Bmax, 83))
+    cs = to_dev(synth.conv_states(sh, Bmax, 84), ad)
+    ws = gdn.decode_workspace(layer, Bmax)
+    for B in (64, 3, 1, 64):
+        for want_core in (True, False):
+            ref = _decode(layer, t, st[:B], cs[:B], B=B, want_core=True)
+            r = gdn.decode(layer, *(t[n][:B] for n in "qkvzab"), st[:B], cs[:B], in_place=False,
+                           want_core=want_core, workspace=ws)
+            torch.cuda.synchronize()
+            keys = ("out", "final_state", "conv_state_out") + (("core_out",) if want_core else ())
+            for key in keys:
+                assert _bits_equal(r[key], ref[key]), (B, want_core, key)
+            assert int(ws.count_nonzero()) == 0, (B, want_core)
+
+
+def test_decode_head_workgroups_in_place_pool():
+    """One work-group per value head on a state pool updated in place (the
+    work-groups of a key head all read its q/k conv history before the last
+    one rewrites it): same bits as one work-group per key head on a copy."""
+    sh = synth.FULL
+    params = synth.layer_params(sh, 85)
+    layer = make_layer(sh, params)
+    ad = act_dtype(sh)
+    B, slots = 3, 7
+    t = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, B, 86).items()}
+    pool_s = to_dev(synth.initial_states(sh, slots, 87))
+    pool_c = to_dev(synth.conv_states(sh, slots, 88), ad)
+    idx = torch.tensor([5, 0, 3], dtype=torch.int32, device="cuda")
+    outs = []
+    for use_ws in (False, True):
+        s_ = pool_s.clone()
+        c_ = pool_c.clone()
+        out = torch.empty((B, sh.Hv, sh.dv), dtype=torch.float32, device="cuda")
+        gdn.decode_raw(layer, B=B, q=t["q"], k=t["k"], v=t["v"], z=t["z"], a=t["a"], b=t["b"], out=out,
+                       state_in=s_, state_out=s_, conv_state_in=c_, conv_state_out=c_, state_slots=idx,
+                       num_slots=slots, workspace=gdn.decode_workspace(layer, B) if use_ws else None)
+        torch.cuda.synchronize()
+        outs.append((out, s_, c_))
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert _bits_equal(a_, b_)
 
 
 def test_decode_chain_matches_prefill_and_oracle():
