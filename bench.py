@@ -653,7 +653,7 @@ def main(argv=None):
             yd = torch.empty((Bd, H), dtype=torch.bfloat16, device=dev)
             sd = [torch.randn((Bd, sh.Hv, sh.dk, sh.dv), generator=gen, device=dev) * 0.1 for _ in range(NL)]
             cd = [torch.zeros((Bd, 3, sh.Cc), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
-            dws = torch.empty(gdn.layer_decode_workspace_bytes(lay, projs[0], Bd), dtype=torch.uint8, device=dev)
+            dws = torch.zeros(gdn.layer_decode_workspace_bytes(lay, projs[0], Bd), dtype=torch.uint8, device=dev)
 
             def ldstep(l):
                 gdn.layer_decode_raw(lay, projs[l], B=Bd, x=xd, y=yd, state_in=sd[l], state_out=sd[l],

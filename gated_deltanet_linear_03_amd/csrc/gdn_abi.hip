@@ -371,12 +371,7 @@ gdn_status gdn_prefill_timed(const gdn_layer* L, const gdn_prefill_io* io, void*
 static size_t decode_ws_bytes(const gdn_layer* L, int32_t B) {
     return (size_t(B) * L->Hk * 4 + 255) / 256 * 256;
 }
-// One work-group per value head spreads a small batch's state stream over
-// twice the compute units; both kernels give the same bits, so the choice
-// is free.
-static bool head_wg_pays(const gdn_layer* L, int32_t B) {
-    return static_cast<int64_t>(B) * L->Hk <= gdn::kDecodeHeadWgMaxGroups;
-}
+
 
 size_t gdn_decode_workspace_bytes(const gdn_layer* L, int32_t B) {
     g_err[0] = 0;
@@ -438,7 +433,9 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
             return fail(GDN_ERR_INVALID_ARGUMENT, "out or core_out overlaps a state");
     }
     const size_t dws_need = decode_ws_bytes(L, B);
-    const bool head_wg = Ts == 0 && io->workspace != nullptr && head_wg_pays(L, B);
+    // with a workspace, one work-group per value head (measured as fast or
+    // faster at every batch size; the same bits either way)
+    const bool head_wg = Ts == 0 && io->workspace != nullptr;
     if (Ts == 0 && io->workspace) {
         if (!aligned(io->workspace, 256))
             return fail(GDN_ERR_WORKSPACE, "decode workspace must be 256-byte aligned");
@@ -537,7 +534,14 @@ struct LayerWs {
     int64_t P = 0, off_proj = 0, off_gated = 0, off_pf = 0, total = 0;
 };
 
-// the projection [rows][P] and the gated output [rows][Hv*dv], bf16
+// Decode only: arrival counters of the one-work-group-per-value-head
+// decode kernel at the start of the workspace, at a place and size that do
+// not depend on B (up to this many (sequence, key head) pairs; beyond, the
+// step runs one work-group per key head and needs none)
+constexpr int64_t kLayerDecodeCounterBytes = 64 << 10;
+
+// (decode: the counters,) the projection [rows][P] and the gated output
+// [rows][Hv*dv], bf16
 gdn_status proj_ws(const gdn_layer* L, const gdn_proj* pr, int64_t rows, bool prefill, LayerWs* w) {
     gdn_status st = check_layer(L, prefill);
     if (st != GDN_OK) return st;
@@ -549,7 +553,7 @@ gdn_status proj_ws(const gdn_layer* L, const gdn_proj* pr, int64_t rows, bool pr
     w->P = 2ll * L->Hk * L->dk + 2ll * L->Hv * L->dv + 2ll * L->Hv;
     if ((2ll * L->Hk * L->dk) % 8 || (static_cast<int64_t>(L->Hv) * L->dv) % 8 || w->P % 8)
         return fail(GDN_ERR_INVALID_ARGUMENT, "projection widths must be multiples of 8");
-    int64_t o = 0;
+    int64_t o = prefill ? 0 : kLayerDecodeCounterBytes;
     w->off_proj = o;
     o = round_up(o + 2 * rows * w->P, 256);
     w->off_gated = o;
@@ -691,6 +695,10 @@ gdn_status gdn_layer_decode(const gdn_layer* L, const gdn_proj* pr, const gdn_la
     dio.core_out = nullptr;
     dio.state_slots = io->state_slots;
     dio.num_slots = io->num_slots;
+    if (B * L->Hk * 4 <= kLayerDecodeCounterBytes) {
+        dio.workspace = base;
+        dio.workspace_bytes = static_cast<size_t>(kLayerDecodeCounterBytes);
+    }
     st = decode_impl(&Lg, &dio, 0, nullptr, stream, false);
     if (st != GDN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);

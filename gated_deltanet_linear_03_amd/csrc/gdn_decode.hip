@@ -115,7 +115,8 @@ __device__ __forceinline__ float dot_wave(const float* a, const float* b, int la
 // Both compute each value head with the same operations in the same order,
 // so they give the same bits.  With HPW = 1 the conv and gate inputs are
 // loaded before the state stream (loads complete in issue order), so the
-// conv, the gates and the L2 norms run while the state arrives.
+// conv, the gates and the L2 norms run while the state arrives; with HPW = 2
+// the conv runs before the stream is issued.
 template <int DK, int DV, bool BF16, int HPW>
 __global__ __launch_bounds__(HPW * kDecodeHalf, 4) void decode_kernel(DecodeParams p) {
     using A = Act<BF16>;
@@ -261,14 +262,16 @@ __global__ __launch_bounds__(HPW * kDecodeHalf, 4) void decode_kernel(DecodePara
         conv_loads(gfirst, true);
         __builtin_amdgcn_sched_barrier(0);      // keep the conv inputs ahead of the stream
         load_state(gfirst);
+        conv_compute(gfirst, true);
     } else {
-        // (two heads' state leaves no registers to hold the conv inputs
-        // across the stream; at the batch sizes this kernel serves the step
-        // is bound by the state stream anyway)
-        load_state(gfirst);
+        // two heads' state leaves no registers to hold the conv inputs
+        // across the stream: the conv first, then the stream (with many
+        // work-groups per compute unit, others keep the stream busy)
         conv_loads(gfirst, true);
+        conv_compute(gfirst, true);
+        __builtin_amdgcn_sched_barrier(0);
+        load_state(gfirst);
     }
-    conv_compute(gfirst, true);
     __syncthreads();
     uint32_t* counter = nullptr;
     uint32_t prev;      // lane 0 of wave 0 only (no default: a merge would force a wait on the atomic)
@@ -307,8 +310,9 @@ __global__ __launch_bounds__(HPW * kDecodeHalf, 4) void decode_kernel(DecodePara
             // the next pair of heads (HPW = 2, G > 2): their v channels and
             // gates, then their state
             conv_loads(g0, false);
-            load_state(g0);
             conv_compute(g0, false);
+            __builtin_amdgcn_sched_barrier(0);
+            load_state(g0);
             __syncthreads();
         }
         if (!p.state_in) {

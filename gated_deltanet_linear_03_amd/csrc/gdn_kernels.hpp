@@ -31,10 +31,6 @@ struct DecodeParams {
     uint32_t* arrive;
 };
 
-// Most (sequence, key head) pairs for which gdn_decode, given a workspace,
-// runs one work-group per value head (beyond, one per key head streams as
-// fast with half the work-groups)
-constexpr int64_t kDecodeHeadWgMaxGroups = int64_t(1) << 30;
 
 constexpr int kMaxVerifyTokens = 16;     // tokens per sequence of one multi-token decode
 

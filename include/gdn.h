@@ -362,7 +362,10 @@ size_t gdn_layer_decode_workspace_bytes(const gdn_layer* layer,
                                         const gdn_proj* proj, int32_t B);
 
 /* in_proj GEMM -> gdn_decode on views into the projection -> out_proj GEMM,
- * on `stream`; validation as for gdn_decode plus the projection's shapes. */
+ * on `stream`; validation as for gdn_decode plus the projection's shapes.
+ * The workspace's first 64 KiB serve as the decode step's arrival counters
+ * (see gdn_decode_io): they must hold zeros before the first use, every call
+ * leaves them so, and a workspace serves one call at a time. */
 gdn_status gdn_layer_decode(const gdn_layer* layer, const gdn_proj* proj,
                             const gdn_layer_decode_io* io, void* workspace,
                             size_t workspace_bytes, void* stream);

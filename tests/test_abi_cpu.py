@@ -627,12 +627,13 @@ def test_layer_workspace_and_rejects():
 
 
 def test_layer_decode_workspace():
-    """The decode layer's workspace: the bf16 projection [B][P] and gated
-    output [B][Hv dv], each 256-byte rounded."""
+    """The decode layer's workspace: 64 KiB of decode arrival counters, then
+    the bf16 projection [B][P] and gated output [B][Hv dv], each 256-byte
+    rounded."""
     lay = gdn.Layer(Hk=16, Hv=32, dk=128, dv=128, chunk=64, conv_w=_FakeTensor(FAKE, 4),
                     A_log=_FakeTensor(FAKE, 1), dt_bias=_FakeTensor(FAKE, 1), norm_w=_FakeTensor(FAKE, 1))
     proj = gdn.Proj(hidden=2048, w_in=_FakeTensor(FAKE, 2048), w_out=_FakeTensor(FAKE, 4096))
     P = 2 * 16 * 128 + 2 * 32 * 128 + 2 * 32
     rnd = lambda n: -(-n // 256) * 256
     for B in (1, 3, 64):
-        assert gdn.layer_decode_workspace_bytes(lay, proj, B) == rnd(2 * B * P) + rnd(2 * B * 32 * 128)
+        assert gdn.layer_decode_workspace_bytes(lay, proj, B) == (64 << 10) + rnd(2 * B * P) + rnd(2 * B * 32 * 128)

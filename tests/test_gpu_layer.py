@@ -154,7 +154,7 @@ def test_layer_decode_parity(shape, hidden, B):
     y = torch.empty((B, hidden), dtype=torch.float32, device="cuda")
     st = to_dev(S0)
     cs = _bf16(C0)
-    ws = torch.empty(gdn.layer_decode_workspace_bytes(layer, proj, B), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(gdn.layer_decode_workspace_bytes(layer, proj, B), dtype=torch.uint8, device="cuda")
     gdn.layer_decode_raw(layer, proj, B=B, x=_bf16(x), y=y, state_in=st, state_out=st,
                          conv_state_in=cs, conv_state_out=cs, workspace=ws)
     torch.cuda.synchronize()
@@ -227,7 +227,7 @@ def _layer_decode(sh, hidden, p, w_in, w_out, x, S0, C0):
     y = torch.empty((B, hidden), dtype=torch.float32, device="cuda")
     st = to_dev(S0)
     cs = _bf16(C0)
-    ws = torch.empty(gdn.layer_decode_workspace_bytes(layer, proj, B), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(gdn.layer_decode_workspace_bytes(layer, proj, B), dtype=torch.uint8, device="cuda")
     gdn.layer_decode_raw(layer, proj, B=B, x=_bf16(x), y=y, state_in=st, state_out=st,
                          conv_state_in=cs, conv_state_out=cs, workspace=ws)
     torch.cuda.synchronize()
