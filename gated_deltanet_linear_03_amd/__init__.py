@@ -28,6 +28,7 @@ GDN_ERR_WORKSPACE = 3
 GDN_ERR_HIP = 4
 GDN_DTYPE_FP32 = 0
 GDN_DTYPE_BF16 = 1
+GDN_STATUS_NONFINITE = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
@@ -106,7 +107,8 @@ class CPrefillIO(ctypes.Structure):
                  ("conv_state_in", ctypes.c_void_p),
                  ("conv_state_out", ctypes.c_void_p),
                  ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p),
-                 ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32)])
+                 ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+                 ("status", ctypes.c_void_p)])
 
 
 class CDecodeIO(ctypes.Structure):
@@ -386,10 +388,11 @@ def prefill_window_slots(layer: Layer, N: int, T_total: int, workspace_bytes: in
 
 
 def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
-                final_state, conv_state_in, conv_state_out, state_slots, num_slots):
+                final_state, conv_state_in, conv_state_out, state_slots, num_slots, status=None):
     _check_tokens(layer, int(T_total), q, k, v, z, a, b, out, core_out)
     _check_index(cu_seqlens, "cu_seqlens", int(N) + 1)
     _check_index(state_slots, "state_slots", int(N))
+    _check_index(status, "status", 1)
     _check_states(layer, int(num_slots) if state_slots is not None else int(N), initial_state,
                   final_state, conv_state_in, conv_state_out, ("initial_state", "final_state"))
     return CPrefillIO(int(N), int(T_total), _ptr(cu_seqlens),
@@ -398,7 +401,7 @@ def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, 
                       _tok_stride(z), _tok_stride(a), _tok_stride(b),
                       _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
                       _ptr(conv_state_out), _ptr(out), _ptr(core_out), _ptr(state_slots),
-                      int(num_slots))
+                      int(num_slots), _ptr(status))
 
 
 def _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
@@ -419,14 +422,16 @@ def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
                 out, core_out=None, initial_state=None, final_state=None,
                 conv_state_in=None, conv_state_out=None, workspace=None,
                 workspace_bytes=None, stream=None, events=None, state_slots=None,
-                num_slots=0):
+                num_slots=0, status=None):
     """Call ``gdn_prefill`` on caller-provided buffers (no allocation).
     events: optional list of len(prefill_launches(...)) + 1 recorded
     torch.cuda.Event(enable_timing=True) objects; the call then goes through
-    ``gdn_prefill_timed`` and consecutive events bracket each kernel."""
+    ``gdn_prefill_timed`` and consecutive events bracket each kernel.
+    status: optional device int32 tensor, 0 after the call, or with bit
+    GDN_STATUS_NONFINITE set when an output or final state is not finite."""
     cl = layer.c()
     io = _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
-                     final_state, conv_state_in, conv_state_out, state_slots, num_slots)
+                     final_state, conv_state_in, conv_state_out, state_slots, num_slots, status)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if events is None:
@@ -442,18 +447,18 @@ def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
 def prefill_noalloc_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b, out,
                         core_out=None, initial_state=None, final_state=None,
                         conv_state_in=None, conv_state_out=None, stream=None,
-                        state_slots=None, num_slots=0):
+                        state_slots=None, num_slots=0, status=None):
     """Call ``gdn_prefill_noalloc``: gdn_prefill on caller-provided buffers
     with the library's static device scratch as the workspace."""
     cl = layer.c()
     io = _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
-                     final_state, conv_state_in, conv_state_out, state_slots, num_slots)
+                     final_state, conv_state_in, conv_state_out, state_slots, num_slots, status)
     _check(lib().gdn_prefill_noalloc(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
 
 
 def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,
             conv_state_in=None, want_core=False, in_place=False, workspace=None,
-            stream=None):
+            stream=None, status=None):
     """Allocate outputs with torch and run ``gdn_prefill``.
 
     q, k [T, Hk, dk]; v, z [T, Hv, dv]; a, b [T, Hv] (act dtype, may be
@@ -482,7 +487,7 @@ def prefill(layer: Layer, q, k, v, z, a, b, cu_seqlens, initial_state=None,
     prefill_raw(layer, N=N, T_total=T, cu_seqlens=cu_seqlens, q=q, k=k, v=v, z=z,
                 a=a, b=b, out=out, core_out=core, initial_state=initial_state,
                 final_state=fs, conv_state_in=conv_state_in, conv_state_out=cs,
-                workspace=workspace, stream=stream)
+                workspace=workspace, stream=stream, status=status)
     res = {"out": out, "final_state": fs, "conv_state_out": cs}
     if want_core:
         res["core_out"] = core
@@ -525,12 +530,12 @@ def step_raw(layer: Layer, *, prefill=None, decode=None, workspace=None, workspa
     pio = dio = None
     if prefill is not None:
         f = dict(core_out=None, initial_state=None, final_state=None, conv_state_in=None,
-                 conv_state_out=None, state_slots=None, num_slots=0)
+                 conv_state_out=None, state_slots=None, num_slots=0, status=None)
         f.update(prefill)
         pio = _prefill_io(layer, f["N"], f["T_total"], f["cu_seqlens"], f["q"], f["k"], f["v"], f["z"],
                           f["a"], f["b"], f["out"], f["core_out"], f["initial_state"],
                           f["final_state"], f["conv_state_in"], f["conv_state_out"],
-                          f["state_slots"], f["num_slots"])
+                          f["state_slots"], f["num_slots"], f["status"])
     if decode is not None:
         f = dict(core_out=None, state_slots=None, num_slots=0, workspace=None)
         f.update(decode)

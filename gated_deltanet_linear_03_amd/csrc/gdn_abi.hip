@@ -234,6 +234,15 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
         output_hits_state(io->core_out, size_t(T) * Hv * dv * 4, io->initial_state, io->final_state,
                           state_bytes, io->conv_state_in, io->conv_state_out, conv_bytes))
         return fail(GDN_ERR_INVALID_ARGUMENT, "out or core_out overlaps a state");
+    if (io->status) {
+        if (!aligned(io->status, 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "status must be 4-byte aligned");
+        if (overlaps(io->status, 4, io->out, out_bytes) ||
+            overlaps(io->status, 4, io->core_out, size_t(T) * Hv * dv * 4) ||
+            output_hits_state(io->status, 4, io->initial_state, io->final_state, state_bytes, io->conv_state_in,
+                              io->conv_state_out, conv_bytes) ||
+            overlaps(io->status, 4, ws, ws_bytes))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "status overlaps an output, a state or the workspace");
+    }
 
     WsLayout w;
     st = fit_workspace(L, N, T, io->core_out == nullptr, ws, ws_bytes, &w);
@@ -253,6 +262,7 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.core = io->core_out ? io->core_out : reinterpret_cast<float*>(base + w.off_core);
     p.slots = io->state_slots;
+    p.status = io->status;
     p.chunk_off = reinterpret_cast<int32_t*>(base + w.off_chunk);
     p.decay = reinterpret_cast<float*>(base + w.off_decay);
     p.sink = reinterpret_cast<float*>(base + w.off_sink);

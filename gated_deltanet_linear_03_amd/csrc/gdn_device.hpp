@@ -227,6 +227,14 @@ __device__ __forceinline__ uintptr_t uniform_ptr(const P* ptr) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Sets bit 0 of *status when any lane of the wave passes `bad` (one atomic
+// per wave, from its lowest such lane)
+__device__ __forceinline__ void flag_nonfinite(int32_t* status, bool bad) {
+    const uint64_t m = __ballot(bad);
+    if (status && m && (__lane_id() == static_cast<unsigned>(__builtin_ctzll(m))))
+        __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // s_waitcnt vmcnt(0): every vector memory access this wave has issued,
 // loads and stores alike, has completed (gfx9 encoding: expcnt and lgkmcnt
 // left at their maxima)

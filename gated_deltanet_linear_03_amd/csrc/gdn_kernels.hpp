@@ -57,6 +57,7 @@ struct PrefillParams {
     int out_bf16;
     float* core;                          // o before the gated norm (user or workspace)
     const int32_t* slots;                 // [N] pool entry of each sequence's states, or NULL (entry n)
+    int32_t* status;                      // optional: cleared by the first kernel, bit 0 set on a non-finite result
     // workspace views
     int32_t* chunk_off;                   // [N+1] first chunk of each sequence (written by the first prep)
     float* decay;                         // [max_chunks][Hv] exp(gamma_last)

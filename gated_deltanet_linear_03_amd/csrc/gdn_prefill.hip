@@ -401,6 +401,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
 
         // leaving state
         if (hout) {
+            bool bad = false;
 #pragma unroll
             for (int qh = 0; qh < QH; ++qh) {
                 const int mth = wave + NW * qh;
@@ -411,8 +412,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                     for (int i = 0; i < 4; ++i) {
                         const int row = mth * 16 + lq * 4 + i;
                         hout[static_cast<size_t>(row) * DV + col0 + nt * 16 + l16] = hacc[qh][nt][i];
+                        bad |= !isfinite(hacc[qh][nt][i]);
                     }
             }
+            // a non-finite final state is reported too
+            if (seq_last) flag_nonfinite(p.status, bad);
         }
     } else {
         // ---------------- output waves ----------------
@@ -626,6 +630,9 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = w[e] * (o[e] * r) * silu(z[e]);
+    // a non-finite output (with finite inputs: the scan's fp16 operand range
+    // exceeded upstream) is reported, never passed on silently
+    flag_nonfinite(p.status, valid && !(isfinite(y[0]) && isfinite(y[1]) && isfinite(y[2]) && isfinite(y[3])));
     if (!valid) return;
     if (p.out_bf16) {
         uint2 v;

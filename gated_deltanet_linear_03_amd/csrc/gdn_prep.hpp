@@ -222,6 +222,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     // stores it), read from the workspace after that
     int total, n = 0, first = 0;
     if (p.win_idx == 0) {
+        // the call's first kernel: clear the caller's status word
+        if (p.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = 0;
         const ChunkPos cp = chunk_table<kPrepThreads>(p.cu, p.N, C, slot, reinterpret_cast<int32_t*>(smem + S::oS),
                                                       blockIdx.x == 0 && blockIdx.y == 0 ? p.chunk_off : nullptr);
         total = cp.total;

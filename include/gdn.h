@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 10
+#define GDN_ABI_VERSION 11
 
 typedef enum {
     GDN_OK = 0,
@@ -123,7 +123,17 @@ typedef struct {
      * entry n, as without a pool (num_slots ignored). */
     const int32_t* state_slots;
     int32_t num_slots;
+    /* optional device int32: the call's first kernel stores 0 there, and
+     * GDN_STATUS_NONFINITE is ORed in when a value of out or of final_state
+     * is not finite.  With finite inputs that happens only when a value on
+     * the scan's fp16 operand path left the fp16 range (|x| >= 65520 rounds
+     * to inf): the state S, or u = beta (v - e^g S k), of magnitude beyond
+     * ~6.5e4 -- activations far beyond a layer's normal scale.  Read it once
+     * the stream has passed the call; NULL: no check. */
+    int32_t* status;
 } gdn_prefill_io;
+
+#define GDN_STATUS_NONFINITE 1
 
 /* One token for each of B sequences.  state_out may equal state_in and
  * conv_state_out may equal conv_state_in (in-place); partial overlap is an

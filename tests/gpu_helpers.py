@@ -71,7 +71,7 @@ def workspace_for_window(layer, N, T, window_slots, with_core_out=True):
 
 
 def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=False,
-                window_slots=None):
+                window_slots=None, status=None):
     """window_slots: run with a workspace that holds only this many chunk
     slots of operand blocks (more, smaller windows); None = default."""
     sh = case.shape
@@ -88,7 +88,7 @@ def gpu_prefill(case, out_dtype=gdn.GDN_DTYPE_FP32, want_core=True, in_place=Fal
                          device="cuda")
     res = gdn.prefill(layer, x["q"], x["k"], x["v"], x["z"], x["a"], x["b"], cu,
                       initial_state=S0, conv_state_in=C0, want_core=want_core,
-                      in_place=in_place, workspace=ws)
+                      in_place=in_place, workspace=ws, status=status)
     torch.cuda.synchronize()
     return res
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 10
+    assert L.gdn_abi_version() == 11
 
 
 def test_status_strings():
@@ -484,7 +484,7 @@ def test_binding_structs_match_the_header(tmp_path):
     checks = {"gdn_layer": (gdn.CLayer, ["Hk", "chunk", "scale", "conv_w", "norm_w"]),
               "gdn_prefill_io": (gdn.CPrefillIO, ["N", "T_total", "cu_seqlens", "b_stride",
                                                   "initial_state", "core_out", "state_slots",
-                                                  "num_slots"]),
+                                                  "num_slots", "status"]),
               "gdn_decode_io": (gdn.CDecodeIO, ["B", "q", "b_stride", "state_in", "core_out",
                                                 "state_slots", "num_slots", "workspace",
                                                 "workspace_bytes"]),
@@ -637,3 +637,18 @@ def test_layer_decode_workspace():
     rnd = lambda n: -(-n // 256) * 256
     for B in (1, 3, 64):
         assert gdn.layer_decode_workspace_bytes(lay, proj, B) == (64 << 10) + rnd(2 * B * P) + rnd(2 * B * 32 * 128)
+
+
+def test_prefill_status_word_checks():
+    """The optional status word must be 4-byte aligned and share no bytes
+    with an output, a state or the workspace."""
+    cl = _full_layer()
+    far = FAKE + (1 << 36)
+    base = dict(out=FAKE + (1 << 34), N=1, T_total=64)
+    for status, msg in ((far + 2, b"aligned"), (FAKE + (1 << 34) + 64, b"overlaps"),
+                        (FAKE + (1 << 40) + 16, b"overlaps")):
+        io = _pio(status=status, **base)
+        st = gdn.lib().gdn_prefill(ctypes.byref(cl), ctypes.byref(io), ctypes.c_void_p(FAKE + (1 << 40)),
+                                   1 << 30, None)
+        assert st == gdn.GDN_ERR_INVALID_ARGUMENT, status
+        assert msg in gdn.lib().gdn_last_error(), status
