@@ -29,6 +29,7 @@ GDN_ERR_HIP = 4
 GDN_DTYPE_FP32 = 0
 GDN_DTYPE_BF16 = 1
 GDN_STATUS_NONFINITE = 1
+GDN_STATUS_BAD_INDEX = 2
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
@@ -69,7 +70,7 @@ class CLayerIO(ctypes.Structure):
                 ("y_dtype", ctypes.c_int32), ("initial_state", ctypes.c_void_p),
                 ("final_state", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
                 ("conv_state_out", ctypes.c_void_p), ("state_slots", ctypes.c_void_p),
-                ("num_slots", ctypes.c_int32)]
+                ("num_slots", ctypes.c_int32), ("status", ctypes.c_void_p)]
 
 
 class CLayerDecodeIO(ctypes.Structure):
@@ -77,7 +78,7 @@ class CLayerDecodeIO(ctypes.Structure):
                 ("y_dtype", ctypes.c_int32), ("state_in", ctypes.c_void_p),
                 ("state_out", ctypes.c_void_p), ("conv_state_in", ctypes.c_void_p),
                 ("conv_state_out", ctypes.c_void_p), ("state_slots", ctypes.c_void_p),
-                ("num_slots", ctypes.c_int32)]
+                ("num_slots", ctypes.c_int32), ("status", ctypes.c_void_p)]
 
 
 class CLayer(ctypes.Structure):
@@ -118,7 +119,8 @@ class CDecodeIO(ctypes.Structure):
                  ("conv_state_out", ctypes.c_void_p),
                  ("out", ctypes.c_void_p), ("core_out", ctypes.c_void_p),
                  ("state_slots", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
-                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)])
+                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                 ("status", ctypes.c_void_p)])
 
 
 _lib = None
@@ -387,6 +389,12 @@ def prefill_window_slots(layer: Layer, N: int, T_total: int, workspace_bytes: in
     return int(n)
 
 
+def _status_ptr(status):
+    """Pointer of an optional device int32 status word (checked)."""
+    _check_index(status, "status", 1)
+    return _ptr(status)
+
+
 def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
                 final_state, conv_state_in, conv_state_out, state_slots, num_slots, status=None):
     _check_tokens(layer, int(T_total), q, k, v, z, a, b, out, core_out)
@@ -405,7 +413,7 @@ def _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, 
 
 
 def _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
-               conv_state_out, state_slots, num_slots, tokens=1, workspace=None):
+               conv_state_out, state_slots, num_slots, tokens=1, workspace=None, status=None):
     _check_tokens(layer, int(B) * int(tokens), q, k, v, z, a, b, out, core_out)
     _check_index(state_slots, "state_slots", int(B))
     _check_states(layer, int(num_slots) if state_slots is not None else int(B), state_in,
@@ -415,7 +423,8 @@ def _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, c
                      _tok_stride(q), _tok_stride(k), _tok_stride(v), _tok_stride(z),
                      _tok_stride(a), _tok_stride(b), _ptr(state_in), _ptr(state_out),
                      _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out),
-                     _ptr(core_out), _ptr(state_slots), int(num_slots), _ptr(workspace), int(wsb))
+                     _ptr(core_out), _ptr(state_slots), int(num_slots), _ptr(workspace), int(wsb),
+                     _status_ptr(status))
 
 
 def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
@@ -428,7 +437,9 @@ def prefill_raw(layer: Layer, *, N, T_total, cu_seqlens, q, k, v, z, a, b,
     torch.cuda.Event(enable_timing=True) objects; the call then goes through
     ``gdn_prefill_timed`` and consecutive events bracket each kernel.
     status: optional device int32 tensor, 0 after the call, or with bit
-    GDN_STATUS_NONFINITE set when an output or final state is not finite."""
+    GDN_STATUS_NONFINITE set when an output or final state is not finite,
+    GDN_STATUS_BAD_INDEX when cu_seqlens or state_slots break their contract
+    (nothing is then written)."""
     cl = layer.c()
     io = _prefill_io(layer, N, T_total, cu_seqlens, q, k, v, z, a, b, out, core_out, initial_state,
                      final_state, conv_state_in, conv_state_out, state_slots, num_slots, status)
@@ -511,14 +522,16 @@ def decode_workspace(layer: Layer, B: int, device="cuda"):
 
 def decode_raw(layer: Layer, *, B, q, k, v, z, a, b, out, state_in, state_out,
                conv_state_in, conv_state_out, core_out=None, stream=None, state_slots=None,
-               num_slots=0, workspace=None):
+               num_slots=0, workspace=None, status=None):
     """Call ``gdn_decode`` on caller-provided buffers (no allocation).  With
     state_slots (device int32 [B]) the states are pools of num_slots entries;
-    with a workspace (``decode_workspace``) a small batch takes the
-    column-split kernel (same bits)."""
+    with a workspace (``decode_workspace``) one work-group per value head
+    (same bits).  status: optional device int32 tensor into which
+    GDN_STATUS_BAD_INDEX is ORed when a pool entry is out of range (that
+    sequence is skipped); the call never clears it."""
     cl = layer.c()
     io = _decode_io(layer, B, q, k, v, z, a, b, out, core_out, state_in, state_out, conv_state_in,
-                    conv_state_out, state_slots, num_slots, workspace=workspace)
+                    conv_state_out, state_slots, num_slots, workspace=workspace, status=status)
     _check(lib().gdn_decode(ctypes.byref(cl), ctypes.byref(io), _stream(stream)))
 
 
@@ -537,12 +550,12 @@ def step_raw(layer: Layer, *, prefill=None, decode=None, workspace=None, workspa
                           f["final_state"], f["conv_state_in"], f["conv_state_out"],
                           f["state_slots"], f["num_slots"], f["status"])
     if decode is not None:
-        f = dict(core_out=None, state_slots=None, num_slots=0, workspace=None)
+        f = dict(core_out=None, state_slots=None, num_slots=0, workspace=None, status=None)
         f.update(decode)
         dio = _decode_io(layer, f["B"], f["q"], f["k"], f["v"], f["z"], f["a"], f["b"], f["out"],
                          f["core_out"], f["state_in"], f["state_out"], f["conv_state_in"],
                          f["conv_state_out"], f["state_slots"], f["num_slots"],
-                         workspace=f["workspace"])
+                         workspace=f["workspace"], status=f["status"])
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_step(ctypes.byref(cl), ctypes.byref(pio) if pio is not None else None,
@@ -658,7 +671,7 @@ def layer_prefill_workspace_bytes(layer: Layer, proj: Proj, N: int, T_total: int
 def layer_prefill_raw(layer: Layer, proj: Proj, *, N, T_total, cu_seqlens, x, y,
                       initial_state=None, final_state=None, conv_state_in=None,
                       conv_state_out=None, workspace=None, workspace_bytes=None,
-                      state_slots=None, num_slots=0, stream=None):
+                      state_slots=None, num_slots=0, stream=None, status=None):
     """Call ``gdn_layer_prefill``: x [T, hidden] bf16 -> y [T, hidden] (bf16
     or fp32), through in_proj, the layer and out_proj."""
     import torch
@@ -673,7 +686,7 @@ def layer_prefill_raw(layer: Layer, proj: Proj, *, N, T_total, cu_seqlens, x, y,
     yd = GDN_DTYPE_BF16 if y is not None and y.dtype == torch.bfloat16 else GDN_DTYPE_FP32
     io = CLayerIO(int(N), int(T_total), _ptr(cu_seqlens), _ptr(x), _ptr(y), yd,
                   _ptr(initial_state), _ptr(final_state), _ptr(conv_state_in),
-                  _ptr(conv_state_out), _ptr(state_slots), int(num_slots))
+                  _ptr(conv_state_out), _ptr(state_slots), int(num_slots), _status_ptr(status))
     nb = workspace_bytes if workspace_bytes is not None else (
         workspace.numel() * workspace.element_size() if workspace is not None else 0)
     _check(lib().gdn_layer_prefill(ctypes.byref(cl), ctypes.byref(cp), ctypes.byref(io),
@@ -690,7 +703,7 @@ def layer_decode_workspace_bytes(layer: Layer, proj: Proj, B: int) -> int:
 
 def layer_decode_raw(layer: Layer, proj: Proj, *, B, x, y, state_in, state_out, conv_state_in,
                      conv_state_out, workspace, workspace_bytes=None, state_slots=None, num_slots=0,
-                     stream=None):
+                     stream=None, status=None):
     """Call ``gdn_layer_decode``: x [B, hidden] bf16 -> y [B, hidden], one
     token per sequence through in_proj, the decode step and out_proj."""
     import torch
@@ -703,7 +716,8 @@ def layer_decode_raw(layer: Layer, proj: Proj, *, B, x, y, state_in, state_out, 
                   state_out, conv_state_in, conv_state_out)
     yd = GDN_DTYPE_BF16 if y is not None and y.dtype == torch.bfloat16 else GDN_DTYPE_FP32
     io = CLayerDecodeIO(int(B), _ptr(x), _ptr(y), yd, _ptr(state_in), _ptr(state_out),
-                        _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_slots), int(num_slots))
+                        _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_slots), int(num_slots),
+                        _status_ptr(status))
     nb = workspace_bytes if workspace_bytes is not None else (
         workspace.numel() * workspace.element_size() if workspace is not None else 0)
     _check(lib().gdn_layer_decode(ctypes.byref(cl), ctypes.byref(cp), ctypes.byref(io),

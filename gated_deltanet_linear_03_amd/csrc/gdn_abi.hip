@@ -130,6 +130,7 @@ int64_t stride_or(int64_t s, int64_t dense) { return s == 0 ? dense : s; }
 extern "C" {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+static_assert(gdn::kStatusBadIndex == GDN_STATUS_BAD_INDEX, "status bits of the kernels and the header");
 
 const char* gdn_status_string(gdn_status st) {
     switch (st) {
@@ -262,6 +263,7 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.core = io->core_out ? io->core_out : reinterpret_cast<float*>(base + w.off_core);
     p.slots = io->state_slots;
+    p.num_slots = static_cast<int>(entries);
     p.status = io->status;
     p.chunk_off = reinterpret_cast<int32_t*>(base + w.off_chunk);
     p.decay = reinterpret_cast<float*>(base + w.off_decay);
@@ -461,6 +463,16 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
             overlaps(io->workspace, io->workspace_bytes, io->core_out, size_t(B) * Hv * dv * 4))
             return fail(GDN_ERR_INVALID_ARGUMENT, "decode workspace overlaps a state or an output");
     }
+    if (io->status) {
+        const size_t rows = size_t(B) * (Ts > 0 ? Ts : 1);
+        const size_t ob = rows * Hv * dv * (L->out_dtype == GDN_DTYPE_BF16 ? 2 : 4);
+        if (!aligned(io->status, 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "status must be 4-byte aligned");
+        if (overlaps(io->status, 4, io->out, ob) || overlaps(io->status, 4, io->core_out, rows * Hv * dv * 4) ||
+            output_hits_state(io->status, 4, io->state_in, io->state_out, state_bytes, io->conv_state_in,
+                              io->conv_state_out, conv_bytes) ||
+            (head_wg && overlaps(io->status, 4, io->workspace, io->workspace_bytes)))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "status overlaps an output, a state or the workspace");
+    }
     if (snap) {
         const size_t snap_bytes = size_t(B) * Ts * Hv * dk * dv * 4;
         if (!aligned(snap, 16)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_snapshots must be 16-byte aligned");
@@ -480,6 +492,8 @@ static gdn_status decode_impl(const gdn_layer* L, const gdn_decode_io* io, int32
     p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16; p.core_out = io->core_out;
     p.Ts = Ts; p.snap = snap;     // Ts = 0: the one-token kernel
     p.slots = io->state_slots;
+    p.num_slots = static_cast<int>(entries);
+    p.status = io->status;
     if (head_wg) p.arrive = static_cast<uint32_t*>(io->workspace);
     if (!launch) return GDN_OK;
     bool supported = false;
@@ -636,6 +650,7 @@ gdn_status gdn_layer_prefill(const gdn_layer* L, const gdn_proj* pr, const gdn_l
     pio.core_out = nullptr;
     pio.state_slots = io->state_slots;
     pio.num_slots = io->num_slots;
+    pio.status = io->status;
     // validate the prefill part before enqueueing anything
     st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr, false);
     if (st != GDN_OK) return st;
@@ -705,6 +720,7 @@ gdn_status gdn_layer_decode(const gdn_layer* L, const gdn_proj* pr, const gdn_la
     dio.core_out = nullptr;
     dio.state_slots = io->state_slots;
     dio.num_slots = io->num_slots;
+    dio.status = io->status;
     if (B * L->Hk * 4 <= kLayerDecodeCounterBytes) {
         dio.workspace = base;
         dio.workspace_bytes = static_cast<size_t>(kLayerDecodeCounterBytes);

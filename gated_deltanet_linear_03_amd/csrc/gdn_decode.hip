@@ -156,6 +156,13 @@ __global__ __launch_bounds__(HPW * kDecodeHalf, 4) void decode_kernel(DecodePara
     const T* cin = static_cast<const T*>(p.conv_in);
     T* cout = static_cast<T*>(p.conv_out);
     const int sb = state_slot(p.slots, b);                // pool entry of the states
+    if (p.slots && static_cast<unsigned>(sb) >= static_cast<unsigned>(p.num_slots)) {
+        // an entry outside the pool: the sequence is skipped (nothing read
+        // or written for it, no arrival counted) and reported
+        if (tid == 0 && p.status)
+            __hip_atomic_fetch_or(p.status, kStatusBadIndex, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const size_t crow = static_cast<size_t>(sb) * 3 * Cc;
 
     // ---- conv and gate inputs ----
@@ -414,6 +421,12 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void verify_kernel(DecodeParams 
     const T* cin = static_cast<const T*>(p.conv_in);
     T* cout = static_cast<T*>(p.conv_out);
     const int sb = state_slot(p.slots, b);                // pool entry of the states
+    if (p.slots && static_cast<unsigned>(sb) >= static_cast<unsigned>(p.num_slots)) {
+        // an entry outside the pool: the sequence is skipped and reported
+        if (tid == 0 && p.status)
+            __hip_atomic_fetch_or(p.status, kStatusBadIndex, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const size_t crow = static_cast<size_t>(sb) * 3 * Cc;
     const int64_t row0 = static_cast<int64_t>(b) * Ts;   // the sequence's first token row
 

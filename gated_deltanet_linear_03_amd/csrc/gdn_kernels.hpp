@@ -25,6 +25,8 @@ struct DecodeParams {
     int Ts;                              // 0: one token (decode); else tokens per sequence (rows b*Ts ..)
     float* snap;                         // [B][Ts][Hv][dk][dv] state after each token, or NULL
     const int32_t* slots;                // [B] pool entry of each sequence's states, or NULL (entry b)
+    int num_slots;                       // pool entries (with slots)
+    int32_t* status;                     // optional: a sequence with an out-of-range entry is skipped and reported
     // one-token step with one work-group per value head (Ts = 0 only):
     // arrival counters [B][Hk], zero on entry and left zero.  NULL: one
     // work-group per key head.
@@ -36,6 +38,11 @@ constexpr int kMaxVerifyTokens = 16;     // tokens per sequence of one multi-tok
 
 // Pool entry holding sequence n's recurrent and conv state.
 __device__ __forceinline__ int state_slot(const int32_t* slots, int n) { return slots ? slots[n] : n; }
+
+// Status bit of a device-side index out of its documented range
+// (cu_seqlens not starting at 0, decreasing or not ending at T_total; a
+// state pool entry outside [0, num_slots)); equal to GDN_STATUS_BAD_INDEX.
+constexpr int32_t kStatusBadIndex = 2;
 
 struct PrefillParams {
     int N, Hk, Hv, G;
@@ -57,9 +64,11 @@ struct PrefillParams {
     int out_bf16;
     float* core;                          // o before the gated norm (user or workspace)
     const int32_t* slots;                 // [N] pool entry of each sequence's states, or NULL (entry n)
-    int32_t* status;                      // optional: cleared by the first kernel, bit 0 set on a non-finite result
+    int num_slots;                        // pool entries (with slots)
+    int32_t* status;                      // optional: cleared by the first kernel, then status bits ORed in
     // workspace views
-    int32_t* chunk_off;                   // [N+1] first chunk of each sequence (written by the first prep)
+    int32_t* chunk_off;                   // [N+1] first chunk of each sequence (written by the first prep);
+                                          // chunk_off[N] < 0: the call's indices were rejected
     float* decay;                         // [max_chunks][Hv] exp(gamma_last)
     float* sink;                          // [64] target of stores to rows past a sequence end
     float* carry;                         // [2][Hv][dk][dv] state across a window boundary

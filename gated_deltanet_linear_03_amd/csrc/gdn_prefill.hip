@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     const int sl = j % NS;
     const int pair = (j / NS) * 8 + xcd;
     if (pair >= p.N * p.Hv) return;
+    if (p.chunk_off[p.N] < 0) return;      // the call's indices were rejected
     const int n = pair / p.Hv, h = pair % p.Hv;
     // this window's chunks of sequence n; a sequence without chunks passes
     // its states through in window 0
@@ -630,10 +631,14 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = w[e] * (o[e] * r) * silu(z[e]);
+    // nothing is written when the call's indices were rejected (o was not
+    // computed); the flag is read here, after the loads were issued, so that
+    // they do not wait for it
+    const bool ok = p.chunk_off[p.N] >= 0;
     // a non-finite output (with finite inputs: the scan's fp16 operand range
     // exceeded upstream) is reported, never passed on silently
-    flag_nonfinite(p.status, valid && !(isfinite(y[0]) && isfinite(y[1]) && isfinite(y[2]) && isfinite(y[3])));
-    if (!valid) return;
+    flag_nonfinite(p.status, ok && valid && !(isfinite(y[0]) && isfinite(y[1]) && isfinite(y[2]) && isfinite(y[3])));
+    if (!valid || !ok) return;
     if (p.out_bf16) {
         uint2 v;
         v.x = f32_to_bf16_bits(y[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(y[1])) << 16);

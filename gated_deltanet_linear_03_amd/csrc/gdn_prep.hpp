@@ -223,7 +223,28 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
     int total, n = 0, first = 0;
     if (p.win_idx == 0) {
         // the call's first kernel: clear the caller's status word
-        if (p.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = 0;
+        const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
+        if (p.status && lead && threadIdx.x == 0) *p.status = 0;
+        // The device-side indices: cu_seqlens starts at 0, never decreases
+        // and ends at T_total, and pool entries lie in [0, num_slots).  Every
+        // work-group reads the same values and reaches the same verdict.  On
+        // a bad one nothing is computed: the chunk table's total becomes -1,
+        // which every later kernel of the call takes as "return at once",
+        // and the status word gets kStatusBadIndex.
+        bool bad = false;
+        for (int m = tid; m < p.N; m += NT) {
+            bad |= p.cu[m + 1] < p.cu[m];
+            if (p.slots) bad |= static_cast<unsigned>(p.slots[m]) >= static_cast<unsigned>(p.num_slots);
+        }
+        if (tid == 0) bad |= p.cu[0] != 0 || static_cast<int64_t>(p.cu[p.N]) != p.T;
+        if (__syncthreads_or(bad)) {
+            if (lead && tid == 0) {
+                p.chunk_off[p.N] = -1;
+                if (p.status)
+                    __hip_atomic_fetch_or(p.status, kStatusBadIndex, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return;
+        }
         const ChunkPos cp = chunk_table<kPrepThreads>(p.cu, p.N, C, slot, reinterpret_cast<int32_t*>(smem + S::oS),
                                                       blockIdx.x == 0 && blockIdx.y == 0 ? p.chunk_off : nullptr);
         total = cp.total;

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 11
+#define GDN_ABI_VERSION 12
 
 typedef enum {
     GDN_OK = 0,
@@ -104,7 +104,8 @@ typedef struct {
 typedef struct {
     int32_t N;
     int64_t T_total;               /* == cu_seqlens[N] */
-    const int32_t* cu_seqlens;     /* device int32 [N+1], non-decreasing, [0] = 0 */
+    const int32_t* cu_seqlens;     /* device int32 [N+1], non-decreasing, [0] = 0
+                                    * (checked on the device: see status) */
     const void *q, *k, *v, *z, *a, *b;
     int64_t q_stride, k_stride, v_stride, z_stride, a_stride, b_stride;
     const float* initial_state;
@@ -123,17 +124,26 @@ typedef struct {
      * entry n, as without a pool (num_slots ignored). */
     const int32_t* state_slots;
     int32_t num_slots;
-    /* optional device int32: the call's first kernel stores 0 there, and
-     * GDN_STATUS_NONFINITE is ORed in when a value of out or of final_state
-     * is not finite.  With finite inputs that happens only when a value on
-     * the scan's fp16 operand path left the fp16 range (|x| >= 65520 rounds
-     * to inf): the state S, or u = beta (v - e^g S k), of magnitude beyond
-     * ~6.5e4 -- activations far beyond a layer's normal scale.  Read it once
-     * the stream has passed the call; NULL: no check. */
+    /* optional device int32: the call's first kernel stores 0 there, then
+     * ORs in status bits:
+     *   GDN_STATUS_NONFINITE when a value of out or of final_state is not
+     *     finite.  With finite inputs that happens only when a value on the
+     *     scan's fp16 operand path left the fp16 range (|x| >= 65520 rounds
+     *     to inf): the state S, or u = beta (v - e^g S k), of magnitude
+     *     beyond ~6.5e4 -- activations far beyond a layer's normal scale.
+     *   GDN_STATUS_BAD_INDEX when the device-side indices break their
+     *     contract: cu_seqlens[0] != 0, a decreasing step, cu_seqlens[N] !=
+     *     T_total, or a state_slots entry outside [0, num_slots).  The call
+     *     then computes and writes nothing (out, core_out, final_state and
+     *     conv_state_out keep their contents), with or without a status
+     *     word; no memory is touched through the bad index.  (Duplicate
+     *     state_slots entries are not detected.)
+     * Read it once the stream has passed the call; NULL: no report. */
     int32_t* status;
 } gdn_prefill_io;
 
 #define GDN_STATUS_NONFINITE 1
+#define GDN_STATUS_BAD_INDEX 2
 
 /* One token for each of B sequences.  state_out may equal state_in and
  * conv_state_out may equal conv_state_in (in-place); partial overlap is an
@@ -166,6 +176,13 @@ typedef struct {
     int32_t num_slots;
     void* workspace;                     /* optional, see above */
     size_t workspace_bytes;
+    /* optional device int32, never cleared by the call:
+     * GDN_STATUS_BAD_INDEX is ORed in when a state_slots entry lies outside
+     * [0, num_slots).  That sequence is skipped: nothing is read or written
+     * for it (its out and core_out rows and its pool entries keep their
+     * contents), the others are computed as usual.  NULL: no report (the
+     * sequence is skipped all the same). */
+    int32_t* status;
 } gdn_decode_io;
 
 /* Bytes of a gdn_decode workspace for up to B sequences: arrival counters
@@ -334,6 +351,10 @@ typedef struct {
     void* conv_state_out;
     const int32_t* state_slots;    /* optional pool entries */
     int32_t num_slots;
+    int32_t* status;               /* optional, as in gdn_prefill_io; on
+                                    * GDN_STATUS_BAD_INDEX the states keep
+                                    * their contents and y is unspecified
+                                    * (out_proj still runs) */
 } gdn_layer_io;
 
 /* Workspace of gdn_layer_prefill: the projection [T][P] bf16, the gated
@@ -366,6 +387,9 @@ typedef struct {
     void* conv_state_out;
     const int32_t* state_slots;
     int32_t num_slots;
+    int32_t* status;               /* optional, as in gdn_decode_io; a
+                                    * skipped sequence's row of y is
+                                    * unspecified (out_proj still runs) */
 } gdn_layer_decode_io;
 
 size_t gdn_layer_decode_workspace_bytes(const gdn_layer* layer,

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 11
+    assert L.gdn_abi_version() == 12
 
 
 def test_status_strings():
@@ -191,6 +191,22 @@ def test_decode_workspace_bytes_and_errors():
     st = gdn.lib().gdn_step(ctypes.byref(cl), ctypes.byref(pio), ctypes.byref(dio), ctypes.c_void_p(ws),
                             nb, None)
     assert st == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_decode_status_word_checks():
+    """The decode status word (where an out-of-range pool entry is reported)
+    must be 4-byte aligned and share no bytes with an output, a state or the
+    workspace."""
+    cl = _full_layer()
+    far = FAKE + (1 << 36)
+    need = gdn.lib().gdn_decode_workspace_bytes(ctypes.byref(cl), 4)
+    base = dict(out=FAKE + (1 << 34), state_in=FAKE, state_out=FAKE, conv_state_in=FAKE + (1 << 30),
+                conv_state_out=FAKE + (1 << 30), workspace=FAKE + (1 << 40), workspace_bytes=need)
+    for status in (far + 2, FAKE + (1 << 34) + 64, FAKE + 4096, FAKE + (1 << 40) + 16):
+        st = gdn.lib().gdn_decode(ctypes.byref(cl), ctypes.byref(_dio(status=status, **base)), None)
+        assert st == gdn.GDN_ERR_INVALID_ARGUMENT, status
+        msg = b"aligned" if status == far + 2 else b"overlaps"
+        assert msg in gdn.lib().gdn_last_error(), status
 
 
 def test_decode_zero_batch_is_a_no_op():
@@ -487,17 +503,17 @@ def test_binding_structs_match_the_header(tmp_path):
                                                   "num_slots", "status"]),
               "gdn_decode_io": (gdn.CDecodeIO, ["B", "q", "b_stride", "state_in", "core_out",
                                                 "state_slots", "num_slots", "workspace",
-                                                "workspace_bytes"]),
+                                                "workspace_bytes", "status"]),
               "gdn_snapshot_header": (gdn.CSnapshotHeader, ["magic", "version", "Hk", "dv",
                                                             "act_dtype", "state_bytes",
                                                             "checksum", "reserved"]),
               "gdn_proj": (gdn.CProj, ["hidden", "w_in", "w_out"]),
               "gdn_layer_io": (gdn.CLayerIO, ["N", "T_total", "cu_seqlens", "x", "y", "y_dtype",
                                               "initial_state", "conv_state_out", "state_slots",
-                                              "num_slots"]),
+                                              "num_slots", "status"]),
               "gdn_layer_decode_io": (gdn.CLayerDecodeIO, ["B", "x", "y", "y_dtype", "state_in",
                                                            "conv_state_out", "state_slots",
-                                                           "num_slots"])}
+                                                           "num_slots", "status"])}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gdn.h"', "int main(void) {"]
     for name, (_, fields) in checks.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
