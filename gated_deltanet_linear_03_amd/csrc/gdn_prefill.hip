@@ -37,25 +37,36 @@ namespace gdn {
 // Chunk table: chunk_off[n] = sum_{m<n} ceil(L_m / C), chunk_off[N] = total
 // chunks (chunks restart at each sequence start, so results do not depend on
 // the packing).  Each work-group of the first prep window derives the total
-// and its own slot's sequence from cu_seqlens with a block-wide scan; the one
-// given `out` also stores the table for the kernels after it.  `scratch`:
-// NT / 64 + 2 ints of LDS.
+// and its own slot's sequence from cu_seqlens with a block-wide scan,
+// checking on the way that cu_seqlens starts at 0, never decreases and ends
+// at T_total and that pool entries lie in [0, num_slots) (every work-group
+// reads the same values, so all reach the same verdict); the one given `out`
+// also stores the table for the kernels after it.  `scratch`: NT / 64 + 2
+// ints of LDS.
 // ---------------------------------------------------------------------------
 struct ChunkPos {
     int total;   // chunks of the batch
     int n;       // sequence owning the slot (when slot < total)
     int first;   // its first chunk
+    bool bad;    // the indices broke their contract: nothing else is set
 };
 
 template <int NT>
-__device__ ChunkPos chunk_table(const int32_t* cu, int N, int C, int slot, int32_t* scratch,
-                                int32_t* out) {
+__device__ ChunkPos chunk_table(const PrefillParams& p, int C, int slot, int32_t* scratch, int32_t* out) {
     constexpr int NW = NT / kWave;
+    const int N = p.N;
+    const int32_t* cu = p.cu;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int per = (N + NT - 1) / NT;
     const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
+    bool bad = tid == 0 && (cu[0] != 0 || static_cast<int64_t>(cu[N]) != p.T);
     int s = 0;
-    for (int m = n0; m < n1; ++m) s += (cu[m + 1] - cu[m] + C - 1) / C;
+    for (int m = n0; m < n1; ++m) {
+        const int32_t a = cu[m], b = cu[m + 1];
+        bad |= b < a;
+        if (p.slots) bad |= static_cast<unsigned>(p.slots[m]) >= static_cast<unsigned>(p.num_slots);
+        s += (b - a + C - 1) / C;
+    }
     int incl = s;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -63,7 +74,9 @@ __device__ ChunkPos chunk_table(const int32_t* cu, int N, int C, int slot, int32
         if (lane >= off) incl += u;
     }
     if (lane == kWave - 1) scratch[wave] = incl;
-    __syncthreads();
+    ChunkPos r;
+    r.bad = __syncthreads_or(bad);
+    if (r.bad) return r;
     int acc = incl - s, total = 0;
     for (int w = 0; w < NW; ++w) {
         const int v = scratch[w];
@@ -81,7 +94,6 @@ __device__ ChunkPos chunk_table(const int32_t* cu, int N, int C, int slot, int32
     }
     if (out && tid == 0) out[N] = total;
     __syncthreads();
-    ChunkPos r;
     r.total = total;
     r.n = scratch[NW];
     r.first = scratch[NW + 1];

@@ -225,19 +225,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
         // the call's first kernel: clear the caller's status word
         const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
         if (p.status && lead && threadIdx.x == 0) *p.status = 0;
-        // The device-side indices: cu_seqlens starts at 0, never decreases
-        // and ends at T_total, and pool entries lie in [0, num_slots).  Every
-        // work-group reads the same values and reaches the same verdict.  On
-        // a bad one nothing is computed: the chunk table's total becomes -1,
-        // which every later kernel of the call takes as "return at once",
-        // and the status word gets kStatusBadIndex.
-        bool bad = false;
-        for (int m = tid; m < p.N; m += NT) {
-            bad |= p.cu[m + 1] < p.cu[m];
-            if (p.slots) bad |= static_cast<unsigned>(p.slots[m]) >= static_cast<unsigned>(p.num_slots);
-        }
-        if (tid == 0) bad |= p.cu[0] != 0 || static_cast<int64_t>(p.cu[p.N]) != p.T;
-        if (__syncthreads_or(bad)) {
+        const ChunkPos cp = chunk_table<kPrepThreads>(p, C, slot, reinterpret_cast<int32_t*>(smem + S::oS),
+                                                      lead ? p.chunk_off : nullptr);
+        if (cp.bad) {
+            // The device-side indices broke their contract (cu_seqlens not
+            // starting at 0, decreasing or not ending at T_total; a pool
+            // entry outside [0, num_slots)).  Nothing is computed: the chunk
+            // table's total becomes -1, which every later kernel of the call
+            // takes as "return at once", and the status word gets
+            // kStatusBadIndex.
             if (lead && tid == 0) {
                 p.chunk_off[p.N] = -1;
                 if (p.status)
@@ -245,8 +241,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p) {
             }
             return;
         }
-        const ChunkPos cp = chunk_table<kPrepThreads>(p.cu, p.N, C, slot, reinterpret_cast<int32_t*>(smem + S::oS),
-                                                      blockIdx.x == 0 && blockIdx.y == 0 ? p.chunk_off : nullptr);
         total = cp.total;
         n = cp.n;
         first = cp.first;
