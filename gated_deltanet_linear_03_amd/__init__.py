@@ -30,6 +30,10 @@ GDN_DTYPE_FP32 = 0
 GDN_DTYPE_BF16 = 1
 GDN_STATUS_NONFINITE = 1
 GDN_STATUS_BAD_INDEX = 2
+GDN_GEMM_AUTO = 0
+GDN_GEMM_TILED = 1
+GDN_GEMM_FEW_ROWS = 2
+GDN_GEMM_LIBRARY = 3
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
@@ -37,7 +41,7 @@ EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_snapshot_restore", "gdn_gemm_bf16", "gdn_layer_prefill_workspace_bytes",
            "gdn_layer_prefill", "gdn_layer_decode_workspace_bytes", "gdn_layer_decode",
            "gdn_status_string", "gdn_last_error", "gdn_selftest_mfma", "gdn_prefill_noalloc",
-           "gdn_prefill_window_slots", "gdn_decode_workspace_bytes")
+           "gdn_prefill_window_slots", "gdn_decode_workspace_bytes", "gdn_gemm_bf16_path")
 NOALLOC_SCRATCH_BYTES = 128 << 20       # GDN_NOALLOC_SCRATCH_BYTES
 SNAPSHOT_MAGIC = 0x50534E47
 SNAPSHOT_VERSION = 1
@@ -178,6 +182,10 @@ def lib():
         L.gdn_gemm_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        L.gdn_gemm_bf16_path.restype = ctypes.c_int
+        L.gdn_gemm_bf16_path.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
         L.gdn_layer_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_prefill_workspace_bytes.argtypes = [ctypes.POINTER(CLayer), ctypes.POINTER(CProj),
                                                         ctypes.c_int32, ctypes.c_int64]
@@ -628,9 +636,10 @@ def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
     return res
 
 
-def gemm_bf16(A, B, C, stream=None):
+def gemm_bf16(A, B, C, stream=None, path=None):
     """C[M, N] = A[M, K] @ B[N, K]^T on the matrix cores: A, B bf16 device
-    tensors (rows may be strided), C bf16 or fp32."""
+    tensors (rows may be strided), C bf16 or fp32.  path: None (as
+    gdn_gemm_bf16) or one of GDN_GEMM_AUTO / TILED / FEW_ROWS / LIBRARY."""
     import torch
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[0])
@@ -638,8 +647,12 @@ def gemm_bf16(A, B, C, stream=None):
     _need(B, "B", N, K, 2)
     _need(C, "C", M, N)
     cd = GDN_DTYPE_BF16 if C.dtype == torch.bfloat16 else GDN_DTYPE_FP32
-    _check(lib().gdn_gemm_bf16(_ptr(A), int(A.stride(0)), _ptr(B), int(B.stride(0)), _ptr(C),
-                               int(C.stride(0)), cd, M, N, K, _stream(stream)))
+    if path is None:
+        _check(lib().gdn_gemm_bf16(_ptr(A), int(A.stride(0)), _ptr(B), int(B.stride(0)), _ptr(C),
+                                   int(C.stride(0)), cd, M, N, K, _stream(stream)))
+    else:
+        _check(lib().gdn_gemm_bf16_path(_ptr(A), int(A.stride(0)), _ptr(B), int(B.stride(0)), _ptr(C),
+                                        int(C.stride(0)), cd, M, N, K, int(path), _stream(stream)))
 
 
 @dataclass

@@ -131,6 +131,9 @@ extern "C" {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 static_assert(gdn::kStatusBadIndex == GDN_STATUS_BAD_INDEX, "status bits of the kernels and the header");
+static_assert(gdn::kGemmAuto == GDN_GEMM_AUTO && gdn::kGemmTiled == GDN_GEMM_TILED &&
+                  gdn::kGemmSkinny == GDN_GEMM_FEW_ROWS && gdn::kGemmLibrary == GDN_GEMM_LIBRARY,
+              "GEMM paths of the kernels and the header");
 
 const char* gdn_status_string(gdn_status st) {
     switch (st) {
@@ -536,7 +539,13 @@ gdn_status gdn_decode_multi(const gdn_layer* L, const gdn_decode_io* io, int32_t
 
 gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                          int32_t c_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    return gdn_gemm_bf16_path(A, lda, B, ldb, C, ldc, c_dtype, M, N, K, GDN_GEMM_AUTO, stream);
+}
+
+gdn_status gdn_gemm_bf16_path(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                              int32_t c_dtype, int64_t M, int64_t N, int64_t K, int32_t path, void* stream) {
     g_err[0] = 0;
+    if (path < GDN_GEMM_AUTO || path > GDN_GEMM_LIBRARY) return fail(GDN_ERR_INVALID_ARGUMENT, "path %d unknown", path);
     if (M < 0 || N < 0 || K < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "M, N, K must be >= 0");
     if (c_dtype != GDN_DTYPE_BF16 && c_dtype != GDN_DTYPE_FP32)
         return fail(GDN_ERR_INVALID_ARGUMENT, "c_dtype %d unknown", c_dtype);
@@ -547,7 +556,7 @@ gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
     if (lda < K || ldb < K || ldc < N) return fail(GDN_ERR_INVALID_ARGUMENT, "leading dimension below the row length");
     if (!aligned(C, c_dtype == GDN_DTYPE_BF16 ? 2 : 4)) return fail(GDN_ERR_INVALID_ARGUMENT, "C misaligned");
     hipError_t e = gdn::launch_gemm_bf16_nt(A, lda, B, ldb, C, ldc, c_dtype == GDN_DTYPE_BF16, M, N, K,
-                                            static_cast<hipStream_t>(stream));
+                                            static_cast<hipStream_t>(stream), static_cast<gdn::GemmPath>(path));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "gemm launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }
@@ -656,15 +665,15 @@ gdn_status gdn_layer_prefill(const gdn_layer* L, const gdn_proj* pr, const gdn_l
     if (st != GDN_OK) return st;
     if (T == 0) return prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // the tiled kernel at every T: a sequence's bits do not depend on how
-    // many tokens share the call
+    // one kernel family at every T (the library's pinned algorithm): a
+    // sequence's bits do not depend on how many tokens share the call
     hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, T, w.P,
-                                            pr->hidden, s, gdn::kGemmTiled);
+                                            pr->hidden, s, gdn::kGemmLibrary);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
     st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
     if (st != GDN_OK) return st;
     e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, T,
-                                 pr->hidden, HD, s, gdn::kGemmTiled);
+                                 pr->hidden, HD, s, gdn::kGemmLibrary);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }

@@ -455,6 +455,10 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
         }
 #undef GDN_SKINNY
     }
+    if (path == kGemmAuto || path == kGemmLibrary) {
+        hipError_t e = hipSuccess;
+        if (gemm_library(A, lda, B, ldb, C, ldc, out_bf16, M, N, K, s, &e)) return e;
+    }
     const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
     if (wide >= cus) return launch_gemm_t<256, 256>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);
     return launch_gemm_t<256, 128>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);

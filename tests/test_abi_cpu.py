@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(_declared()) <= set(gdn.EXPORTS) | {"gdn_selftest_mfma"}
-    assert L.gdn_abi_version() == 12
+    assert L.gdn_abi_version() == 13
 
 
 def test_status_strings():
@@ -618,6 +618,18 @@ def test_gemm_rejects(kw, msg):
     st = gdn.lib().gdn_gemm_bf16(args["A"], args["lda"], args["B"], args["ldb"], args["C"],
                                  args["ldc"], args["c_dtype"], args["M"], args["N"], args["K"], None)
     assert st == gdn.GDN_ERR_INVALID_ARGUMENT and msg in gdn.lib().gdn_last_error().decode()
+
+
+def test_gemm_path_rejects_unknown_and_validates_first():
+    """gdn_gemm_bf16_path refuses an unknown kernel family, and every family
+    goes through the same argument checks before anything runs."""
+    args = (FAKE, 16, FAKE, 16, FAKE, 8, gdn.GDN_DTYPE_FP32, 4, 8, 16)
+    for path in (-1, 4):
+        assert gdn.lib().gdn_gemm_bf16_path(*args, path, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+        assert b"path" in gdn.lib().gdn_last_error()
+    for path in (gdn.GDN_GEMM_AUTO, gdn.GDN_GEMM_TILED, gdn.GDN_GEMM_FEW_ROWS, gdn.GDN_GEMM_LIBRARY):
+        bad = (FAKE, 16, FAKE, 16, FAKE, 8, gdn.GDN_DTYPE_FP32, 4, 8, 12)      # K not a multiple of 8
+        assert gdn.lib().gdn_gemm_bf16_path(*bad, path, None) == gdn.GDN_ERR_INVALID_ARGUMENT
 
 
 def test_layer_workspace_and_rejects():

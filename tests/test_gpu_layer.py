@@ -23,38 +23,49 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
 
 
+PATHS = [None, gdn.GDN_GEMM_TILED, gdn.GDN_GEMM_FEW_ROWS, gdn.GDN_GEMM_LIBRARY]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["auto", "tiled", "few_rows", "library"])
 @pytest.mark.parametrize("M, N, K", [(300, 200, 136), (1, 392, 64), (257, 12352, 2048),
                                      (64, 2048, 4096), (17, 12352, 2048), (40, 100, 200),
                                      (3, 2056, 4104)])
-def test_gemm_matches_fp64(M, N, K):
+def test_gemm_matches_fp64(M, N, K, path):
     r = np.random.default_rng(M + N + K)
     A = synth.bf16_round(r.standard_normal((M, K)).astype(np.float32))
     B = synth.bf16_round((r.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
     ref = A.astype(np.float64) @ B.astype(np.float64).T
     C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     C16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    gdn.gemm_bf16(_bf16(A), _bf16(B), C32)
-    gdn.gemm_bf16(_bf16(A), _bf16(B), C16)
+    gdn.gemm_bf16(_bf16(A), _bf16(B), C32, path=path)
+    gdn.gemm_bf16(_bf16(A), _bf16(B), C16, path=path)
     torch.cuda.synchronize()
     got = C32.cpu().numpy().astype(np.float64)
     # fp32 accumulation of K exact products: a few ulp of the largest partial sum
     bound = 4 * K * 2.0 ** -24 * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T)
     assert np.all(np.abs(got - ref) <= bound + 1e-30)
-    # bf16 output: the nearest bf16 of the fp32 result
-    assert torch.equal(C16.float(), C32.to(torch.bfloat16).float())
+    if path == gdn.GDN_GEMM_LIBRARY or (path is None and M > 64):
+        # the library may pick another algorithm for a bf16 C: its result is
+        # a rounding of some fp32 sum within the same bound
+        g16 = C16.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(g16 - ref) <= bound + 2.0 ** -8 * np.abs(ref) + 1e-30)
+    else:
+        # bf16 output: the nearest bf16 of the fp32 result
+        assert torch.equal(C16.float(), C32.to(torch.bfloat16).float())
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["auto", "tiled", "few_rows", "library"])
 @pytest.mark.parametrize("M", [130, 7])
-def test_gemm_strided_rows(M):
+def test_gemm_strided_rows(M, path):
     """Row strides beyond K (views into wider buffers); 7 rows take the
-    few-row kernel."""
+    few-row kernel by default."""
     r = np.random.default_rng(3)
     N, K = 70, 96
     Aw = _bf16(r.standard_normal((M, K + 24)))
     Bw = _bf16(r.standard_normal((N, K + 8)))
     A, B = Aw[:, 8:8 + K], Bw[:, :K]
     Cw = torch.zeros((M, N + 5), dtype=torch.float32, device="cuda")
-    gdn.gemm_bf16(A, B, Cw[:, :N])
+    gdn.gemm_bf16(A, B, Cw[:, :N], path=path)
     torch.cuda.synchronize()
     ref = A.float().cpu().double() @ B.float().cpu().double().T
     assert torch.allclose(Cw[:, :N].cpu().double(), ref, rtol=1e-5, atol=1e-5)
@@ -76,6 +87,29 @@ def test_gemm_few_rows_batch_invariant():
         gdn.gemm_bf16(A[rows[0]:rows[1]], B, part)
         torch.cuda.synchronize()
         assert torch.equal(part, full[rows[0]:rows[1]]), rows
+
+
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+@pytest.mark.parametrize("N, K", [(12352, 2048), (2048, 4096)])
+def test_gemm_library_rows_do_not_depend_on_m(N, K, out):
+    """The library path (gdn_layer_prefill's projections) keeps one algorithm
+    per shape: every row's bits are those of the 4096-row product, at any
+    number of rows, and repeat calls give the same bits."""
+    r = np.random.default_rng(N + K)
+    A = _bf16(r.standard_normal((4096, K)))
+    B = _bf16(r.standard_normal((N, K)) / np.sqrt(K))
+    dt = torch.float32 if out == "fp32" else torch.bfloat16
+    full = torch.empty((4096, N), dtype=dt, device="cuda")
+    gdn.gemm_bf16(A, B, full, path=gdn.GDN_GEMM_LIBRARY)
+    again = torch.empty_like(full)
+    gdn.gemm_bf16(A, B, again, path=gdn.GDN_GEMM_LIBRARY)
+    torch.cuda.synchronize()
+    assert torch.equal(full, again)
+    for m in (1, 3, 64, 65, 300, 4095):
+        part = torch.empty((m, N), dtype=dt, device="cuda")
+        gdn.gemm_bf16(A[:m], B, part, path=gdn.GDN_GEMM_LIBRARY)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[:m]), m
 
 
 def _layer_case(sh, hidden, lens, seed, with_states):
