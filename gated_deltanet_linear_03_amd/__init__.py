@@ -34,6 +34,7 @@ GDN_GEMM_AUTO = 0
 GDN_GEMM_TILED = 1
 GDN_GEMM_FEW_ROWS = 2
 GDN_GEMM_LIBRARY = 3
+GDN_GEMM_LIBRARY_FEW_ROWS = 4
 
 EXPORTS = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill",
            "gdn_prefill_timed", "gdn_prefill_launches", "gdn_decode", "gdn_decode_multi",
@@ -639,7 +640,8 @@ def decode(layer: Layer, q, k, v, z, a, b, state, conv_state, in_place=True,
 def gemm_bf16(A, B, C, stream=None, path=None):
     """C[M, N] = A[M, K] @ B[N, K]^T on the matrix cores: A, B bf16 device
     tensors (rows may be strided), C bf16 or fp32.  path: None (as
-    gdn_gemm_bf16) or one of GDN_GEMM_AUTO / TILED / FEW_ROWS / LIBRARY."""
+    gdn_gemm_bf16) or one of GDN_GEMM_AUTO / TILED / FEW_ROWS / LIBRARY /
+    LIBRARY_FEW_ROWS."""
     import torch
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[0])

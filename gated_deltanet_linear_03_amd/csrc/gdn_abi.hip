@@ -132,7 +132,8 @@ extern "C" {
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 static_assert(gdn::kStatusBadIndex == GDN_STATUS_BAD_INDEX, "status bits of the kernels and the header");
 static_assert(gdn::kGemmAuto == GDN_GEMM_AUTO && gdn::kGemmTiled == GDN_GEMM_TILED &&
-                  gdn::kGemmSkinny == GDN_GEMM_FEW_ROWS && gdn::kGemmLibrary == GDN_GEMM_LIBRARY,
+                  gdn::kGemmSkinny == GDN_GEMM_FEW_ROWS && gdn::kGemmLibrary == GDN_GEMM_LIBRARY &&
+                  gdn::kGemmLibraryFew == GDN_GEMM_LIBRARY_FEW_ROWS,
               "GEMM paths of the kernels and the header");
 
 const char* gdn_status_string(gdn_status st) {
@@ -545,7 +546,7 @@ gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
 gdn_status gdn_gemm_bf16_path(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                               int32_t c_dtype, int64_t M, int64_t N, int64_t K, int32_t path, void* stream) {
     g_err[0] = 0;
-    if (path < GDN_GEMM_AUTO || path > GDN_GEMM_LIBRARY) return fail(GDN_ERR_INVALID_ARGUMENT, "path %d unknown", path);
+    if (path < GDN_GEMM_AUTO || path > GDN_GEMM_LIBRARY_FEW_ROWS) return fail(GDN_ERR_INVALID_ARGUMENT, "path %d unknown", path);
     if (M < 0 || N < 0 || K < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "M, N, K must be >= 0");
     if (c_dtype != GDN_DTYPE_BF16 && c_dtype != GDN_DTYPE_FP32)
         return fail(GDN_ERR_INVALID_ARGUMENT, "c_dtype %d unknown", c_dtype);
@@ -737,15 +738,15 @@ gdn_status gdn_layer_decode(const gdn_layer* L, const gdn_proj* pr, const gdn_la
     st = decode_impl(&Lg, &dio, 0, nullptr, stream, false);
     if (st != GDN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // the few-row kernel at every B: a sequence's bits do not depend on the
-    // batch size
+    // one kernel family at every B (the library's algorithm pinned at 64
+    // rows): a sequence's bits do not depend on the batch size
     hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, B, w.P,
-                                            pr->hidden, s, gdn::kGemmSkinny);
+                                            pr->hidden, s, gdn::kGemmLibraryFew);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
     st = decode_impl(&Lg, &dio, 0, nullptr, stream);
     if (st != GDN_OK) return st;
     e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, B,
-                                 pr->hidden, HD, s, gdn::kGemmSkinny);
+                                 pr->hidden, HD, s, gdn::kGemmLibraryFew);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "out_proj launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }

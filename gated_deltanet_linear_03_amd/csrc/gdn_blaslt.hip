@@ -4,14 +4,20 @@
 // fp32 out) is, in the library's column-major terms, C^T (N x M) = op_T(B)
 // op_N(A) with B stored as a K x N and A as a K x M column-major matrix.
 //
-// One algorithm per (device, N, K, leading dimensions, output type): the
-// first of the library's ranked choices for that shape at kPinRows rows
-// that needs no workspace (so no split of K over work-groups; some library
-// versions rank such a split first even when asked for no workspace).  It is then used at every
-// M, so an output element is summed in the same order whatever the number
-// of rows (a row's bits do not depend on the batch), and the choice does not
-// depend on timing, so it is the same in every process on the same library
-// and device.  Only the library's C interface is used.
+// One algorithm per (device, N, K, leading dimensions, output type, pinning
+// size): the first of the library's ranked choices for that shape at the
+// pinning size in rows (4096 for the prefill projections, 64 for the decode
+// ones) that needs no workspace (so no split of K over work-groups; some library
+// versions rank such a split first even when asked for no workspace).  It is
+// then used at every M, so an output element is summed in the same order
+// whatever the number of rows (a row's bits do not depend on the batch), and
+// the choice does not depend on timing, so it is the same in every process on
+// the same library and device.  The algorithm's fitness (and its need of no
+// workspace) is only established up to the size it was chosen at, and the
+// library does not check a caller's algorithm against a larger problem, so a
+// product with more rows runs in blocks of at most that many rows; rows are
+// independent, so blocking changes no bit.  Only the library's C interface is
+// used.
 #include <hipblaslt/hipblaslt.h>
 
 #include <map>
@@ -24,15 +30,15 @@ namespace gdn {
 
 namespace {
 
-constexpr int64_t kPinRows = 4096;
 constexpr int kRanked = 16;          // ranked choices looked through
 
 struct PlanKey {
     int dev;
-    int64_t n, k, lda, ldb, ldc;
+    int64_t n, k, lda, ldb, ldc, pin;
     bool bf16;
     bool operator<(const PlanKey& o) const {
-        return std::tie(dev, n, k, lda, ldb, ldc, bf16) < std::tie(o.dev, o.n, o.k, o.lda, o.ldb, o.ldc, o.bf16);
+        return std::tie(dev, n, k, lda, ldb, ldc, pin, bf16) <
+               std::tie(o.dev, o.n, o.k, o.lda, o.ldb, o.ldc, o.pin, o.bf16);
     }
 };
 
@@ -79,7 +85,7 @@ Plan make_plan(hipblasLtHandle_t h, const PlanKey& key) {
             HIPBLAS_STATUS_SUCCESS &&
         hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) ==
             HIPBLAS_STATUS_SUCCESS &&
-        make_layouts(kPinRows, key, l);
+        make_layouts(key.pin, key, l);
     if (!ok) {
         hipblasLtMatmulDescDestroy(p.desc);
         return Plan{};
@@ -107,7 +113,8 @@ Plan make_plan(hipblasLtHandle_t h, const PlanKey& key) {
 }  // namespace
 
 bool gemm_library(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                  bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s, hipError_t* err) {
+                  bool out_bf16, int64_t M, int64_t N, int64_t K, int64_t pin_rows, hipStream_t s,
+                  hipError_t* err) {
     *err = hipSuccess;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
@@ -120,18 +127,27 @@ bool gemm_library(const void* A, int64_t lda, const void* B, int64_t ldb, void* 
     }
     hipblasLtHandle_t h = hit->second;
     if (!h) return false;
-    const PlanKey key{dev, N, K, lda, ldb, ldc, out_bf16};
+    const PlanKey key{dev, N, K, lda, ldb, ldc, pin_rows, out_bf16};
     auto pit = g_plans.find(key);
     if (pit == g_plans.end()) pit = g_plans.emplace(key, make_plan(h, key)).first;
     Plan& plan = pit->second;
     if (!plan.ok) return false;
-    hipblasLtMatrixLayout_t l[3];
-    if (!make_layouts(M, key, l)) return false;
     const float alpha = 1.f, beta = 0.f;
-    const hipblasStatus_t st = hipblasLtMatmul(h, plan.desc, &alpha, B, l[0], A, l[1], &beta, C, l[2], C, l[2],
-                                               &plan.algo, nullptr, 0, s);
-    drop_layouts(l);
-    return st == HIPBLAS_STATUS_SUCCESS;
+    const size_t c_elem = out_bf16 ? 2 : 4;
+    for (int64_t m0 = 0; m0 < M; m0 += pin_rows) {
+        const int64_t mb = M - m0 < pin_rows ? M - m0 : pin_rows;
+        hipblasLtMatrixLayout_t l[3];
+        if (!make_layouts(mb, key, l)) return m0 == 0 ? false : (*err = hipErrorUnknown, true);
+        const void* a = static_cast<const uint16_t*>(A) + m0 * lda;
+        void* c = static_cast<uint8_t*>(C) + static_cast<size_t>(m0 * ldc) * c_elem;
+        const hipblasStatus_t st =
+            hipblasLtMatmul(h, plan.desc, &alpha, B, l[0], a, l[1], &beta, c, l[2], c, l[2], &plan.algo, nullptr, 0, s);
+        drop_layouts(l);
+        // the library declining the first block leaves room for another
+        // family; a later refusal leaves rows already written, so it is an error
+        if (st != HIPBLAS_STATUS_SUCCESS) return m0 == 0 ? false : (*err = hipErrorUnknown, true);
+    }
+    return true;
 }
 
 }  // namespace gdn

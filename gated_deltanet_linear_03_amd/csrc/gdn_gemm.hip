@@ -428,7 +428,12 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (path == kGemmSkinny || (path == kGemmAuto && M <= kSkinnyMax)) {
+    const bool few = path == kGemmSkinny || path == kGemmLibraryFew || (path == kGemmAuto && M <= kSkinnyMax);
+    if (path == kGemmLibraryFew || (path == kGemmAuto && M <= kSkinnyMax)) {
+        hipError_t e = hipSuccess;
+        if (gemm_library(A, lda, B, ldb, C, ldc, out_bf16, M, N, K, kSkinnyMax, s, &e)) return e;
+    }
+    if (few) {
         // few rows (A rows and lda are 16-byte aligned, K a multiple of 8)
         // With n tiles to spare (at least two per compute unit) K is split
         // over 4 waves and, past 16 rows, a work-group takes 4 n tiles so
@@ -457,7 +462,7 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
     }
     if (path == kGemmAuto || path == kGemmLibrary) {
         hipError_t e = hipSuccess;
-        if (gemm_library(A, lda, B, ldb, C, ldc, out_bf16, M, N, K, s, &e)) return e;
+        if (gemm_library(A, lda, B, ldb, C, ldc, out_bf16, M, N, K, 4096, s, &e)) return e;
     }
     const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
     if (wide >= cus) return launch_gemm_t<256, 256>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);

@@ -141,20 +141,26 @@ hipError_t launch_selftest_mfma(const float* A, const float* B, float* C, hipStr
 // output element in an order that depends on K (and, for the few-row one,
 // on N) but never on M, so a row's bits are independent of the other rows
 // as long as the family is fixed:
-//   kGemmAuto     the few-row kernel up to 64 rows, else the library path
-//   kGemmTiled    always this library's tiled kernel
-//   kGemmSkinny   always the few-row kernel, over 64-row blocks (the layer's
-//                 decode projections, at any batch size)
-//   kGemmLibrary  hipBLASLt with one algorithm per shape, at every M (the
-//                 layer's prefill projections); the tiled kernel where the
-//                 library declines (no handle, no algorithm for the shape)
+//   kGemmAuto        up to 64 rows kGemmLibraryFew, else kGemmLibrary
+//   kGemmTiled       always this library's tiled kernel
+//   kGemmSkinny      always this library's few-row kernel, over 64-row
+//                    blocks
+//   kGemmLibrary     hipBLASLt with one algorithm per shape, chosen at 4096
+//                    rows and used at every M (the layer's prefill
+//                    projections); the tiled kernel where the library
+//                    declines (no handle, no algorithm for the shape)
+//   kGemmLibraryFew  the same with the algorithm chosen at 64 rows (the
+//                    layer's decode projections, at any batch size); the
+//                    few-row kernel where the library declines
 // The values are those of GDN_GEMM_* in gdn.h.
-enum GemmPath { kGemmAuto = 0, kGemmTiled = 1, kGemmSkinny = 2, kGemmLibrary = 3 };
+enum GemmPath { kGemmAuto = 0, kGemmTiled = 1, kGemmSkinny = 2, kGemmLibrary = 3, kGemmLibraryFew = 4 };
 
-// The library path (gdn_blaslt.hip): true when the product was enqueued
-// (*err the launch status), false when the library declines it.
+// The library path (gdn_blaslt.hip) with its algorithm chosen at pin_rows
+// rows: true when the product was enqueued (*err the launch status), false
+// when the library declines it.
 bool gemm_library(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                  bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s, hipError_t* err);
+                  bool out_bf16, int64_t M, int64_t N, int64_t K, int64_t pin_rows, hipStream_t s,
+                  hipError_t* err);
 
 // C[M][N] = A[M][K] B[N][K]^T, bf16 in, fp32 accumulation, bf16 or fp32 out
 hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,

@@ -318,10 +318,10 @@ gdn_status gdn_decode_multi(const gdn_layer* layer, const gdn_decode_io* io,
 /* C[M][N] = A[M][K] * B[N][K]^T: A, B bf16 (k contiguous, leading dims lda,
  * ldb in elements), C in c_dtype (GDN_DTYPE_BF16 or GDN_DTYPE_FP32, leading
  * dim ldc), fp32 accumulation.  K, lda, ldb multiples of 8 and A, B 16-byte
- * aligned; M, N, K >= 0.  Enqueued on `stream`.  Up to 64 rows run on a
- * weight-streaming few-row kernel, more on the library path (below); each
- * sums an output in an order that depends on K and N only, but the orders
- * differ, so a row's bits may change when M crosses 64.  gdn_layer_prefill
+ * aligned; M, N, K >= 0.  Enqueued on `stream`.  Up to 64 rows run on the
+ * library path pinned at 64 rows, more on the one pinned at 4096 (below);
+ * each sums an output in an order that depends on K and N only, but the
+ * orders may differ, so a row's bits may change when M crosses 64.  gdn_layer_prefill
  * and gdn_layer_decode each keep to one kernel family at every size, so
  * their results do not depend on the batch. */
 gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -331,18 +331,26 @@ gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
 /* gdn_gemm_bf16 on a chosen kernel family:
  *   GDN_GEMM_AUTO       as gdn_gemm_bf16
  *   GDN_GEMM_TILED      this library's tiled kernel (256-row tiles)
- *   GDN_GEMM_FEW_ROWS   the weight-streaming few-row kernel, over 64-row
- *                       blocks at any M (gdn_layer_decode's projections)
+ *   GDN_GEMM_FEW_ROWS   this library's weight-streaming few-row kernel,
+ *                       over 64-row blocks at any M
  *   GDN_GEMM_LIBRARY    hipBLASLt (the vendor's GEMM library; plain GEMMs
  *                       are its job) with one algorithm per (device, N, K,
  *                       leading dimensions, C type): the first of its
  *                       ranked choices at 4096 rows that needs no
- *                       workspace, kept for the life of
- *                       the process and used at every M, so a row's bits do
- *                       not depend on M and, on the same library and
- *                       device, not on the process either
- *                       (gdn_layer_prefill's projections).  Where the
- *                       library declines a shape the tiled kernel runs.
+ *                       workspace, kept for the life of the process and
+ *                       used at every M (a larger M in blocks of 4096
+ *                       rows: an algorithm is only known to fit the size
+ *                       it was ranked at), so a row's bits do not depend
+ *                       on M and, on the same library and device, not on
+ *                       the process either (gdn_layer_prefill's
+ *                       projections).
+ *                       Where the library declines a shape the tiled
+ *                       kernel runs.
+ *   GDN_GEMM_LIBRARY_FEW_ROWS  the same with the algorithm chosen at 64
+ *                       rows and run in blocks of 64 rows
+ *                       (gdn_layer_decode's projections, at any batch
+ *                       size); the few-row kernel where the library
+ *                       declines.
  * The library path keeps a hipBLASLt handle per device for the life of the
  * process; its first call on a device and shape must not be under graph
  * capture (it loads the algorithm's code).  An unknown path:
@@ -351,6 +359,7 @@ gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
 #define GDN_GEMM_TILED 1
 #define GDN_GEMM_FEW_ROWS 2
 #define GDN_GEMM_LIBRARY 3
+#define GDN_GEMM_LIBRARY_FEW_ROWS 4
 gdn_status gdn_gemm_bf16_path(const void* A, int64_t lda, const void* B, int64_t ldb,
                               void* C, int64_t ldc, int32_t c_dtype, int64_t M,
                               int64_t N, int64_t K, int32_t path, void* stream);

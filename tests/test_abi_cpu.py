@@ -624,10 +624,11 @@ def test_gemm_path_rejects_unknown_and_validates_first():
     """gdn_gemm_bf16_path refuses an unknown kernel family, and every family
     goes through the same argument checks before anything runs."""
     args = (FAKE, 16, FAKE, 16, FAKE, 8, gdn.GDN_DTYPE_FP32, 4, 8, 16)
-    for path in (-1, 4):
+    for path in (-1, 5):
         assert gdn.lib().gdn_gemm_bf16_path(*args, path, None) == gdn.GDN_ERR_INVALID_ARGUMENT
         assert b"path" in gdn.lib().gdn_last_error()
-    for path in (gdn.GDN_GEMM_AUTO, gdn.GDN_GEMM_TILED, gdn.GDN_GEMM_FEW_ROWS, gdn.GDN_GEMM_LIBRARY):
+    for path in (gdn.GDN_GEMM_AUTO, gdn.GDN_GEMM_TILED, gdn.GDN_GEMM_FEW_ROWS, gdn.GDN_GEMM_LIBRARY,
+                 gdn.GDN_GEMM_LIBRARY_FEW_ROWS):
         bad = (FAKE, 16, FAKE, 16, FAKE, 8, gdn.GDN_DTYPE_FP32, 4, 8, 12)      # K not a multiple of 8
         assert gdn.lib().gdn_gemm_bf16_path(*bad, path, None) == gdn.GDN_ERR_INVALID_ARGUMENT
 

@@ -23,10 +23,11 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
 
 
-PATHS = [None, gdn.GDN_GEMM_TILED, gdn.GDN_GEMM_FEW_ROWS, gdn.GDN_GEMM_LIBRARY]
+PATHS = [None, gdn.GDN_GEMM_TILED, gdn.GDN_GEMM_FEW_ROWS, gdn.GDN_GEMM_LIBRARY, gdn.GDN_GEMM_LIBRARY_FEW_ROWS]
+PATH_IDS = ["auto", "tiled", "few_rows", "library", "library_few"]
 
 
-@pytest.mark.parametrize("path", PATHS, ids=["auto", "tiled", "few_rows", "library"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("M, N, K", [(300, 200, 136), (1, 392, 64), (257, 12352, 2048),
                                      (64, 2048, 4096), (17, 12352, 2048), (40, 100, 200),
                                      (3, 2056, 4104)])
@@ -44,7 +45,7 @@ def test_gemm_matches_fp64(M, N, K, path):
     # fp32 accumulation of K exact products: a few ulp of the largest partial sum
     bound = 4 * K * 2.0 ** -24 * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T)
     assert np.all(np.abs(got - ref) <= bound + 1e-30)
-    if path == gdn.GDN_GEMM_LIBRARY or (path is None and M > 64):
+    if path in (gdn.GDN_GEMM_LIBRARY, gdn.GDN_GEMM_LIBRARY_FEW_ROWS) or path is None:
         # the library may pick another algorithm for a bf16 C: its result is
         # a rounding of some fp32 sum within the same bound
         g16 = C16.float().cpu().numpy().astype(np.float64)
@@ -54,7 +55,7 @@ def test_gemm_matches_fp64(M, N, K, path):
         assert torch.equal(C16.float(), C32.to(torch.bfloat16).float())
 
 
-@pytest.mark.parametrize("path", PATHS, ids=["auto", "tiled", "few_rows", "library"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("M", [130, 7])
 def test_gemm_strided_rows(M, path):
     """Row strides beyond K (views into wider buffers); 7 rows take the
@@ -89,25 +90,31 @@ def test_gemm_few_rows_batch_invariant():
         assert torch.equal(part, full[rows[0]:rows[1]]), rows
 
 
+@pytest.mark.parametrize("path", [gdn.GDN_GEMM_LIBRARY, gdn.GDN_GEMM_LIBRARY_FEW_ROWS],
+                         ids=["library", "library_few"])
 @pytest.mark.parametrize("out", ["fp32", "bf16"])
 @pytest.mark.parametrize("N, K", [(12352, 2048), (2048, 4096)])
-def test_gemm_library_rows_do_not_depend_on_m(N, K, out):
-    """The library path (gdn_layer_prefill's projections) keeps one algorithm
-    per shape: every row's bits are those of the 4096-row product, at any
-    number of rows, and repeat calls give the same bits."""
+def test_gemm_library_rows_do_not_depend_on_m(N, K, out, path):
+    """The library paths (the layer's prefill and decode projections) keep
+    one algorithm per shape: every row's bits are those of the largest
+    product (more rows than either path's algorithm was chosen at, so it
+    runs in row blocks), at any number of rows, and repeat calls give the
+    same bits."""
     r = np.random.default_rng(N + K)
-    A = _bf16(r.standard_normal((4096, K)))
+    M = 4096 + 97
+    A = _bf16(r.standard_normal((M, K)))
     B = _bf16(r.standard_normal((N, K)) / np.sqrt(K))
     dt = torch.float32 if out == "fp32" else torch.bfloat16
-    full = torch.empty((4096, N), dtype=dt, device="cuda")
-    gdn.gemm_bf16(A, B, full, path=gdn.GDN_GEMM_LIBRARY)
+    print(f"gemm rows case N={N} K={K} out={out} path={path}", flush=True)
+    full = torch.empty((M, N), dtype=dt, device="cuda")
+    gdn.gemm_bf16(A, B, full, path=path)
     again = torch.empty_like(full)
-    gdn.gemm_bf16(A, B, again, path=gdn.GDN_GEMM_LIBRARY)
+    gdn.gemm_bf16(A, B, again, path=path)
     torch.cuda.synchronize()
     assert torch.equal(full, again)
-    for m in (1, 3, 64, 65, 300, 4095):
+    for m in (1, 3, 64, 65, 300, 4095, 4096):
         part = torch.empty((m, N), dtype=dt, device="cuda")
-        gdn.gemm_bf16(A[:m], B, part, path=gdn.GDN_GEMM_LIBRARY)
+        gdn.gemm_bf16(A[:m], B, part, path=path)
         torch.cuda.synchronize()
         assert torch.equal(part, full[:m]), m
 
