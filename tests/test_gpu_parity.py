@@ -69,6 +69,26 @@ def test_prefill_windows_bitwise(window_slots):
     check_prefill(case, got, oracle_prefill(case), label=f"windows-{window_slots}")
 
 
+@pytest.mark.parametrize("out_dtype, want_core", [(gdn.GDN_DTYPE_FP32, True), (gdn.GDN_DTYPE_BF16, False)],
+                         ids=["fp32-core", "bf16-nocore"])
+def test_prefill_windows_wide_slices_bitwise(out_dtype, want_core):
+    """Many windows over a batch wide enough for 32-column scan slices, with
+    empty sequences among the ragged ones: a window's rows get their gated
+    norm inside the next window's scan (two row groups per pass in the wide
+    slices), the last window's in the epilogue kernel; the bits equal the
+    single-window run, where the epilogue kernel does every row."""
+    lens = [int(v) for v in np.random.default_rng(43).integers(0, 40, 40)]
+    lens[3] = lens[20] = 0
+    case = synth.prefill_case(synth.TINY, lens, seed=44, with_state=True,
+                              with_conv_state=True, norm_w_jitter=True)
+    ref = gpu_prefill(case, out_dtype=out_dtype, want_core=want_core)
+    got = gpu_prefill(case, out_dtype=out_dtype, want_core=want_core, window_slots=3)
+    for key in ("out", "final_state", "conv_state_out") + (("core_out",) if want_core else ()):
+        assert torch.equal(ref[key], got[key]), key
+    if out_dtype == gdn.GDN_DTYPE_FP32:
+        check_prefill(case, got, oracle_prefill(case), label="windows-wide")
+
+
 def test_prefill_wide_batch_bitwise_vs_alone():
     """40 short sequences: the batch has more (sequence, head, slice) groups
     than there are compute units, so its scan runs 32-column slices, while
