@@ -461,8 +461,22 @@ hipError_t launch_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_
 #undef GDN_SKINNY
     }
     if (path == kGemmAuto || path == kGemmLibrary) {
+        // N past a multiple of 256 (in_proj's 12352 = 48 x 256 + 64 for the
+        // a and b gates) leaves the library's tile grid a last column of
+        // nearly empty tiles, and at 4096 rows a nearly empty last round of
+        // them over the compute units: the full 256-column blocks run as one
+        // product and the rest as another (each with its own algorithm;
+        // columns are independent, so each column's bits are still fixed by
+        // its range alone)
         hipError_t e = hipSuccess;
-        if (gemm_library(A, lda, B, ldb, C, ldc, out_bf16, M, N, K, 4096, s, &e)) return e;
+        const int64_t rest = N % 256;
+        const int64_t main_n = N > 256 ? N - rest : N;
+        if (gemm_library(A, lda, B, ldb, C, ldc, out_bf16, M, main_n, K, 4096, s, &e)) {
+            if (e != hipSuccess || main_n == N) return e;
+            return launch_gemm_bf16_nt(A, lda, b + main_n * ldb, ldb,
+                                       static_cast<uint8_t*>(C) + main_n * (out_bf16 ? 2 : 4), ldc, out_bf16, M,
+                                       rest, K, s, kGemmLibrary);
+        }
     }
     const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
     if (wide >= cus) return launch_gemm_t<256, 256>(a, lda, b, ldb, C, ldc, out_bf16, M, N, K, s);

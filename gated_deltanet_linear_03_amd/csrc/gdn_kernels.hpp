@@ -147,8 +147,10 @@ hipError_t launch_selftest_mfma(const float* A, const float* B, float* C, hipStr
 //                    blocks
 //   kGemmLibrary     hipBLASLt with one algorithm per shape, chosen at 4096
 //                    rows and used at every M (the layer's prefill
-//                    projections); the tiled kernel where the library
-//                    declines (no handle, no algorithm for the shape)
+//                    projections), N past a multiple of 256 as two
+//                    products (the full 256-column blocks, the rest); the
+//                    tiled kernel where the library declines (no handle,
+//                    no algorithm for the shape)
 //   kGemmLibraryFew  the same with the algorithm chosen at 64 rows (the
 //                    layer's decode projections, at any batch size); the
 //                    few-row kernel where the library declines

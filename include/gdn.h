@@ -343,7 +343,11 @@ gdn_status gdn_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
  *                       it was ranked at), so a row's bits do not depend
  *                       on M and, on the same library and device, not on
  *                       the process either (gdn_layer_prefill's
- *                       projections).
+ *                       projections).  An N past a multiple of 256 runs as
+ *                       two products, the full 256-column blocks and the
+ *                       rest, each with its own algorithm (a nearly empty
+ *                       last column of tiles would cost a whole round of
+ *                       them).
  *                       Where the library declines a shape the tiled
  *                       kernel runs.
  *   GDN_GEMM_LIBRARY_FEW_ROWS  the same with the algorithm chosen at 64
