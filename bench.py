@@ -53,7 +53,7 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--headline-only", action="store_true",
                     help="only the 131072-token headline (for profiling)")
-    ap.add_argument("--only", choices=["4k", "varlen", "decode"], default=None,
+    ap.add_argument("--only", choices=["4k", "varlen", "decode", "layer"], default=None,
                     help="only this extra workload, no headline and no JSON line (for profiling)")
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--decode-batches", default="64,3,1")
@@ -354,7 +354,8 @@ def main(argv=None):
         args.headline_only = False
         args.no_4k, args.no_varlen, args.no_decode = (args.only != "4k", args.only != "varlen",
                                                       args.only != "decode")
-        args.no_layer = args.no_cpu_baseline = True
+        args.no_layer = args.only != "layer"
+        args.no_cpu_baseline = True
         result = {}
     else:
         result = headline(131072)
