@@ -119,6 +119,50 @@ def test_gemm_library_rows_do_not_depend_on_m(N, K, out, path):
         assert torch.equal(part, full[:m]), m
 
 
+_CHILD_GEMM = """
+import hashlib, sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import gated_deltanet_linear_03_amd as gdn
+M, N, K, path, f32 = (int(v) for v in sys.argv[2:7])
+r = np.random.default_rng(M + N + K)
+A = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).cuda().to(torch.bfloat16)
+B = torch.from_numpy((r.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)).cuda().to(torch.bfloat16)
+C = torch.empty((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+gdn.gemm_bf16(A, B, C, path=path)
+torch.cuda.synchronize()
+print(hashlib.sha256(C.cpu().contiguous().view(torch.uint8).numpy().tobytes()).hexdigest())
+"""
+
+
+@pytest.mark.parametrize("M, N, K, path, f32", [
+    (300, 12352, 2048, gdn.GDN_GEMM_LIBRARY, 0),          # in_proj, split into 12288 + 64 columns
+    (300, 2048, 4096, gdn.GDN_GEMM_LIBRARY, 1),           # out_proj, fp32 out
+    (5, 12352, 2048, gdn.GDN_GEMM_LIBRARY_FEW_ROWS, 0),   # the decode projections' pin
+])
+def test_gemm_library_bits_same_in_another_process(M, N, K, path, f32):
+    """The library path's algorithm is chosen without timing (the first
+    no-workspace candidate the library ranks), so a second process on the
+    same library and device computes the same bits."""
+    import hashlib
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = np.random.default_rng(M + N + K)
+    A = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).cuda().to(torch.bfloat16)
+    B = torch.from_numpy((r.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)).cuda().to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    gdn.gemm_bf16(A, B, C, path=path)
+    torch.cuda.synchronize()
+    mine = hashlib.sha256(C.cpu().contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
+    print(f"child process: gemm M={M} N={N} K={K} path={path}", flush=True)
+    out = subprocess.run([sys.executable, "-c", _CHILD_GEMM, root, str(M), str(N), str(K), str(path), str(f32)],
+                         capture_output=True, text=True, timeout=90)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.split()[-1] == mine
+
+
 def _layer_case(sh, hidden, lens, seed, with_states):
     p = synth.layer_params(sh, seed)
     # in_proj exact in bf16 (see proj_weights_exact): both sides hand the
