@@ -58,8 +58,9 @@ def test_gemm_matches_fp64(M, N, K, path):
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("M", [130, 7])
 def test_gemm_strided_rows(M, path):
-    """Row strides beyond K (views into wider buffers); 7 rows take the
-    few-row kernel by default."""
+    """Row strides beyond K (views into wider buffers), on every kernel
+    family; by default 7 rows take the library's 64-row choice and 130 rows
+    its 4096-row one."""
     r = np.random.default_rng(3)
     N, K = 70, 96
     Aw = _bf16(r.standard_normal((M, K + 24)))
@@ -74,9 +75,8 @@ def test_gemm_strided_rows(M, path):
 
 
 def test_gemm_few_rows_batch_invariant():
-    """Up to 64 rows: each output row's bits depend on its own A row only,
-    not on how many rows are in the call (the decode projections' batch
-    invariance)."""
+    """Up to 64 rows (the default path's 64-row family): each output row's
+    bits depend on its own A row only, not on how many rows are in the call."""
     r = np.random.default_rng(11)
     N, K = 12352, 2048
     A = _bf16(r.standard_normal((64, K)))
@@ -338,8 +338,63 @@ def test_layer_decode_batch_invariant_across_64_rows():
         assert torch.equal(st, ref_st[:B]) and torch.equal(cs, ref_cs[:B]), B
 
 
+def test_layer_decode_graph_replays_match_eager():
+    """gdn_layer_decode (in_proj, the decode step, out_proj; the projections
+    through hipBLASLt with no workspace) captured in a HIP graph after eager
+    calls have chosen the GEMM algorithms: every replay, with eager work
+    between replays, gives the bits of the same eager step."""
+    sh = synth.FULL
+    hidden, B, reps = 2048, 5, 4
+    p = synth.layer_params(sh, 640)
+    w_in, w_out = synth.proj_weights(sh, hidden, 640)
+    layer = make_layer(sh, p)
+    proj = gdn.Proj(hidden=hidden, w_in=_bf16(w_in), w_out=_bf16(w_out))
+    xs = [_bf16(synth.hidden_inputs(B, hidden, 641 + r)) for r in range(reps)]
+    x = torch.empty_like(xs[0])
+    S0 = to_dev(synth.initial_states(sh, B, 650))
+    C0 = _bf16(synth.conv_states(sh, B, 651))
+    y = torch.empty((B, hidden), dtype=torch.float32, device="cuda")
+    st, cs = S0.clone(), C0.clone()
+    ws = torch.zeros(gdn.layer_decode_workspace_bytes(layer, proj, B), dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdn.layer_decode_raw(layer, proj, B=B, x=x, y=y, state_in=st, state_out=st,
+                             conv_state_in=cs, conv_state_out=cs, workspace=ws)
+
+    ref = []
+    for r in range(reps):
+        x.copy_(xs[r])
+        step()
+        torch.cuda.synchronize()
+        ref.append((y.clone(), st.clone(), cs.clone()))
+    st.copy_(S0)
+    cs.copy_(C0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    st.copy_(S0)
+    cs.copy_(C0)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        x.copy_(xs[r])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[r][0]), r
+        assert torch.equal(st, ref[r][1]) and torch.equal(cs, ref[r][2]), r
+        del junk
+
+
 def test_layer_prefill_short_sequence_alone_vs_packed():
-    """The prefill layer's projections use the tiled kernel at every token
+    """The prefill layer's projections keep one kernel family at every token
     count: a 40-token sequence gives the same bits alone (40 rows) and packed
     behind a 300-token one."""
     sh = synth.FULL
