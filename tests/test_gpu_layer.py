@@ -393,6 +393,59 @@ def test_layer_decode_graph_replays_match_eager():
         del junk
 
 
+def test_layer_prefill_graph_replays_match_eager():
+    """gdn_layer_prefill (in_proj, the three prefill kernels, out_proj)
+    captured in a HIP graph after an eager call: every replay, with eager work
+    between replays and new inputs copied in before each, gives the eager
+    call's bits."""
+    sh = synth.FULL
+    hidden, lens, reps = 2048, [300, 0, 77], 3
+    p = synth.layer_params(sh, 660)
+    w_in, w_out = synth.proj_weights(sh, hidden, 660)
+    layer = make_layer(sh, p)
+    proj = gdn.Proj(hidden=hidden, w_in=_bf16(w_in), w_out=_bf16(w_out))
+    cu_np = synth.cu_from_lengths(lens)
+    T, N = int(cu_np[-1]), len(lens)
+    cu = to_dev(cu_np)
+    xs = [_bf16(synth.hidden_inputs(T, hidden, 661 + r)) for r in range(reps)]
+    x = torch.empty_like(xs[0])
+    S0 = to_dev(synth.initial_states(sh, N, 670))
+    y = torch.empty((T, hidden), dtype=torch.float32, device="cuda")
+    fs = torch.empty((N, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device="cuda")
+    cs = torch.empty((N, sh.K - 1, sh.Cc), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.layer_prefill_workspace_bytes(layer, proj, N, T), dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdn.layer_prefill_raw(layer, proj, N=N, T_total=T, cu_seqlens=cu, x=x, y=y, initial_state=S0,
+                              final_state=fs, conv_state_out=cs, workspace=ws)
+
+    ref = []
+    for r in range(reps):
+        x.copy_(xs[r])
+        step()
+        torch.cuda.synchronize()
+        ref.append((y.clone(), fs.clone(), cs.clone()))
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        x.copy_(xs[r])
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[r][0]), r
+        assert torch.equal(fs, ref[r][1]) and torch.equal(cs, ref[r][2]), r
+        del junk
+
+
 def test_layer_prefill_short_sequence_alone_vs_packed():
     """The prefill layer's projections keep one kernel family at every token
     count: a 40-token sequence gives the same bits alone (40 rows) and packed
