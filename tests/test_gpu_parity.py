@@ -73,10 +73,9 @@ def test_prefill_windows_bitwise(window_slots):
                          ids=["fp32-core", "bf16-nocore"])
 def test_prefill_windows_wide_slices_bitwise(out_dtype, want_core):
     """Many windows over a batch wide enough for 32-column scan slices, with
-    empty sequences among the ragged ones: a window's rows get their gated
-    norm inside the next window's scan (two row groups per pass in the wide
-    slices), the last window's in the epilogue kernel; the bits equal the
-    single-window run, where the epilogue kernel does every row."""
+    empty sequences among the ragged ones, fp32 out with the pre-norm tap and
+    bf16 out with the pre-norm output kept in the workspace: the bits equal
+    the single-window run's."""
     lens = [int(v) for v in np.random.default_rng(43).integers(0, 40, 40)]
     lens[3] = lens[20] = 0
     case = synth.prefill_case(synth.TINY, lens, seed=44, with_state=True,
@@ -87,6 +86,24 @@ def test_prefill_windows_wide_slices_bitwise(out_dtype, want_core):
         assert torch.equal(ref[key], got[key]), key
     if out_dtype == gdn.GDN_DTYPE_FP32:
         check_prefill(case, got, oracle_prefill(case), label="windows-wide")
+
+
+@pytest.mark.parametrize("shape", ["tiny", "full"])
+def test_prefill_all_sequences_empty(shape):
+    """T_total = 0 over three empty sequences: only the first prep window
+    runs (it builds the chunk table), the scan passes every state through
+    and the epilogue has no rows.  The recurrent and conv states come out
+    bit-identical to the ones in, as the oracle has them."""
+    sh = synth.TINY if shape == "tiny" else synth.FULL
+    case = synth.prefill_case(sh, [0, 0, 0], seed=12, with_state=True, with_conv_state=True)
+    res = gpu_prefill(case)
+    ref = oracle_prefill(case)
+    assert res["out"].numel() == 0
+    assert np.array_equal(res["final_state"].cpu().numpy(), case.initial_state)
+    assert np.array_equal(ref["final_state"], case.initial_state.astype(np.float64))
+    got_cs = res["conv_state_out"].float().cpu().numpy()
+    assert np.array_equal(got_cs, case.conv_state.astype(np.float32))
+    assert np.array_equal(got_cs, ref["conv_state_out"])
 
 
 def test_prefill_wide_batch_bitwise_vs_alone():
