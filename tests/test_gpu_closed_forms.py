@@ -15,12 +15,13 @@ import numpy as np
 import pytest
 import torch
 
+import gated_deltanet_linear_03_amd as gdn
 import oracle
 from gated_deltanet_linear_03_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-from gpu_helpers import TOL, check_prefill, gpu_prefill, oracle_prefill  # noqa: E402
+from gpu_helpers import TOL, act_dtype, check_prefill, gpu_prefill, make_layer, oracle_prefill, to_dev  # noqa: E402
 
 
 def _extreme_case(sh, lens, seed, b_logit):
@@ -82,3 +83,45 @@ def test_beta_one_retrieves_the_last_pair(shape):
     assert worst < TOL
     # and the whole output against the oracle at these gates
     check_prefill(case, res, oracle_prefill(case), label=f"beta=1 {shape}")
+
+
+@pytest.mark.parametrize("shape", ["tiny", "full"])
+@pytest.mark.parametrize("b_logit", [-100.0, 100.0], ids=["beta0", "beta1"])
+def test_decode_closed_forms(shape, b_logit):
+    """The one-token decode kernel on the same closed forms: beta = 0 leaves
+    the state bit for bit and gives o = S q^; beta = 1 gives S' k^ = v^."""
+    sh = synth.TINY if shape == "tiny" else synth.FULL
+    B = 5
+    p = dict(synth.layer_params(sh, 23))
+    conv_w = np.zeros_like(p["conv_w"])
+    conv_w[:, -1] = 1.0
+    p["conv_w"] = conv_w
+    p["A_log"] = np.full_like(p["A_log"], -100.0)
+    layer = make_layer(sh, p)
+    x = dict(synth.token_inputs(sh, B, 24))
+    x["b"] = np.full_like(x["b"], b_logit)
+    ad = act_dtype(sh)
+    S0 = synth.initial_states(sh, B, 25)
+    C0 = synth.conv_states(sh, B, 26)
+    res = gdn.decode(layer, *(to_dev(x[n], ad) for n in "qkvzab"), to_dev(S0), to_dev(C0, ad),
+                     in_place=False, want_core=True)
+    torch.cuda.synchronize()
+    fs = res["final_state"].cpu().numpy()
+    core = res["core_out"].double().cpu().numpy()
+    G = sh.Hv // sh.Hk
+    worst = 0.0
+    for n in range(B):
+        for h in range(sh.Hv):
+            if b_logit < 0:
+                qh = oracle.l2norm(_silu(x["q"][n, h // G]), sh.eps_l2, sh.scale)
+                want, got = S0[n, h].astype(np.float64).T @ qh, core[n, h]
+            else:
+                kh = oracle.l2norm(_silu(x["k"][n, h // G]), sh.eps_l2)
+                want, got = _silu(x["v"][n, h]), fs[n, h].astype(np.float64).T @ kh
+            worst = max(worst, np.abs(got - want).max() / np.abs(want).max())
+    print(f"decode {shape} b = {b_logit}: {worst:.2e}", flush=True)
+    if b_logit < 0:
+        assert np.array_equal(fs, S0)
+        assert worst < 1e-5
+    else:
+        assert worst < 1e-4
