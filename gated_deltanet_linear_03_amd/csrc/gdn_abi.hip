@@ -836,7 +836,12 @@ gdn_status gdn_snapshot_inspect(const void* host, size_t host_bytes, gdn_snapsho
     if (hd.version != GDN_SNAPSHOT_VERSION)
         return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot version %u, this library reads %u", hd.version,
                     static_cast<unsigned>(GDN_SNAPSHOT_VERSION));
-    if (hd.Hk <= 0 || hd.Hv <= 0 || hd.dk <= 0 || hd.dv <= 0 || hd.conv_K < 1 ||
+    // each dimension below 2^16 and K below 2^8: the size products and their
+    // sum below stay far from wrapping around 64 bits, so a header cannot
+    // pass the size checks with wrapped values
+    constexpr int32_t kDimMax = 1 << 16;
+    if (hd.Hk <= 0 || hd.Hv <= 0 || hd.dk <= 0 || hd.dv <= 0 || hd.conv_K < 1 || hd.Hk > kDimMax ||
+        hd.Hv > kDimMax || hd.dk > kDimMax || hd.dv > kDimMax || hd.conv_K > 256 ||
         (hd.act_dtype != GDN_DTYPE_FP32 && hd.act_dtype != GDN_DTYPE_BF16))
         return fail(GDN_ERR_INVALID_ARGUMENT, "snapshot header has an invalid geometry or dtype");
     const uint64_t Cc = 2ull * hd.Hk * hd.dk + static_cast<uint64_t>(hd.Hv) * hd.dv;

@@ -483,9 +483,11 @@ gdn_status gdn_snapshot_save(const gdn_layer* layer, const float* state,
                              int32_t num_slots, void* host_buf,
                              size_t host_bytes, void* stream);
 
-/* Validate a snapshot in host memory (magic, version, sizes, checksum) and
- * return its header; touches no device.  GDN_ERR_INVALID_ARGUMENT with the
- * reason in gdn_last_error() when it is not a whole, intact snapshot. */
+/* Validate a snapshot in host memory (magic, version, geometry with every
+ * dimension in [1, 65536] and conv_K in [1, 256], sizes, checksum) and
+ * return its header; touches no device and reads at most host_bytes.
+ * GDN_ERR_INVALID_ARGUMENT with the reason in gdn_last_error() when it is not
+ * a whole, intact snapshot. */
 gdn_status gdn_snapshot_inspect(const void* host_buf, size_t host_bytes,
                                 gdn_snapshot_header* header);
 

@@ -580,6 +580,20 @@ def test_snapshot_inspect_rejects_damage(damage, msg):
     assert ei.value.status == gdn.GDN_ERR_INVALID_ARGUMENT and msg in ei.value.detail
 
 
+def test_snapshot_inspect_rejects_sizes_that_wrap():
+    """A header whose geometry makes Hv*dk*dv*4 = 2^64, i.e. 0 once wrapped
+    around 64 bits, with conv_K = 1 (no conv state), sizes 0 and the
+    checksum of an empty payload: every size check would pass on the
+    wrapped values, so the geometry itself is refused."""
+    Hk, Hv, dk, dv = 1, 1 << 21, 1 << 21, 1 << 20
+    assert (Hv * dk * dv * 4) % (1 << 64) == 0
+    hd = gdn.CSnapshotHeader(gdn.SNAPSHOT_MAGIC, gdn.SNAPSHOT_VERSION, Hk, Hv, dk, dv, 1, gdn.GDN_DTYPE_FP32,
+                             0, 0, _fnv1a64(b""), 0)
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.snapshot_inspect(bytes(hd))
+    assert "invalid geometry" in ei.value.detail
+
+
 def test_snapshot_restore_rejects_another_layer():
     """A snapshot taken at one geometry or dtype is refused by a layer of
     another before any device copy (the pointers here are never touched)."""
