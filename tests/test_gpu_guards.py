@@ -144,3 +144,31 @@ def test_layer_writes_stay_inside():
     for name, g in (("y", yd), ("state", fs), ("conv", cs), ("workspace", dws)):
         assert g.intact(), name
     assert bool(torch.isfinite(yd.t).all())
+
+
+def test_verify_writes_stay_inside():
+    """Multi-token verify with per-token state snapshots (the largest writes
+    of a decode step) on guarded buffers, states in place."""
+    sh = synth.FULL
+    B, tok = 3, 4
+    ad = act_dtype(sh)
+    layer = make_layer(sh, synth.layer_params(sh, 79))
+    x = {k: to_dev(v, ad) for k, v in synth.token_inputs(sh, B * tok, 80).items()}
+    S0 = to_dev(synth.initial_states(sh, B, 81))
+    C0 = to_dev(synth.conv_states(sh, B, 82), ad)
+    out = Guarded((B * tok, sh.Hv, sh.dv), torch.float32)
+    core = Guarded((B * tok, sh.Hv, sh.dv), torch.float32)
+    st = Guarded(tuple(S0.shape), torch.float32, S0)
+    cs = Guarded(tuple(C0.shape), ad, C0)
+    snap = Guarded((B, tok, sh.Hv, sh.dk, sh.dv), torch.float32)
+    gdn.decode_multi_raw(layer, B=B, tokens=tok, q=x["q"], k=x["k"], v=x["v"], z=x["z"], a=x["a"], b=x["b"],
+                         out=out.t, core_out=core.t, state_in=st.t, state_out=st.t, conv_state_in=cs.t,
+                         conv_state_out=cs.t, state_snapshots=snap.t)
+    torch.cuda.synchronize()
+    for name, g in (("out", out), ("core_out", core), ("state", st), ("conv", cs), ("snapshots", snap)):
+        assert g.intact(), name
+    ref = gdn.decode_multi(layer, x["q"], x["k"], x["v"], x["z"], x["a"], x["b"], S0.clone(), C0.clone(),
+                           tok, want_core=True, want_snapshots=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.t, ref["out"]) and torch.equal(st.t, ref["final_state"])
+    assert torch.equal(snap.t, ref["state_snapshots"])
