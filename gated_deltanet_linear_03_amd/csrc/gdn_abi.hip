@@ -114,7 +114,7 @@ WsLayout ws_layout(const gdn_layer* L, int32_t N, int64_t T, bool need_core, int
     w.off_decay = o;
     o = round_up(o + 4 * w.max_chunks * L->Hv, 256);
     w.off_core = o;
-    if (need_core) o = round_up(o + 4 * T * L->Hv * L->dv, 256);
+    if (need_core) o = round_up(o + 2 * T * L->Hv * L->dv, 256);   // o as fp16
     w.off_carry = o;
     o = round_up(o + 2ll * 4 * L->Hv * L->dk * L->dv, 256);
     w.off_vch = o;
@@ -266,6 +266,7 @@ static gdn_status prefill_impl(const gdn_layer* L, const gdn_prefill_io* io, voi
     p.out = io->out; p.out_bf16 = L->out_dtype == GDN_DTYPE_BF16;
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.core = io->core_out ? io->core_out : reinterpret_cast<float*>(base + w.off_core);
+    p.core_f16 = io->core_out ? 0 : 1;
     p.slots = io->state_slots;
     p.num_slots = static_cast<int>(entries);
     p.status = io->status;

@@ -63,6 +63,7 @@ struct PrefillParams {
     void* out;
     int out_bf16;
     float* core;                          // o before the gated norm (user or workspace)
+    int core_f16;                         // 1: `core` holds o as fp16 (the workspace copy), 0: fp32 (core_out)
     const int32_t* slots;                 // [N] pool entry of each sequence's states, or NULL (entry n)
     int num_slots;                        // pool entries (with slots)
     int32_t* status;                      // optional: cleared by the first kernel, then status bits ORed in

@@ -153,7 +153,9 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
 
-template <int DK, int DV, int C, int DVS, bool BF16>
+// O16: the output waves store o as fp16 (the workspace copy the epilogue
+// reads), else as fp32 (the caller's core_out).
+template <int DK, int DV, int C, int DVS, bool BF16, bool O16>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
     using L = VchLayout<DK, DV, C>;
     constexpr int CK = L::CK;
@@ -509,24 +511,33 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 // offset; in a partial one, rows past the sequence end go to
                 // a sink, so that every lane issues the same stores (the
                 // memory counter the next chunk's operand waits rely on then
-                // counts them exactly)
-                float* cbase = p.core + (t0 * p.Hv + h) * DV + col0;
-                if (Lc == C) {
+                // counts them exactly).  The workspace copy for the epilogue
+                // is fp16 (half the bytes out and back); a caller's core_out
+                // gets fp32.
+                const int64_t cofs = (t0 * p.Hv + h) * DV + col0;
+                auto store_o = [&](auto* cbase, auto* sink, auto cvt) {
+                    if (Lc == C) {
 #pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt)
+                        for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) cbase[lane_off + i * rstride + nt * 16] = acco[nt][i];
-                } else {
+                            for (int i = 0; i < 4; ++i) cbase[lane_off + i * rstride + nt * 16] = cvt(acco[nt][i]);
+                    } else {
 #pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) {
+                        for (int nt = 0; nt < NTL; ++nt) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = mt * 16 + lq * 4 + i;
-                            float* dst = r < Lc ? cbase + lane_off + i * rstride + nt * 16 : p.sink + lane;
-                            *dst = acco[nt][i];
+                            for (int i = 0; i < 4; ++i) {
+                                const int r = mt * 16 + lq * 4 + i;
+                                auto* dst = r < Lc ? cbase + lane_off + i * rstride + nt * 16 : sink;
+                                *dst = cvt(acco[nt][i]);
+                            }
                         }
                     }
-                }
+                };
+                if constexpr (O16)
+                    store_o(reinterpret_cast<uint16_t*>(p.core) + cofs, reinterpret_cast<uint16_t*>(p.sink) + lane,
+                            [](float x) { return f32_to_f16_bits(x); });
+                else
+                    store_o(p.core + cofs, p.sink + lane, [](float x) { return x; });
             }
             __syncthreads();
         };
@@ -605,7 +616,11 @@ struct EpiGeom {
     static_assert(DV % 4 == 0 && LPR <= kWave && kWave % LPR == 0, "row geometry");
 };
 
-template <int DV, bool BF16>
+// O16: o comes as fp16 (the scan's workspace copy), else as the caller's
+// fp32 core_out, rounded to fp16 here the same way so that `out` has the
+// same bits either way (a template argument, not a branch: the o and z
+// loads must both be in flight before the first wait).
+template <int DV, bool BF16, bool O16>
 __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
     using G = EpiGeom<DV>;
     const int lr = threadIdx.x % G::LPR;
@@ -614,7 +629,18 @@ __global__ __launch_bounds__(256) void epi_kernel(PrefillParams p) {
     const int64_t rr = valid ? row : 0;
     const int64_t t = rr / p.Hv;
     const int h = static_cast<int>(rr % p.Hv);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(p.core + rr * DV + 4 * lr);
+    float o[4];
+    if constexpr (O16) {
+        const uint2 oo = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.core) + rr * DV + 4 * lr);
+        o[0] = f16_bits_to_f32(static_cast<uint16_t>(oo.x));
+        o[1] = f16_bits_to_f32(static_cast<uint16_t>(oo.x >> 16));
+        o[2] = f16_bits_to_f32(static_cast<uint16_t>(oo.y));
+        o[3] = f16_bits_to_f32(static_cast<uint16_t>(oo.y >> 16));
+    } else {
+        const f32x4 oo = *reinterpret_cast<const f32x4*>(p.core + rr * DV + 4 * lr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f16_bits_to_f32(f32_to_f16_bits(oo[e]));
+    }
     float z[4];
     if constexpr (BF16) {
         const uint2 zz = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.z) + t * p.zs + h * DV + 4 * lr);
@@ -720,20 +746,27 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s,
         mark(ev_i++);
         if (pairs > 0) {
             const int groups = (pairs + 7) / 8;
-            if (static_cast<int64_t>(groups) * 8 * (DV / DVS) <= compute_units())
-                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16>), dim3(groups * 8 * (DV / DVS)),
-                                   dim3(kScanThreads), 0, s, q);
+            const bool narrow = static_cast<int64_t>(groups) * 8 * (DV / DVS) <= compute_units();
+            const dim3 grid(groups * 8 * (DV / (narrow ? DVS : DVSW)));
+            if (narrow && p.core_f16)
+                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16, true>), grid, dim3(kScanThreads), 0, s, q);
+            else if (narrow)
+                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVS, BF16, false>), grid, dim3(kScanThreads), 0, s, q);
+            else if (p.core_f16)
+                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVSW, BF16, true>), grid, dim3(kScanThreads), 0, s, q);
             else
-                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVSW, BF16>), dim3(groups * 8 * (DV / DVSW)),
-                                   dim3(kScanThreads), 0, s, q);
+                hipLaunchKernelGGL((scan_kernel<DK, DV, C, DVSW, BF16, false>), grid, dim3(kScanThreads), 0, s, q);
         }
         mark(ev_i++);
     }
     if (p.T > 0) {
         const int64_t rows = p.T * p.Hv;
         constexpr int RPB = EpiGeom<DV>::RPB;
-        hipLaunchKernelGGL((epi_kernel<DV, BF16>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)),
-                           dim3(256), 0, s, p);
+        const dim3 grid(static_cast<unsigned>((rows + RPB - 1) / RPB));
+        if (p.core_f16)
+            hipLaunchKernelGGL((epi_kernel<DV, BF16, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((epi_kernel<DV, BF16, false>), grid, dim3(256), 0, s, p);
     }
     mark(ev_i++);
     if (e != hipSuccess) return e;

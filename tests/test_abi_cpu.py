@@ -334,7 +334,7 @@ def test_prefill_windows_follow_the_workspace():
     assert window(131072 // 64) == 32
     assert len(gdn.prefill_launches(lay, 1, 131072)) == 1 + 2 * 64
     nb_long = gdn.prefill_workspace_bytes(lay, 1, 131072)
-    assert nb_long - nb == ((131072 - T) * 32 * 128 * 4 + 4 * (131072 - T) // 64 * 32
+    assert nb_long - nb == ((131072 - T) * 32 * 128 * 2 + 4 * (131072 - T) // 64 * 32
                             + (window(131072 // 64) - win) * slot)
     # half the window: twice the windows
     half = len(gdn.prefill_launches(lay, 1, T, nb - (win - win // 2) * slot))
@@ -347,7 +347,7 @@ def test_prefill_windows_follow_the_workspace():
         gdn.prefill_launches(lay, 1, T, floor - 256)
     # with core_out the pre-norm output needs no workspace: the same size
     # then holds that many more chunk slots
-    pre_norm = T * 32 * 128 * 4
+    pre_norm = T * 32 * 128 * 2          # o as fp16
     extra = pre_norm // slot
     assert gdn.prefill_window_slots(lay, 1, T, floor, with_core_out=True) == 1 + extra
     assert (len(gdn.prefill_launches(lay, 1, T, floor, with_core_out=True))

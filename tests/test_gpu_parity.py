@@ -89,6 +89,26 @@ def test_prefill_windows_wide_slices_bitwise(out_dtype, want_core):
 
 
 @pytest.mark.parametrize("shape", ["tiny", "full"])
+def test_prefill_out_same_bits_with_or_without_core_out(shape):
+    """The scan hands o to the epilogue as fp16 in the workspace when no
+    core_out is given, and as fp32 in core_out when one is; the epilogue
+    rounds core_out to fp16 before the norm, so `out` has the same bits
+    either way, while core_out itself keeps fp32 precision.  Both meet the
+    oracle."""
+    sh = synth.TINY if shape == "tiny" else synth.FULL
+    case = synth.prefill_case(sh, [70, 0, 129, 5], seed=46, with_state=True, with_conv_state=True,
+                              norm_w_jitter=True)
+    with_core = gpu_prefill(case, want_core=True)
+    without = gpu_prefill(case, want_core=False)
+    assert torch.equal(with_core["out"], without["out"])
+    for key in ("final_state", "conv_state_out"):
+        assert torch.equal(with_core[key], without[key]), key
+    core = with_core["core_out"]
+    assert not torch.equal(core, core.half().float()), "core_out is fp32, not the fp16 hand-off"
+    check_prefill(case, with_core, oracle_prefill(case), label=f"core-out-{shape}")
+
+
+@pytest.mark.parametrize("shape", ["tiny", "full"])
 def test_prefill_all_sequences_empty(shape):
     """T_total = 0 over three empty sequences: only the first prep window
     runs (it builds the chunk table), the scan passes every state through

@@ -71,10 +71,11 @@ def test_noalloc_prefill_matches_prefill_twice(shape):
 
 
 def test_noalloc_prefill_refuses_what_does_not_fit():
-    """Without core_out the pre-norm output must fit the array too: a 4096-
-    token batch of the full shape needs 64 MiB for it plus the carry slots
-    and one chunk slot, which fits; 16384 tokens do not, and nothing is
-    enqueued (the output keeps its poison)."""
+    """Without core_out the pre-norm output (fp16) must fit the array too:
+    a 4096-token batch of the full shape needs 32 MiB for it plus the carry
+    slots and one chunk slot, which fits; 16384 tokens need 128 MiB for it
+    alone, which does not, and nothing is enqueued (the output keeps its
+    poison)."""
     sh = synth.FULL
     layer = make_layer(sh, synth.layer_params(sh, 703))
     T = 16384
