@@ -100,7 +100,9 @@ typedef struct {
  * (in-place update) but must not partially overlap it; NULL = not written.
  * conv_state_in NULL means zero history; conv_state_out may equal
  * conv_state_in; NULL = not written.  core_out (optional) receives o_t
- * before the gated RMSNorm, in fp32. */
+ * before the gated RMSNorm, in fp32.  The gated RMSNorm normalises o_t
+ * rounded to fp16 (to nearest even), with or without core_out, so `out`
+ * has the same bits either way. */
 typedef struct {
     int32_t N;
     int64_t T_total;               /* == cu_seqlens[N] */
@@ -195,7 +197,7 @@ int gdn_abi_version(void);
 
 /* Bytes of device workspace gdn_prefill needs for N sequences holding
  * T_total tokens in all (an upper bound over every length split).  It holds
- * the chunk table, the fp32 pre-norm output (when no core_out is given),
+ * the chunk table, the pre-norm output as fp16 (when no core_out is given),
  * two recurrent-state carry slots and the per-chunk operand blocks of one
  * window of chunks.  The prefill runs window by window: for one sequence
  * the window is at most about 144 MiB of operand blocks (sized for the
@@ -230,7 +232,7 @@ gdn_status gdn_prefill(const gdn_layer* layer, const gdn_prefill_io* io,
  * allocating routine.  Same kernels and bit-identical results as
  * gdn_prefill with a workspace of that size.  Sizes whose workspace does not
  * fit that array (the fixed parts plus one chunk slot of operand blocks,
- * plus T_total*Hv*dv*4 bytes of pre-norm output when core_out is NULL) are
+ * plus T_total*Hv*dv*2 bytes of fp16 pre-norm output when core_out is NULL) are
  * refused with GDN_ERR_WORKSPACE before anything is enqueued.  The stream's
  * device must be the current device (else GDN_ERR_INVALID_ARGUMENT).  All
  * calls on one device share its array: calls that overlap in time on one
