@@ -513,14 +513,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 // memory counter the next chunk's operand waits rely on then
                 // counts them exactly).  The workspace copy for the epilogue
                 // is fp16 (half the bytes out and back); a caller's core_out
-                // gets fp32.
+                // gets fp32.  Non-temporal: o is read again only by the
+                // epilogue after the last window, and should not evict the
+                // operand blocks the next steps read.
                 const int64_t cofs = (t0 * p.Hv + h) * DV + col0;
                 auto store_o = [&](auto* cbase, auto* sink, auto cvt) {
                     if (Lc == C) {
 #pragma unroll
                         for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) cbase[lane_off + i * rstride + nt * 16] = cvt(acco[nt][i]);
+                            for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(cvt(acco[nt][i]), cbase + lane_off + i * rstride + nt * 16);
                     } else {
 #pragma unroll
                         for (int nt = 0; nt < NTL; ++nt) {
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                             for (int i = 0; i < 4; ++i) {
                                 const int r = mt * 16 + lq * 4 + i;
                                 auto* dst = r < Lc ? cbase + lane_off + i * rstride + nt * 16 : sink;
-                                *dst = cvt(acco[nt][i]);
+                                __builtin_nontemporal_store(cvt(acco[nt][i]), dst);
                             }
                         }
                     }
