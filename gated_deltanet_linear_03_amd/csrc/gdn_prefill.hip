@@ -489,13 +489,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
             for (int kt = 0; kt < KTH - 1; ++kt) qh_step(kt);
             __syncthreads();
             qh_step(KTH - 1);
+            f32x4 acco[NTL];
             if (has_row) {
-                // (2) O += P U, store the valid rows
+                // (2) O += P U; the valid rows are stored after the barrier
                 u32x4 ub[KTC][NTL], ubl[KTC][NTL];
                 read_U(UT, ub);
                 read_U(UTl, ubl);
                 load_p(nxt, cn);
-                f32x4 acco[NTL];
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
@@ -507,6 +507,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                     for (int nt = 0; nt < NTL; ++nt)
                         acco[nt] = mfma_h3(cur.p[kt], cur.pl[kt], ub[kt][nt], ubl[kt][nt], acco[nt]);
                 }
+            }
+            // the step's last barrier first: the state waves need not wait
+            // for the conversions and stores below, which then overlap the
+            // next step's first half
+            __syncthreads();
+            if (has_row) {
                 // a full chunk stores at a per-chunk base plus this lane's
                 // offset; in a partial one, rows past the sequence end go to
                 // a sink, so that every lane issues the same stores (the
@@ -541,7 +547,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(PrefillParams p) {
                 else
                     store_o(p.core + cofs, p.sink + lane, [](float x) { return x; });
             }
-            __syncthreads();
         };
 
         Ops opA, opB, opC;
