@@ -35,15 +35,15 @@ def test_prefill_long_131072_head_sample():
     check_prefill(case, res, ref, heads=ref["heads"], label="long")
 
 
-@pytest.mark.parametrize("T", [2048, 32768])
+@pytest.mark.parametrize("T", [2048, 32768, 131072])
 def test_prefill_weak_decay_long_head_sample(T):
     """Weak decay over a long sequence: A_log in [ln 1e-4, ln 1e-3] (e^g
     about 0.999 per token), so the state remembers across hundreds of
     chunks and the scan's single-fp16 state chain (-W H and K_d^T U, with
     the state itself kept in fp32) rounds that slowly decaying state chunk
     after chunk.  One sequence of T tokens from a N(0, 0.02) state, key
-    heads 3 and 12 against the oracle; T = 2048 and 32768 show how the
-    error grows with the length."""
+    heads 3 and 12 against the oracle; T = 2048, 32768 and 131072 (2048
+    chunks, 64 windows) show how the error grows with the length."""
     case = synth.prefill_case(synth.FULL, [T], seed=31, with_state=True,
                               A_log_range=(math.log(1e-4), math.log(1e-3)))
     res = gpu_prefill(case, want_core=True)
