@@ -92,12 +92,15 @@ __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
          + 4ll * C * DV;         // U~    (fp32 accumulator fragments)
 }
 
-// Target size of one window's operand blocks.  One sequence: small enough
-// to stay in the 256 MiB Infinity Cache between the kernel that writes them
-// and the one that reads them.  Several sequences run their chunks
-// concurrently in one window (a window boundary would serialise them), up to
-// a cap that bounds the workspace.
-constexpr int64_t kPrefillWindowBytes = 144ll << 20;
+// Target size of one window's operand blocks.  One sequence: as large as
+// still stays in the 256 MiB Infinity Cache between the kernel that writes
+// them and the one that reads them (the other traffic of a step passes it
+// by: inputs are read and outputs written non-temporally); at 128/128/64 and
+// 32 value heads that is 64 chunk slots, 230 MB, four rounds of prep
+// work-groups.  Several sequences run their chunks concurrently in one
+// window (a window boundary would serialise them), up to a cap that bounds
+// the workspace.
+constexpr int64_t kPrefillWindowBytes = 240ll << 20;
 constexpr int64_t kPrefillBatchWindowBytes = 4ll << 30;
 
 // Chunk slots per window for a layer: as many as the target size allows.

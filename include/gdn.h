@@ -200,7 +200,7 @@ int gdn_abi_version(void);
  * the chunk table, the pre-norm output as fp16 (when no core_out is given),
  * two recurrent-state carry slots and the per-chunk operand blocks of one
  * window of chunks.  The prefill runs window by window: for one sequence
- * the window is at most about 144 MiB of operand blocks (sized for the
+ * the window is at most about 240 MiB of operand blocks (sized for the
  * Infinity Cache; cut to whole rounds of the first kernel's work-groups over
  * the device's compute units when the sequence takes several windows), so
  * the size grows with T_total only through the pre-norm output;

@@ -302,7 +302,7 @@ def test_binding_marshals_to_the_abi_and_raises():
 
 def test_prefill_windows_follow_the_workspace():
     """The prefill runs window by window over the chunk slots: the default
-    workspace gives windows of up to ~144 MiB of operand blocks at the 35B-A3B
+    workspace gives windows of up to ~240 MiB of operand blocks at the 35B-A3B
     shape, cut to whole rounds of prep work-groups when several windows are
     needed, a smaller workspace more windows, down to one chunk slot; below
     that the call is refused."""
@@ -316,7 +316,7 @@ def test_prefill_windows_follow_the_workspace():
         # whole rounds of the 16 value-head pairs' prep work-groups over 256
         # compute units (16 slots) when several windows are needed, else
         # evened out
-        w = min((144 << 20) // slot, n_chunks)
+        w = min((240 << 20) // slot, n_chunks)
         if w < n_chunks and w >= 16:
             return w // 16 * 16
         return -(-n_chunks // -(-n_chunks // w))
@@ -328,11 +328,11 @@ def test_prefill_windows_follow_the_workspace():
     assert names[:-1] == ["prep", "scan"] * ((len(names) - 1) // 2)
     n_chunks = (T + 63) // 64                     # the bound the library plans for
     win = window(n_chunks)                        # chunk slots per window
-    assert win == 32 and len(names) == 1 + 2 * 2
+    assert win == 64 and len(names) == 1 + 2 * 1
     # beyond the pre-norm output and the decay table, only the window grows
-    # (131072 tokens: 64 windows of 32 slots, two rounds each)
-    assert window(131072 // 64) == 32
-    assert len(gdn.prefill_launches(lay, 1, 131072)) == 1 + 2 * 64
+    # (131072 tokens: 32 windows of 64 slots, four rounds each)
+    assert window(131072 // 64) == 64
+    assert len(gdn.prefill_launches(lay, 1, 131072)) == 1 + 2 * 32
     nb_long = gdn.prefill_workspace_bytes(lay, 1, 131072)
     assert nb_long - nb == ((131072 - T) * 32 * 128 * 2 + 4 * (131072 - T) // 64 * 32
                             + (window(131072 // 64) - win) * slot)

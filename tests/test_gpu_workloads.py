@@ -43,7 +43,7 @@ def test_prefill_weak_decay_long_head_sample(T):
     the state itself kept in fp32) rounds that slowly decaying state chunk
     after chunk.  One sequence of T tokens from a N(0, 0.02) state, key
     heads 3 and 12 against the oracle; T = 2048, 32768 and 131072 (2048
-    chunks, 64 windows) show how the error grows with the length."""
+    chunks, 32 windows) show how the error grows with the length."""
     case = synth.prefill_case(synth.FULL, [T], seed=31, with_state=True,
                               A_log_range=(math.log(1e-4), math.log(1e-3)))
     res = gpu_prefill(case, want_core=True)
