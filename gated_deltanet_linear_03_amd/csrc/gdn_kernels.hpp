@@ -97,11 +97,10 @@ __host__ __device__ constexpr int64_t vch_bytes(int DK, int DV, int C) {
 // them and the one that reads them (the other traffic of a step passes it
 // by: inputs are read and outputs written non-temporally); at 128/128/64 and
 // 32 value heads that is 64 chunk slots, 230 MB, four rounds of prep
-// work-groups.  Several sequences run their chunks concurrently in one
-// window (a window boundary would serialise them), up to a cap that bounds
-// the workspace.
+// work-groups.  A batch of several sequences uses the same size: the
+// sequences whose chunks share a window run concurrently, and keeping the
+// blocks cached outweighs the serialisation at window boundaries.
 constexpr int64_t kPrefillWindowBytes = 240ll << 20;
-constexpr int64_t kPrefillBatchWindowBytes = 4ll << 30;
 
 // Chunk slots per window for a layer: as many as the target size allows.
 // When that takes several windows and holds at least one round of prep
@@ -112,7 +111,7 @@ constexpr int64_t kPrefillBatchWindowBytes = 4ll << 30;
 inline int64_t prefill_window_slots(int DK, int DV, int C, int Hk, int Hv, int N, int64_t max_chunks,
                                     int compute_units) {
     const int64_t slot = static_cast<int64_t>(Hv) * vch_bytes(DK, DV, C);
-    int64_t w = (N > 1 ? kPrefillBatchWindowBytes : kPrefillWindowBytes) / slot;
+    int64_t w = kPrefillWindowBytes / slot;
     const int64_t cap = max_chunks > 1 ? max_chunks : 1;
     w = w < 1 ? 1 : (w > cap ? cap : w);
     const int G = Hk > 0 ? Hv / Hk : 1;

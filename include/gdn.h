@@ -199,13 +199,11 @@ int gdn_abi_version(void);
  * T_total tokens in all (an upper bound over every length split).  It holds
  * the chunk table, the pre-norm output as fp16 (when no core_out is given),
  * two recurrent-state carry slots and the per-chunk operand blocks of one
- * window of chunks.  The prefill runs window by window: for one sequence
- * the window is at most about 240 MiB of operand blocks (sized for the
- * Infinity Cache; cut to whole rounds of the first kernel's work-groups over
- * the device's compute units when the sequence takes several windows), so
- * the size grows with T_total only through the pre-norm output;
- * for N > 1 the sequences share windows of up to 4 GiB (all of a batch's
- * chunks at once, unless it is larger).  Returns 0 and sets
+ * window of chunks.  The prefill runs window by window: the window is at
+ * most about 240 MiB of operand blocks (sized for the Infinity Cache; cut to
+ * whole rounds of the first kernel's work-groups over the device's compute
+ * units when the batch takes several windows), so the size grows with
+ * T_total only through the pre-norm output.  Returns 0 and sets
  * gdn_last_error() if the layer is invalid or unsupported. */
 size_t gdn_prefill_workspace_bytes(const gdn_layer* layer, int32_t N,
                                    int64_t T_total);
