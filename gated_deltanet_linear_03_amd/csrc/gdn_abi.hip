@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/gdn.h"
@@ -662,17 +663,25 @@ gdn_status gdn_layer_prefill(const gdn_layer* L, const gdn_proj* pr, const gdn_l
     pio.state_slots = io->state_slots;
     pio.num_slots = io->num_slots;
     pio.status = io->status;
+    // The prefill inside the layer runs windows of half the default size:
+    // in_proj's output, just written, shares the Infinity Cache with the
+    // operand blocks here (measured at 4096 tokens: 0.463 ms per layer step
+    // with 32-slot windows, 0.492 with 64).  Only the window changes, not
+    // the bits.
+    const WsLayout pw = ws_layout(&Lg, io->N, T, true, 0);
+    const size_t pf_cap = static_cast<size_t>(pw.off_vch + std::max<int64_t>(1, pw.win_slots / 2) * pw.slot_bytes);
+    const size_t pf_bytes = std::min(ws_bytes - w.off_pf, pf_cap);
     // validate the prefill part before enqueueing anything
-    st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr, false);
+    st = prefill_impl(&Lg, &pio, base + w.off_pf, pf_bytes, stream, nullptr, false);
     if (st != GDN_OK) return st;
-    if (T == 0) return prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
+    if (T == 0) return prefill_impl(&Lg, &pio, base + w.off_pf, pf_bytes, stream, nullptr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     // one kernel family at every T (the library's pinned algorithm): a
     // sequence's bits do not depend on how many tokens share the call
     hipError_t e = gdn::launch_gemm_bf16_nt(io->x, pr->hidden, pr->w_in, pr->hidden, proj, w.P, true, T, w.P,
                                             pr->hidden, s, gdn::kGemmLibrary);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "in_proj launch failed: %s", hipGetErrorString(e));
-    st = prefill_impl(&Lg, &pio, base + w.off_pf, ws_bytes - w.off_pf, stream, nullptr);
+    st = prefill_impl(&Lg, &pio, base + w.off_pf, pf_bytes, stream, nullptr);
     if (st != GDN_OK) return st;
     e = gdn::launch_gemm_bf16_nt(gated, HD, pr->w_out, HD, io->y, pr->hidden, io->y_dtype == GDN_DTYPE_BF16, T,
                                  pr->hidden, HD, s, gdn::kGemmLibrary);
